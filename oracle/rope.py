@@ -1,0 +1,54 @@
+"""Rotary position encoding (RoPE) as a complex multiplication per pair, float64.
+
+Source of the operation: the InferScale review (arXiv 2607.27090), "What
+carries the argument" -- keys are stored before rotary position encoding and
+re-rotated to serving-time positions on injection -- and the "Axiom &
+Free-Parameter Ledger" axiom R_a^T R_b = R_{b-a} (Theorem 6, section 5.1).
+The rotation itself is RoFormer's (reference [20] of that page).
+
+Readings (the pages give no formula):
+* Pairing: half split (GPT-NeoX style): element j pairs with j + D/2,
+  j = 0 .. D/2-1.  The pair is the complex number z_j = x[j] + i x[j + D/2].
+* Frequencies: theta_j = base ** (-2j / D) radians per position.
+* Sign: z_j' = z_j * exp(+i * pos * theta_j), i.e.
+  x'[j] = x[j] cos - x[j+D/2] sin,  x'[j+D/2] = x[j+D/2] cos + x[j] sin.
+* Positions are 0-based integers; position 0 is the identity.
+"""
+
+import numpy as np
+
+
+def inv_freq(head_dim, base):
+    """theta_j = base ** (-2j / D) for j = 0 .. D/2 - 1, float64."""
+    if head_dim % 2:
+        raise ValueError("head_dim must be even")
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(base) ** (-(2.0 * j) / head_dim)
+
+
+def rotation_factors(pos, head_dim, base):
+    """exp(i * pos * theta_j) as complex128, shape pos.shape + (D/2,)."""
+    ang = np.asarray(pos, dtype=np.float64)[..., None] * inv_freq(head_dim, base)
+    w = np.empty(ang.shape, dtype=np.complex128)
+    w.real = np.cos(ang)
+    w.imag = np.sin(ang)
+    return w
+
+
+def rotate(x, pos, base):
+    """Rotate float64 vectors x[..., D] to positions pos (broadcast to x[..., 0]).
+
+    Returns float64 x' with x'[j] + i x'[j+D/2] = (x[j] + i x[j+D/2]) * exp(i pos theta_j).
+    """
+    x = np.asarray(x, dtype=np.float64)
+    d = x.shape[-1]
+    half = d // 2
+    w = rotation_factors(pos, d, base)
+    z = np.empty(x.shape[:-1] + (half,), dtype=np.complex128)
+    z.real = x[..., :half]
+    z.imag = x[..., half:]
+    zr = z * w
+    out = np.empty_like(x)
+    out[..., :half] = zr.real
+    out[..., half:] = zr.imag
+    return out

@@ -1,0 +1,124 @@
+"""Planted mistakes in the oracle (on the CPU) must be caught by the pins.
+
+Each mutant replaces one oracle function with a plausible slip; the test
+asserts that at least one pin in test_oracle_pins fails under it.  This shows
+the pins constrain the oracle rather than restate it.
+"""
+
+import numpy as np
+import pytest
+
+from oracle import bf16, paged, rope
+
+import test_oracle_pins as pins
+
+
+def _rotate_sign_flipped(x, pos, base):
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    w = np.conj(rope.rotation_factors(pos, x.shape[-1], base))
+    z = x[..., :half] + 1j * x[..., half:]
+    zr = z * w
+    return np.concatenate([zr.real, zr.imag], axis=-1)
+
+
+def _rotate_interleaved(x, pos, base):
+    # GPT-J pairing (2j, 2j+1) instead of the half split
+    x = np.asarray(x, dtype=np.float64)
+    w = rope.rotation_factors(pos, x.shape[-1], base)
+    z = x[..., 0::2] + 1j * x[..., 1::2]
+    zr = z * w
+    out = np.empty_like(x)
+    out[..., 0::2] = zr.real
+    out[..., 1::2] = zr.imag
+    return out
+
+
+def _inv_freq_wrong_exponent(head_dim, base):
+    j = np.arange(head_dim // 2, dtype=np.float64)
+    return np.float64(base) ** (-j / head_dim)
+
+
+def _rotate_dropped_term(x, pos, base):
+    # x'[j] = x[j] cos (the -x[j+D/2] sin term dropped)
+    x = np.asarray(x, dtype=np.float64)
+    half = x.shape[-1] // 2
+    w = rope.rotation_factors(pos, x.shape[-1], base)
+    out = np.empty_like(x)
+    out[..., :half] = x[..., :half] * w.real
+    out[..., half:] = x[..., half:] * w.real + x[..., :half] * w.imag
+    return out
+
+
+def _round_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f = x.astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _round_half_up(x):
+    x = np.asarray(x, dtype=np.float64)
+    m, e = np.frexp(x)
+    r = np.ldexp(np.floor(np.ldexp(m, 8) + 0.5), e - 8)
+    with np.errstate(over="ignore", invalid="ignore"):
+        f = np.where(np.isfinite(x), r, x).astype(np.float32)
+    return (f.view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def _positions_off_by_one(prefix_len, fact_lengths):
+    out, p = [], int(prefix_len) + 1
+    for length in fact_lengths:
+        out.append(list(range(p, p + int(length))))
+        p += int(length)
+    return out
+
+
+def _positions_sorted_facts(prefix_len, fact_lengths):
+    # facts placed by length instead of in list order
+    order = sorted(range(len(fact_lengths)), key=lambda i: fact_lengths[i])
+    starts, p = {}, int(prefix_len)
+    for i in order:
+        starts[i] = p
+        p += int(fact_lengths[i])
+    return [list(range(starts[i], starts[i] + int(fact_lengths[i])))
+            for i in range(len(fact_lengths))]
+
+
+def _slot_logical(pos, block_table, block_size):
+    # forgets the block table (logical == physical)
+    return int(pos)
+
+
+def _slot_swapped(pos, block_table, block_size):
+    pos = int(pos)
+    return int(block_table[pos % len(block_table)]) * block_size + pos // len(block_table)
+
+
+MUTANTS = [
+    ("rope sign flipped", rope, "rotate", _rotate_sign_flipped),
+    ("rope interleaved pairing", rope, "rotate", _rotate_interleaved),
+    ("rope frequency exponent", rope, "inv_freq", _inv_freq_wrong_exponent),
+    ("rope dropped sin term", rope, "rotate", _rotate_dropped_term),
+    ("bf16 truncation", bf16, "f64_to_bf16_bits", _round_truncate),
+    ("bf16 round half up", bf16, "f64_to_bf16_bits", _round_half_up),
+    ("positions off by one", paged, "fact_positions", _positions_off_by_one),
+    ("facts reordered", paged, "fact_positions", _positions_sorted_facts),
+    ("slot ignores block table", paged, "slot_of", _slot_logical),
+    ("slot index swapped", paged, "slot_of", _slot_swapped),
+]
+
+
+@pytest.mark.parametrize("name,module,attr,fn", MUTANTS, ids=[m[0] for m in MUTANTS])
+def test_mutant_is_caught(monkeypatch, name, module, attr, fn):
+    monkeypatch.setattr(module, attr, fn)
+    failures = []
+    for check in pins.ALL_CHECKS:
+        try:
+            with np.errstate(all="ignore"):
+                check()
+        except AssertionError:
+            failures.append(check.__name__)
+        except (IndexError, KeyError, ValueError):
+            failures.append(check.__name__ + " (error)")
+    assert failures, f"no pin caught mutant: {name}"
