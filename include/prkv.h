@@ -1,0 +1,180 @@
+/*
+ * prkv.h -- pre-RoPE KV injection with Chunked RoPE into a paged KV cache.
+ *
+ * C ABI of libprkv.so (gfx950 / MI355X).  The operation is the serving-time
+ * step of "InferScale: GPU-Native KV Injection for Personalized LLM Serving"
+ * (Pith review of arXiv 2607.27090): facts' keys and values are precomputed
+ * once and kept GPU-resident with keys BEFORE rotary position encoding; at
+ * serving time the top-k retrieved facts are resolved to their KV by fact_id,
+ * the keys are rotated to the facts' serving-time positions (Chunked RoPE),
+ * and K and V are scatter-copied into the engine's paged KV cache so that
+ * only the query needs prefill ("The pith"; "Referee Report", Summary;
+ * Figure 2 caption; "Axiom & Free-Parameter Ledger", KV-connector axiom,
+ * section 3.4).
+ *
+ * Conventions
+ *  - bf16 values are passed as raw 16-bit patterns (uint16_t storage).
+ *  - Every call returns PRKV_OK (0) or a negative PRKV_ERR_* code; the text
+ *    of the last error on the calling thread is last_error_string().
+ *  - Validation is complete before anything is enqueued: on error nothing is
+ *    enqueued and no output is modified.
+ *  - Device memory is always owned by the caller.  The library never
+ *    allocates device memory; it keeps host-side metadata only.
+ *  - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *    Enqueued work is asynchronous with respect to the host unless stated.
+ *  - Device pointers must be 16-byte aligned.
+ *
+ * Layouts
+ *  - Store arenas (K and V separately): [L][capacity_rows][H][D] bf16,
+ *    layer-major; a fact owns the same contiguous row range in every layer.
+ *  - Paged cache, one K and one V tensor per layer:
+ *    [num_blocks][block_size][H][D] bf16; slot = block * block_size + offset.
+ *  - RoPE: half-split pairing (element j pairs with j + D/2),
+ *    theta_j = rope_theta^(-2j/D), x' = (x_j + i x_{j+D/2}) * exp(+i pos theta_j).
+ */
+#ifndef PRKV_H
+#define PRKV_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+enum prkv_status {
+  PRKV_OK = 0,
+  PRKV_ERR_INVALID_ARG = -1,    /* bad size, null pointer, bad descriptor   */
+  PRKV_ERR_ALIGNMENT = -2,      /* device pointer not 16-byte aligned       */
+  PRKV_ERR_UNKNOWN_FACT = -3,   /* fact id never put                        */
+  PRKV_ERR_DUPLICATE_FACT = -4, /* fact id put twice                        */
+  PRKV_ERR_CAPACITY = -5,       /* arena rows exhausted / id >= max_facts   */
+  PRKV_ERR_OUT_OF_RANGE = -6,   /* position, block index or block id        */
+  PRKV_ERR_DUPLICATE_SLOT = -7, /* two injected tokens map to one slot      */
+  PRKV_ERR_BUFFER_TOO_SMALL = -8,
+  PRKV_ERR_NO_DEVICE = -9,      /* metadata-only store used for device work */
+  PRKV_ERR_HIP = -10,           /* a HIP runtime call failed                */
+  PRKV_ERR_NO_MEMORY = -11      /* host allocation failed                   */
+};
+
+enum prkv_rope_style { PRKV_ROPE_HALF_SPLIT = 0 };
+
+/* Shape of a store and of the model it serves. */
+typedef struct prkv_store_desc {
+  int32_t num_layers;    /* L, 1..128                                         */
+  int32_t num_kv_heads;  /* H >= 1                                            */
+  int32_t head_dim;      /* D in {16, 32, 64, 128, 256, 512, 1024}            */
+  int32_t max_facts;     /* fact ids are 0 .. max_facts-1                     */
+  int64_t capacity_rows; /* rows per layer in each arena, <= 2^31-1           */
+  int32_t max_position;  /* positions must be < max_position                  */
+  int32_t rope_style;    /* PRKV_ROPE_HALF_SPLIT                              */
+  double rope_theta;     /* RoPE base, > 1                                    */
+} prkv_store_desc;
+
+typedef struct prkv_store prkv_store; /* opaque host-side store handle */
+
+/* Bytes the caller must allocate on the device for ONE arena (K or V) and for
+ * the RoPE table that store_create fills:
+ *   arena = L * capacity_rows * H * D * 2,
+ *   rope  = max_position * (D/2) * 16   (cos, sin as float32 hi/lo pairs). */
+int store_required_bytes(const prkv_store_desc* desc, size_t* arena_bytes_each,
+                         size_t* rope_table_bytes);
+
+/* Create a store over caller-owned device memory.
+ * Source: InferScale review, "Referee Report" Summary ("stored pre-RoPE
+ * alongside semantic embeddings", GPU-resident) and Figure 2 (one fact_id
+ * names the fact's embedding and its pre-RoPE K/V).
+ * k_arena, v_arena: device, arena_bytes_each each.  rope_table: device,
+ * rope_table_bytes; filled here (float64 angles split into float32 hi + lo)
+ * with a copy on `stream` that this call waits for.  Passing all three
+ * pointers as NULL creates a metadata-only store: facts can be reserved and
+ * build_slot_mapping works, device calls return PRKV_ERR_NO_DEVICE.
+ * On success *out receives the handle (free with store_destroy). */
+int store_create(const prkv_store_desc* desc, void* k_arena, void* v_arena,
+                 void* rope_table, void* stream, prkv_store** out);
+
+/* Append one fact: `len` rows in every layer, the same row range in K and V.
+ * Source: InferScale review, Figure 2 caption (offline, each fact is encoded
+ * once under a shared fact_id) and the ledger's read-mostly-store axiom
+ * (Proposition 5; online updates are future work, so the store is
+ * append-only and has no delete).
+ * k_src, v_src: [L][len][H][D] bf16, contiguous, device memory or pinned host
+ * memory; copied on `stream` (asynchronous: keep them alive until the stream
+ * passes).  With both NULL the rows are only reserved (another producer may
+ * write them; see store_fact_info).  Errors: INVALID_ARG, CAPACITY (id >=
+ * max_facts or not enough rows), DUPLICATE_FACT, NO_DEVICE (sources given to a
+ * metadata-only store), HIP. */
+int store_put_fact(prkv_store* st, int32_t fact_id, int32_t len, const void* k_src,
+                   const void* v_src, void* stream);
+
+/* Row range of a fact: *first_row and *len (UNKNOWN_FACT if never put). */
+int store_fact_info(const prkv_store* st, int32_t fact_id, int64_t* first_row,
+                    int32_t* len);
+
+/* Release the host-side handle.  Device memory stays the caller's. */
+void store_destroy(prkv_store* st);
+
+/* Flatten a batch of requests into per-token (arena row, position, slot).
+ * Source: InferScale review, "If this is right" bullet 2 and "invented
+ * entities: Chunked RoPE" (facts encoded once are placed at arbitrary prompt
+ * positions, dynamically ordered), and the KV-connector axiom (section 3.4:
+ * the prefix is marked externally available, blocks are allocated without
+ * prefill, then K/V are scatter-copied).
+ * Host-only; makes no HIP call.
+ *   Request r has facts fact_ids[req_fact_ptr[r] .. req_fact_ptr[r+1]) in
+ *   rank order and a prefix of start_pos[r] tokens.  Its facts occupy
+ *   positions start_pos[r], start_pos[r]+1, ... contiguously, in list order;
+ *   position p lives in slot block_tables[r*bt_stride + p/block_size] *
+ *   block_size + p % block_size, for p/block_size < bt_len[r].
+ * Outputs (host int32, `capacity` entries each), in request, fact, token
+ * order: src_row (arena row), pos (position), slot (cache slot); *n_tokens
+ * is the token count.  If capacity is too small, BUFFER_TOO_SMALL is returned
+ * with *n_tokens set to the count needed and the outputs untouched.
+ * Errors: INVALID_ARG, UNKNOWN_FACT, OUT_OF_RANGE (position >= max_position,
+ * block table too short, block id outside [0, num_blocks)), DUPLICATE_SLOT
+ * (two tokens of this call in one slot; the same fact twice in one request is
+ * legal, at two positions).  Safe to call concurrently on one store. */
+int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_fact_ptr,
+                       const int32_t* fact_ids, const int32_t* start_pos,
+                       const int32_t* block_tables, int32_t bt_stride,
+                       const int32_t* bt_len, int32_t block_size, int64_t num_blocks,
+                       int32_t* src_row, int32_t* pos, int32_t* slot, int64_t capacity,
+                       int64_t* n_tokens);
+
+/* Gather, rotate and scatter: for every token t and layer l,
+ *   Kcache_l[slot[t]] = RoPE(pos[t]) applied to Karena[l][src_row[t]]
+ *   Vcache_l[slot[t]] = Varena[l][src_row[t]]            (bit copy)
+ * Source: InferScale review, "What carries the argument" (keys stored
+ * pre-RoPE are re-rotated to serving-time positions on injection into the
+ * paged cache) and "Referee Report" Summary (scatter-copy into vLLM's paged
+ * KV cache); Theorem 6 (rotation at injection is an exact relocation).
+ * One kernel launch covers every token, layer and KV head.  K is rotated in
+ * float32 with compensated (hi/lo) cos/sin and rounded to nearest-even bf16.
+ * d_src_row, d_pos, d_slot: device int32[n_tokens] (from build_slot_mapping).
+ * k_cache_layers, v_cache_layers: HOST arrays of L device pointers, each a
+ * [num_blocks][block_size][H][D] bf16 tensor.  d_status: optional device
+ * int32; if non-NULL the kernel ORs 1 (row out of range), 2 (position out of
+ * range) or 4 (slot out of range) into it for any token it skipped; tokens
+ * out of range are never read or written.  n_tokens == 0 is a no-op.
+ * Asynchronous on `stream`; never synchronizes.  Slots must be distinct
+ * (build_slot_mapping guarantees it); otherwise the result is undefined. */
+int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row,
+                const int32_t* d_pos, const int32_t* d_slot,
+                void* const* k_cache_layers, void* const* v_cache_layers,
+                int32_t block_size, int64_t num_blocks, int32_t* d_status,
+                void* stream);
+
+/* Fill a HOST buffer with the RoPE table store_create would upload:
+ * [max_position][D/2][4] float32 = (cos_hi, cos_lo, sin_hi, sin_lo) with
+ * cos_hi = fl32(cos a), cos_lo = fl32(cos a - cos_hi), a = pos * theta_j in
+ * float64.  out_bytes must be >= rope_table_bytes. */
+int rope_table_fill(const prkv_store_desc* desc, float* out, size_t out_bytes);
+
+/* Text of the last error on this thread ("" if none). */
+const char* last_error_string(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* PRKV_H */

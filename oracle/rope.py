@@ -15,15 +15,26 @@ Readings (the pages give no formula):
 * Positions are 0-based integers; position 0 is the identity.
 """
 
+from decimal import Decimal, localcontext
+
 import numpy as np
 
 
 def inv_freq(head_dim, base):
-    """theta_j = base ** (-2j / D) for j = 0 .. D/2 - 1, float64."""
+    """theta_j = base ** (-2j / D) for j = 0 .. D/2 - 1, rounded once to float64.
+
+    Evaluated in 60-digit decimal arithmetic and then rounded, so the value is
+    the float64 nearest the exact power on every machine (a vectorised float64
+    power is not correctly rounded on every CPU, and an ulp in theta_j moves
+    the angle pos * theta_j by up to ~2e-12 at the positions used here).
+    """
     if head_dim % 2:
         raise ValueError("head_dim must be even")
-    j = np.arange(head_dim // 2, dtype=np.float64)
-    return np.float64(base) ** (-(2.0 * j) / head_dim)
+    with localcontext() as ctx:
+        ctx.prec = 60
+        b = Decimal(repr(float(base)))
+        vals = [float(b ** (Decimal(-2 * j) / Decimal(head_dim))) for j in range(head_dim // 2)]
+    return np.array(vals, dtype=np.float64)
 
 
 def rotation_factors(pos, head_dim, base):

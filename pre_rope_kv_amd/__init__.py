@@ -11,13 +11,3 @@ call into the binding raises if ``libprkv.so`` has not been built.
 """
 
 __all__ = ["prkv", "workloads"]
-
-
-def __getattr__(name):
-    if name == "prkv":
-        from . import prkv
-        return prkv
-    if name == "workloads":
-        from . import workloads
-        return workloads
-    raise AttributeError(name)

@@ -1,0 +1,65 @@
+"""Build libprkv.so in-tree for gfx950.
+
+    python -m pre_rope_kv_amd.build        (or __graft_entry__.build())
+
+The host half (prkv_host.cpp) is plain C++17 built with g++; the device half
+(prkv_inject.hip) is built with hipcc for gfx950 only.  Packed fp32 VALU
+instructions are disabled and FP contraction is off: the compensated
+rotation relies on every product and sum being rounded exactly as written.
+"""
+
+import os
+import subprocess
+import sys
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+ROOT = os.path.dirname(HERE)
+CSRC = os.path.join(HERE, "csrc")
+INCLUDE = os.path.join(ROOT, "include")
+BUILD = os.path.join(ROOT, "_build")
+LIB = os.path.join(HERE, "libprkv.so")
+ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
+ARCH = "gfx950"
+
+HIP_FLAGS = [
+    f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
+    "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    "-Wall", "-Wno-unused-command-line-argument",
+]
+
+
+def _run(cmd, verbose):
+    if verbose:
+        print(" ".join(cmd), flush=True)
+    res = subprocess.run(cmd, capture_output=True, text=True)
+    if res.returncode != 0:
+        sys.stderr.write(res.stdout + res.stderr)
+        raise RuntimeError(f"build step failed: {' '.join(cmd[:2])} ... (exit {res.returncode})")
+    return res
+
+
+def build(verbose=False):
+    os.makedirs(BUILD, exist_ok=True)
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    host_o = os.path.join(BUILD, "prkv_host.o")
+    dev_o = os.path.join(BUILD, "prkv_inject.o")
+    _run(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
+          "-c", os.path.join(CSRC, "prkv_host.cpp"), "-o", host_o], verbose)
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "prkv_inject.hip"),
+          "-o", dev_o], verbose)
+    tmp = LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, host_o, dev_o,
+          f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    os.replace(tmp, LIB)
+    return LIB
+
+
+def device_asm(out_path):
+    """Write the gfx950 assembly of the device half (for inspection only)."""
+    hipcc = os.path.join(ROCM, "bin", "hipcc")
+    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "--cuda-device-only", "-S",
+          os.path.join(CSRC, "prkv_inject.hip"), "-o", out_path], False)
+
+
+if __name__ == "__main__":
+    print(build(verbose=True))

@@ -1,0 +1,275 @@
+// Host half of libprkv.so: descriptor validation, the fact table, the
+// slot-mapping builder and the RoPE table builder.  Plain C++17; no HIP calls.
+//
+// Operation sources (page "InferScale: GPU-Native KV Injection for
+// Personalized LLM Serving", Pith review of arXiv 2607.27090):
+//  - fact table keyed by fact_id: Figure 2 caption (each fact encoded once
+//    under a shared fact_id) and the ledger's read-mostly-store axiom
+//    (Proposition 5): append-only, no delete.
+//  - slot mapping: "If this is right" bullet 2 and "invented entities:
+//    Chunked RoPE" (dynamic top-k placement at arbitrary positions) and the
+//    KV-connector axiom, section 3.4 (prefix external, blocks allocated
+//    without prefill, then scatter-copy).
+//  - RoPE table: ledger axiom R_a^T R_b = R_{b-a} (Theorem 6, section 5.1);
+//    frequencies of RoFormer (reference [20]) with half-split pairing.
+
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <limits>
+#include <new>
+#include <string>
+
+#include "prkv_internal.h"
+
+namespace prkv {
+
+static thread_local std::string g_error;
+
+int fail(int code, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_error = buf;
+  return code;
+}
+
+void clear_error() { g_error.clear(); }
+
+static bool pow2(int64_t v) { return v > 0 && (v & (v - 1)) == 0; }
+
+int validate_desc(const prkv_store_desc* d) {
+  if (!d) return fail(PRKV_ERR_INVALID_ARG, "descriptor is NULL");
+  if (d->num_layers < 1 || d->num_layers > kMaxLayers)
+    return fail(PRKV_ERR_INVALID_ARG, "num_layers %d not in [1, %d]", d->num_layers, kMaxLayers);
+  if (d->num_kv_heads < 1)
+    return fail(PRKV_ERR_INVALID_ARG, "num_kv_heads %d < 1", d->num_kv_heads);
+  if (!pow2(d->head_dim) || d->head_dim < 16 || d->head_dim > 1024)
+    return fail(PRKV_ERR_INVALID_ARG, "head_dim %d must be a power of two in [16, 1024]",
+                d->head_dim);
+  if (d->max_facts < 1) return fail(PRKV_ERR_INVALID_ARG, "max_facts %d < 1", d->max_facts);
+  if (d->capacity_rows < 1 || d->capacity_rows > std::numeric_limits<int32_t>::max())
+    return fail(PRKV_ERR_INVALID_ARG, "capacity_rows %lld not in [1, 2^31-1]",
+                (long long)d->capacity_rows);
+  if (d->max_position < 1) return fail(PRKV_ERR_INVALID_ARG, "max_position %d < 1", d->max_position);
+  if (d->rope_style != PRKV_ROPE_HALF_SPLIT)
+    return fail(PRKV_ERR_INVALID_ARG, "rope_style %d unsupported", d->rope_style);
+  if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta))
+    return fail(PRKV_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  const double heads_dim = double(d->num_kv_heads) * d->head_dim;
+  if (heads_dim * d->capacity_rows * d->num_layers * 2.0 > 9.0e18)
+    return fail(PRKV_ERR_INVALID_ARG, "arena size overflows");
+  return PRKV_OK;
+}
+
+size_t arena_bytes(const prkv_store_desc& d) {
+  return size_t(d.num_layers) * size_t(d.capacity_rows) * size_t(row_elems(d)) * 2u;
+}
+
+size_t rope_bytes(const prkv_store_desc& d) {
+  return size_t(d.max_position) * size_t(d.head_dim / 2) * 16u;
+}
+
+int store_new(const prkv_store_desc* d, prkv_store** out) {
+  prkv_store* st = new (std::nothrow) prkv_store();
+  if (!st) return fail(PRKV_ERR_NO_MEMORY, "out of host memory");
+  st->desc = *d;
+  try {
+    st->first_row.assign(size_t(d->max_facts), -1);
+    st->length.assign(size_t(d->max_facts), 0);
+  } catch (const std::bad_alloc&) {
+    delete st;
+    return fail(PRKV_ERR_NO_MEMORY, "fact table of %d entries", d->max_facts);
+  }
+  *out = st;
+  return PRKV_OK;
+}
+
+int check_put(const prkv_store* st, int32_t fact_id, int32_t len) {
+  if (!st) return fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (fact_id < 0 || fact_id >= st->desc.max_facts)
+    return fail(PRKV_ERR_CAPACITY, "fact id %d outside [0, %d)", fact_id, st->desc.max_facts);
+  if (len < 1) return fail(PRKV_ERR_INVALID_ARG, "fact %d: length %d < 1", fact_id, len);
+  if (st->first_row[fact_id] >= 0)
+    return fail(PRKV_ERR_DUPLICATE_FACT, "fact %d already stored", fact_id);
+  if (st->rows_used + len > st->desc.capacity_rows)
+    return fail(PRKV_ERR_CAPACITY, "fact %d: %d rows exceed capacity (%lld of %lld used)",
+                fact_id, len, (long long)st->rows_used, (long long)st->desc.capacity_rows);
+  return PRKV_OK;
+}
+
+void commit_put(prkv_store* st, int32_t fact_id, int32_t len) {
+  st->first_row[fact_id] = st->rows_used;
+  st->length[fact_id] = len;
+  st->rows_used += len;
+}
+
+}  // namespace prkv
+
+using namespace prkv;
+
+extern "C" {
+
+const char* last_error_string(void) { return g_error.c_str(); }
+
+int store_required_bytes(const prkv_store_desc* desc, size_t* arena_bytes_each,
+                         size_t* rope_table_bytes) {
+  clear_error();
+  if (int rc = validate_desc(desc)) return rc;
+  if (!arena_bytes_each || !rope_table_bytes)
+    return fail(PRKV_ERR_INVALID_ARG, "output pointer is NULL");
+  *arena_bytes_each = arena_bytes(*desc);
+  *rope_table_bytes = rope_bytes(*desc);
+  return PRKV_OK;
+}
+
+int store_fact_info(const prkv_store* st, int32_t fact_id, int64_t* first_row, int32_t* len) {
+  clear_error();
+  if (!st || !first_row || !len) return fail(PRKV_ERR_INVALID_ARG, "NULL argument");
+  if (fact_id < 0 || fact_id >= st->desc.max_facts || st->first_row[fact_id] < 0)
+    return fail(PRKV_ERR_UNKNOWN_FACT, "fact %d not stored", fact_id);
+  *first_row = st->first_row[fact_id];
+  *len = st->length[fact_id];
+  return PRKV_OK;
+}
+
+void store_destroy(prkv_store* st) { delete st; }
+
+int rope_table_fill(const prkv_store_desc* desc, float* out, size_t out_bytes) {
+  clear_error();
+  if (int rc = validate_desc(desc)) return rc;
+  if (!out) return fail(PRKV_ERR_INVALID_ARG, "output is NULL");
+  const size_t need = rope_bytes(*desc);
+  if (out_bytes < need)
+    return fail(PRKV_ERR_BUFFER_TOO_SMALL, "rope table needs %zu bytes, got %zu", need, out_bytes);
+  const int half = desc->head_dim / 2;
+  // theta_j in extended precision, then one rounding to double
+  std::vector<double> inv(half);
+  for (int j = 0; j < half; ++j)
+    inv[j] = double(std::pow((long double)desc->rope_theta,
+                             -(2.0L * j) / (long double)desc->head_dim));
+  for (int64_t p = 0; p < desc->max_position; ++p) {
+    float* row = out + p * int64_t(half) * 4;
+    for (int j = 0; j < half; ++j) {
+      const double a = double(p) * inv[j];
+      const double c = std::cos(a), s = std::sin(a);
+      const float ch = float(c), sh = float(s);
+      row[4 * j + 0] = ch;
+      row[4 * j + 1] = float(c - double(ch));
+      row[4 * j + 2] = sh;
+      row[4 * j + 3] = float(s - double(sh));
+    }
+  }
+  return PRKV_OK;
+}
+
+int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_fact_ptr,
+                       const int32_t* fact_ids, const int32_t* start_pos,
+                       const int32_t* block_tables, int32_t bt_stride, const int32_t* bt_len,
+                       int32_t block_size, int64_t num_blocks, int32_t* src_row, int32_t* pos,
+                       int32_t* slot, int64_t capacity, int64_t* n_tokens) {
+  clear_error();
+  if (!st) return fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (!n_tokens) return fail(PRKV_ERR_INVALID_ARG, "n_tokens is NULL");
+  if (n_req < 0) return fail(PRKV_ERR_INVALID_ARG, "n_req %d < 0", n_req);
+  if (block_size < 1) return fail(PRKV_ERR_INVALID_ARG, "block_size %d < 1", block_size);
+  if (num_blocks < 1) return fail(PRKV_ERR_INVALID_ARG, "num_blocks %lld < 1", (long long)num_blocks);
+  const int64_t num_slots = num_blocks * int64_t(block_size);
+  if (num_blocks > std::numeric_limits<int32_t>::max() ||
+      num_slots > std::numeric_limits<int32_t>::max())
+    return fail(PRKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds 2^31-1");
+  if (n_req == 0) {
+    *n_tokens = 0;
+    return PRKV_OK;
+  }
+  if (!req_fact_ptr || !start_pos || !bt_len)
+    return fail(PRKV_ERR_INVALID_ARG, "request arrays must not be NULL");
+  if (req_fact_ptr[0] != 0) return fail(PRKV_ERR_INVALID_ARG, "req_fact_ptr[0] must be 0");
+  if (bt_stride < 0) return fail(PRKV_ERR_INVALID_ARG, "bt_stride %d < 0", bt_stride);
+  for (int32_t r = 0; r < n_req; ++r) {
+    if (req_fact_ptr[r + 1] < req_fact_ptr[r])
+      return fail(PRKV_ERR_INVALID_ARG, "req_fact_ptr decreases at request %d", r);
+    if (bt_len[r] < 0 || bt_len[r] > bt_stride)
+      return fail(PRKV_ERR_INVALID_ARG, "request %d: bt_len %d not in [0, bt_stride=%d]", r,
+                  bt_len[r], bt_stride);
+    if (start_pos[r] < 0) return fail(PRKV_ERR_INVALID_ARG, "request %d: start_pos < 0", r);
+  }
+  if (req_fact_ptr[n_req] > 0 && !fact_ids) return fail(PRKV_ERR_INVALID_ARG, "fact_ids is NULL");
+  if (!block_tables && bt_stride > 0) return fail(PRKV_ERR_INVALID_ARG, "block_tables is NULL");
+
+  // Pass 1: resolve, place and validate into per-thread scratch; detect
+  // duplicate slots with a bitmap over all slots (bits are cleared again below).
+  static thread_local std::vector<int32_t> s_row, s_pos, s_slot;
+  static thread_local std::vector<uint64_t> seen;
+  s_row.clear();
+  s_pos.clear();
+  s_slot.clear();
+  const size_t words = size_t((num_slots + 63) / 64);
+  if (seen.size() < words) seen.resize(words, 0);
+  const prkv_store_desc& d = st->desc;
+  int rc = PRKV_OK;
+  for (int32_t r = 0; r < n_req && rc == PRKV_OK; ++r) {
+    const int32_t* bt = block_tables + int64_t(r) * bt_stride;
+    int64_t p = start_pos[r];
+    for (int32_t i = req_fact_ptr[r]; i < req_fact_ptr[r + 1] && rc == PRKV_OK; ++i) {
+      const int32_t f = fact_ids[i];
+      if (f < 0 || f >= d.max_facts || st->first_row[f] < 0) {
+        rc = fail(PRKV_ERR_UNKNOWN_FACT, "request %d, fact %d: id %d not stored", r,
+                  i - req_fact_ptr[r], f);
+        break;
+      }
+      const int64_t row0 = st->first_row[f];
+      const int32_t len = st->length[f];
+      if (p + len > d.max_position) {
+        rc = fail(PRKV_ERR_OUT_OF_RANGE, "request %d: position %lld >= max_position %d", r,
+                  (long long)(p + len - 1), d.max_position);
+        break;
+      }
+      for (int32_t t = 0; t < len; ++t, ++p) {
+        const int64_t bi = p / block_size;
+        if (bi >= bt_len[r]) {
+          rc = fail(PRKV_ERR_OUT_OF_RANGE,
+                    "request %d: position %lld needs block index %lld, table has %d", r,
+                    (long long)p, (long long)bi, bt_len[r]);
+          break;
+        }
+        const int64_t b = bt[bi];
+        if (b < 0 || b >= num_blocks) {
+          rc = fail(PRKV_ERR_OUT_OF_RANGE, "request %d: block id %lld outside [0, %lld)", r,
+                    (long long)b, (long long)num_blocks);
+          break;
+        }
+        const int64_t s = b * block_size + p % block_size;
+        uint64_t& w = seen[size_t(s >> 6)];
+        const uint64_t bit = uint64_t(1) << (s & 63);
+        if (w & bit) {
+          rc = fail(PRKV_ERR_DUPLICATE_SLOT, "request %d: slot %lld written twice", r,
+                    (long long)s);
+          break;
+        }
+        w |= bit;
+        s_row.push_back(int32_t(row0 + t));
+        s_pos.push_back(int32_t(p));
+        s_slot.push_back(int32_t(s));
+      }
+    }
+  }
+  for (int32_t s : s_slot) seen[size_t(s) >> 6] = 0;
+  const int64_t total = int64_t(s_row.size());
+  if (rc != PRKV_OK) return rc;
+  *n_tokens = total;
+  if (total > capacity)
+    return fail(PRKV_ERR_BUFFER_TOO_SMALL, "%lld tokens, capacity %lld", (long long)total,
+                (long long)capacity);
+  if (total > 0 && (!src_row || !pos || !slot))
+    return fail(PRKV_ERR_INVALID_ARG, "output arrays must not be NULL");
+  std::memcpy(src_row, s_row.data(), size_t(total) * 4);
+  std::memcpy(pos, s_pos.data(), size_t(total) * 4);
+  std::memcpy(slot, s_slot.data(), size_t(total) * 4);
+  return PRKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,437 @@
+// Device half of libprkv.so for gfx950 (MI355X): store creation and fact
+// upload (HIP runtime copies), and the inject kernel.
+//
+// Operation (page "InferScale: GPU-Native KV Injection for Personalized LLM
+// Serving", Pith review of arXiv 2607.27090): "What carries the argument" --
+// keys stored before rotary encoding are re-rotated to serving-time positions
+// on injection into the paged cache; "Referee Report", Summary -- retrieved
+// facts' KV are scatter-copied into vLLM's paged KV cache; Theorem 6 (ledger
+// axiom R_a^T R_b = R_{b-a}) -- rotating at injection is an exact relocation.
+//
+// The kernel is a pure HBM-bound gather-rotate-scatter: per (token, layer) it
+// reads one K row and one V row (H*D bf16 each) from the arenas and writes
+// them to the token's slot of that layer's K and V cache.  No MFMA: the
+// rotation is a few fp32 VALU operations per element, far below the ridge.
+//
+// Work layout
+//  - A workgroup is 4 waves (256 lanes) and owns a tile of 4*TPW tokens and
+//    a contiguous share ("split") of each token's chunk range.
+//  - A token's work is L*H*D/16 "chunks"; chunk (l, h, c) covers 8 RoPE
+//    pairs: 16 bytes at element h*D + 8c (first half of the head) and 16
+//    bytes at h*D + D/2 + 8c (second half).  A lane owns whole pairs, so no
+//    cross-lane exchange is needed.  Lanes take chunks lane, lane+64, ...;
+//    since 64 is a multiple of D/16, a lane's c is fixed (lane % (D/16)) and
+//    its 8 (cos, sin) pairs are loaded once per token and kept in VGPRs for
+//    every layer.
+//  - Token metadata for the tile is gathered with one coalesced load per
+//    lane; each token's cos/sin row (read once per (position, pair) per tile)
+//    is staged in LDS, laid out so lanes with consecutive c read consecutive
+//    16-byte words.
+//  - Rotation: x1' = x1 c - x2 s, x2' = x2 c + x1 s with c = c_hi + c_lo and
+//    s = s_hi + s_lo (float32 hi/lo of the float64 value); each product with
+//    the hi part is made exact with an FMA error term, so the only rounding
+//    before the final bf16 rounding is one float32 rounding of the result
+//    (plus terms ~2^-48 |x|).  Rounding to bf16 is nearest-even
+//    (v_cvt_pk_bf16_f32).
+//  - 16-byte nontemporal loads and stores; 64-bit addressing (one layer of
+//    a large cache exceeds 4 GiB).
+
+#include <hip/hip_runtime.h>
+
+#include <atomic>
+#include <cstdint>
+#include <vector>
+
+#include "prkv_internal.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef float f32x2 __attribute__((ext_vector_type(2)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr int kWavesPerGroup = 4;
+constexpr int kThreads = kWave * kWavesPerGroup;
+constexpr int kUnroll = 2;
+
+struct LayerPtrs {
+  uint16_t* p[prkv::kMaxLayers];
+};
+
+struct InjectParams {
+  const uint16_t* k_arena;
+  const uint16_t* v_arena;
+  const f32x4* rope;  // [max_position][D/2] (cos_hi, cos_lo, sin_hi, sin_lo)
+  const int32_t* src_row;
+  const int32_t* pos;
+  const int32_t* slot;
+  int32_t* status;
+  int64_t n_tokens;
+  int64_t capacity_rows;
+  int64_t num_slots;
+  int32_t max_position;
+  int32_t num_layers;
+  int32_t num_heads;
+  int64_t n_tiles;           // tiles of 4*TPW tokens
+  int32_t tokens_per_wave;   // TPW
+  int32_t n_splits;          // workgroups per tile
+  int32_t iters_per_split;   // 64-chunk iterations per split
+};
+
+__device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
+
+__device__ __forceinline__ unsigned pack_bf16(float a, float b) {
+  f32x2 v = {a, b};
+  return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
+}
+
+// x1 * c - x2 * s with c = ch + cl, s = sh + sl.
+__device__ __forceinline__ float rot_first(float x1, float x2, f32x4 cs) {
+  const float p = x1 * cs.x;
+  const float e = __builtin_fmaf(x1, cs.x, -p);
+  const float q = x2 * cs.z;
+  const float f = __builtin_fmaf(x2, cs.z, -q);
+  const float a = p - q;
+  float t = __builtin_fmaf(x1, cs.y, e);
+  t = __builtin_fmaf(-x2, cs.w, t);
+  t = t - f;
+  return a + t;
+}
+
+// x2 * c + x1 * s.
+__device__ __forceinline__ float rot_second(float x1, float x2, f32x4 cs) {
+  const float p = x2 * cs.x;
+  const float e = __builtin_fmaf(x2, cs.x, -p);
+  const float q = x1 * cs.z;
+  const float f = __builtin_fmaf(x1, cs.z, -q);
+  const float a = p + q;
+  float t = __builtin_fmaf(x2, cs.y, e);
+  t = __builtin_fmaf(x1, cs.w, t);
+  t = t + f;
+  return a + t;
+}
+
+// Rotates 8 pairs: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
+__device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const f32x4 (&cs)[8]) {
+  u32x4 olo, ohi;
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float a0 = lo_bf16(lo[d]), a1 = hi_bf16(lo[d]);
+    const float b0 = lo_bf16(hi[d]), b1 = hi_bf16(hi[d]);
+    olo[d] = pack_bf16(rot_first(a0, b0, cs[2 * d]), rot_first(a1, b1, cs[2 * d + 1]));
+    ohi[d] = pack_bf16(rot_second(a0, b0, cs[2 * d]), rot_second(a1, b1, cs[2 * d + 1]));
+  }
+  lo = olo;
+  hi = ohi;
+}
+
+template <int D>
+__global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerPtrs kc,
+                                                          LayerPtrs vc) {
+  constexpr int CPH = D / 16;   // 16-byte chunks per half head
+  constexpr int HALF = D / 2;   // pairs per head
+  extern __shared__ f32x4 smem[];
+
+  const int tpw = p.tokens_per_wave;
+  const int tile_tokens = kWavesPerGroup * tpw;
+  const int split = blockIdx.x % p.n_splits;
+  const int64_t tile_stride = gridDim.x / p.n_splits;
+  int* meta = reinterpret_cast<int*>(smem + tile_tokens * HALF);  // row, pos, slot
+
+  const int wave = threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int c = lane % CPH;
+  const int H = p.num_heads;
+  const int nc = H * CPH;                 // chunks per (token, layer) row
+  const int total = p.num_layers * nc;    // chunks per token
+  const int it0 = split * p.iters_per_split;
+  int it1 = it0 + p.iters_per_split;
+  const int max_it = (total + kWave - 1) / kWave;
+  if (it1 > max_it) it1 = max_it;
+  const int64_t row_elems = int64_t(H) * D;
+  const int64_t layer_elems = p.capacity_rows * row_elems;
+
+  for (int64_t tile = blockIdx.x / p.n_splits; tile < p.n_tiles; tile += tile_stride) {
+    const int64_t tok0 = tile * tile_tokens;
+    __syncthreads();  // LDS of the previous tile is no longer read
+
+    // 1. Wave-wide gather of the tile's (row, pos, slot); out-of-range tokens
+    //    are marked row = -1 and skipped.
+    for (int i = threadIdx.x; i < tile_tokens; i += kThreads) {
+      const int64_t t = tok0 + i;
+      int row = -1, pos = 0, slot = 0;
+      if (t < p.n_tokens) {
+        row = p.src_row[t];
+        pos = p.pos[t];
+        slot = p.slot[t];
+        const int bad = ((row < 0 || row >= p.capacity_rows) ? 1 : 0) |
+                        ((pos < 0 || pos >= p.max_position) ? 2 : 0) |
+                        ((slot < 0 || slot >= p.num_slots) ? 4 : 0);
+        if (bad) {
+          if (p.status && split == 0) atomicOr(p.status, bad);
+          row = -1;
+        }
+      }
+      meta[3 * i + 0] = row;
+      meta[3 * i + 1] = pos;
+      meta[3 * i + 2] = slot;
+    }
+    __syncthreads();
+
+    // 2. Stage each token's cos/sin row in LDS: pair j = 8c + k goes to k*CPH + c.
+    for (int e = threadIdx.x; e < tile_tokens * HALF; e += kThreads) {
+      const int i = e / HALF, j = e - (e / HALF) * HALF;
+      if (meta[3 * i] < 0) continue;
+      const f32x4 v = p.rope[int64_t(meta[3 * i + 1]) * HALF + j];
+      smem[i * HALF + (j & 7) * CPH + (j >> 3)] = v;
+    }
+    __syncthreads();
+
+    // 3. Each wave streams its tokens through every layer of its split.
+    for (int ti = 0; ti < tpw; ++ti) {
+      const int i = wave * tpw + ti;
+      const int row = __builtin_amdgcn_readfirstlane(meta[3 * i + 0]);
+      if (row < 0) continue;
+      const int slot = __builtin_amdgcn_readfirstlane(meta[3 * i + 2]);
+
+      f32x4 cs[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cs[k] = smem[i * HALF + k * CPH + c];
+
+      for (int it = it0; it < it1; it += kUnroll) {
+        u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
+        int64_t soff[kUnroll];
+        int lay[kUnroll];
+        bool live[kUnroll];
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          const int e = (it + u) * kWave + lane;
+          live[u] = (it + u) < it1 && e < total;
+          const int l = e / nc;
+          const int r = e - l * nc;
+          const int h = r / CPH;
+          lay[u] = l;
+          const int64_t in_row = int64_t(h) * D + c * 8;
+          soff[u] = int64_t(slot) * row_elems + in_row;
+          if (live[u]) {
+            const int64_t aoff = int64_t(l) * layer_elems + int64_t(row) * row_elems + in_row;
+            ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_arena + aoff));
+            kb[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(p.k_arena + aoff + HALF));
+            va[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v_arena + aoff));
+            vb[u] = __builtin_nontemporal_load(
+                reinterpret_cast<const u32x4*>(p.v_arena + aoff + HALF));
+          }
+        }
+#pragma unroll
+        for (int u = 0; u < kUnroll; ++u) {
+          if (!live[u]) continue;
+          rotate8(ka[u], kb[u], cs);
+          uint16_t* kd = kc.p[lay[u]] + soff[u];
+          uint16_t* vd = vc.p[lay[u]] + soff[u];
+          __builtin_nontemporal_store(ka[u], reinterpret_cast<u32x4*>(kd));
+          __builtin_nontemporal_store(kb[u], reinterpret_cast<u32x4*>(kd + HALF));
+          __builtin_nontemporal_store(va[u], reinterpret_cast<u32x4*>(vd));
+          __builtin_nontemporal_store(vb[u], reinterpret_cast<u32x4*>(vd + HALF));
+        }
+      }
+    }
+  }
+}
+
+int hip_fail(hipError_t e, const char* what) {
+  return prkv::fail(PRKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
+
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D>
+hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
+                  int64_t grid, size_t lds, hipStream_t s) {
+  hipLaunchKernelGGL(inject_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), lds, s, p, kc, vc);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int store_create(const prkv_store_desc* desc, void* k_arena, void* v_arena, void* rope_table,
+                 void* stream, prkv_store** out) {
+  prkv::clear_error();
+  if (int rc = prkv::validate_desc(desc)) return rc;
+  if (!out) return prkv::fail(PRKV_ERR_INVALID_ARG, "out is NULL");
+  const bool any = k_arena || v_arena || rope_table;
+  const bool all = k_arena && v_arena && rope_table;
+  if (any && !all)
+    return prkv::fail(PRKV_ERR_INVALID_ARG,
+                      "k_arena, v_arena and rope_table must be all set or all NULL");
+  if (all && (!aligned16(k_arena) || !aligned16(v_arena) || !aligned16(rope_table)))
+    return prkv::fail(PRKV_ERR_ALIGNMENT, "device pointers must be 16-byte aligned");
+  prkv_store* st = nullptr;
+  if (int rc = prkv::store_new(desc, &st)) return rc;
+  if (all) {
+    std::vector<float> table;
+    try {
+      table.resize(prkv::rope_bytes(*desc) / sizeof(float));
+    } catch (const std::bad_alloc&) {
+      store_destroy(st);
+      return prkv::fail(PRKV_ERR_NO_MEMORY, "rope table staging");
+    }
+    if (int rc = rope_table_fill(desc, table.data(), table.size() * sizeof(float))) {
+      store_destroy(st);
+      return rc;
+    }
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpyAsync(rope_table, table.data(), prkv::rope_bytes(*desc),
+                                  hipMemcpyHostToDevice, s);
+    if (e == hipSuccess) e = hipStreamSynchronize(s);
+    if (e != hipSuccess) {
+      store_destroy(st);
+      return hip_fail(e, "rope table upload");
+    }
+    st->k_arena = k_arena;
+    st->v_arena = v_arena;
+    st->rope = rope_table;
+  }
+  *out = st;
+  return PRKV_OK;
+}
+
+int store_put_fact(prkv_store* st, int32_t fact_id, int32_t len, const void* k_src,
+                   const void* v_src, void* stream) {
+  prkv::clear_error();
+  if (int rc = prkv::check_put(st, fact_id, len)) return rc;
+  if ((k_src == nullptr) != (v_src == nullptr))
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "k_src and v_src must both be set or both NULL");
+  if (k_src) {
+    if (!st->device_backed())
+      return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store cannot take fact data");
+    const prkv_store_desc& d = st->desc;
+    const size_t row_bytes = size_t(prkv::row_elems(d)) * 2u;
+    const size_t width = size_t(len) * row_bytes;
+    const size_t dpitch = size_t(d.capacity_rows) * row_bytes;
+    const size_t doff = size_t(st->rows_used) * row_bytes;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    hipError_t e = hipMemcpy2DAsync(static_cast<char*>(st->k_arena) + doff, dpitch, k_src, width,
+                                    width, size_t(d.num_layers), hipMemcpyDefault, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(static_cast<char*>(st->v_arena) + doff, dpitch, v_src, width, width,
+                           size_t(d.num_layers), hipMemcpyDefault, s);
+    if (e != hipSuccess) return hip_fail(e, "fact upload");
+  }
+  prkv::commit_put(st, fact_id, len);
+  return PRKV_OK;
+}
+
+int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row,
+                const int32_t* d_pos, const int32_t* d_slot, void* const* k_cache_layers,
+                void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
+                int32_t* d_status, void* stream) {
+  prkv::clear_error();
+  if (!st) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (!st->device_backed()) return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store");
+  if (n_tokens < 0) return prkv::fail(PRKV_ERR_INVALID_ARG, "n_tokens < 0");
+  if (block_size < 1 || num_blocks < 1)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "block_size and num_blocks must be >= 1");
+  const int64_t num_slots = num_blocks * int64_t(block_size);
+  if (num_blocks > INT32_MAX || num_slots > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds 2^31-1");
+  if (n_tokens > num_slots)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "n_tokens %lld exceeds the cache's %lld slots",
+                      (long long)n_tokens, (long long)num_slots);
+  if (n_tokens == 0) return PRKV_OK;
+  if (!d_src_row || !d_pos || !d_slot || !k_cache_layers || !v_cache_layers)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((reinterpret_cast<uintptr_t>(d_src_row) | reinterpret_cast<uintptr_t>(d_pos) |
+       reinterpret_cast<uintptr_t>(d_slot) | reinterpret_cast<uintptr_t>(d_status)) & 3u)
+    return prkv::fail(PRKV_ERR_ALIGNMENT, "int32 arrays must be 4-byte aligned");
+  const prkv_store_desc& d = st->desc;
+  LayerPtrs kc{}, vc{};
+  for (int l = 0; l < d.num_layers; ++l) {
+    if (!k_cache_layers[l] || !v_cache_layers[l])
+      return prkv::fail(PRKV_ERR_INVALID_ARG, "cache pointer of layer %d is NULL", l);
+    if (!aligned16(k_cache_layers[l]) || !aligned16(v_cache_layers[l]))
+      return prkv::fail(PRKV_ERR_ALIGNMENT, "cache pointer of layer %d not 16-byte aligned", l);
+    kc.p[l] = static_cast<uint16_t*>(k_cache_layers[l]);
+    vc.p[l] = static_cast<uint16_t*>(v_cache_layers[l]);
+  }
+
+  // Launch shape: tiles of 4*TPW tokens; split each token's chunk range
+  // across workgroups until the grid holds enough waves to cover the chip.
+  const int D = d.head_dim;
+  const int64_t chunks = int64_t(d.num_layers) * d.num_kv_heads * (D / 16);
+  const int iters = int((chunks + kWave - 1) / kWave);
+  const int64_t want_waves = int64_t(compute_units()) * 16;
+  int tpw = 4;
+  while (tpw > 1 && (n_tokens + 4 * tpw - 1) / (4 * tpw) * 4 < want_waves) tpw /= 2;
+  // LDS: 8*D bytes of cos/sin per token, keep a tile under 32 KiB
+  while (tpw > 1 && int64_t(kWavesPerGroup) * tpw * D * 8 > 32768) tpw /= 2;
+  const int64_t tiles = (n_tokens + kWavesPerGroup * tpw - 1) / (kWavesPerGroup * tpw);
+  int n_splits = 1;
+  while (n_splits < iters && tiles * n_splits * kWavesPerGroup < want_waves) n_splits *= 2;
+  if (n_splits > iters) n_splits = iters;
+  int per = (iters + n_splits - 1) / n_splits;
+  per = (per + kUnroll - 1) / kUnroll * kUnroll;
+  n_splits = (iters + per - 1) / per;
+  // at most 2^20 workgroups; each loops over tiles with a grid stride
+  const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
+                                                                    : (int64_t(1) << 20) / n_splits;
+  const int64_t grid = grid_tiles * n_splits;
+  const size_t lds = size_t(kWavesPerGroup) * tpw * (size_t(D / 2) * 16 + 12);
+
+  InjectParams p;
+  p.k_arena = static_cast<const uint16_t*>(st->k_arena);
+  p.v_arena = static_cast<const uint16_t*>(st->v_arena);
+  p.rope = static_cast<const f32x4*>(st->rope);
+  p.src_row = d_src_row;
+  p.pos = d_pos;
+  p.slot = d_slot;
+  p.status = d_status;
+  p.n_tokens = n_tokens;
+  p.capacity_rows = d.capacity_rows;
+  p.num_slots = num_slots;
+  p.max_position = d.max_position;
+  p.num_layers = d.num_layers;
+  p.num_heads = d.num_kv_heads;
+  p.n_tiles = tiles;
+  p.tokens_per_wave = tpw;
+  p.n_splits = n_splits;
+  p.iters_per_split = per;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (D) {
+    case 16: e = launch<16>(p, kc, vc, grid, lds, s); break;
+    case 32: e = launch<32>(p, kc, vc, grid, lds, s); break;
+    case 64: e = launch<64>(p, kc, vc, grid, lds, s); break;
+    case 128: e = launch<128>(p, kc, vc, grid, lds, s); break;
+    case 256: e = launch<256>(p, kc, vc, grid, lds, s); break;
+    case 512: e = launch<512>(p, kc, vc, grid, lds, s); break;
+    case 1024: e = launch<1024>(p, kc, vc, grid, lds, s); break;
+    default: return prkv::fail(PRKV_ERR_INVALID_ARG, "head_dim %d unsupported", D);
+  }
+  if (e != hipSuccess) return hip_fail(e, "inject launch");
+  return PRKV_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,236 @@
+"""Thin ctypes binding of libprkv.so (C ABI in include/prkv.h), same names.
+
+Argument marshalling only: device buffers are passed as raw pointers taken
+from torch tensors (``tensor.data_ptr()``) or plain ints; host arrays as
+NumPy int32 arrays; streams as ``torch.cuda.Stream`` objects, raw handles or
+None (the current torch stream).  Every step of the path runs in the native
+library.  A missing library is an error, never a fallback.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libprkv.so")
+
+PRKV_OK = 0
+ERRORS = {
+    -1: "INVALID_ARG", -2: "ALIGNMENT", -3: "UNKNOWN_FACT", -4: "DUPLICATE_FACT",
+    -5: "CAPACITY", -6: "OUT_OF_RANGE", -7: "DUPLICATE_SLOT", -8: "BUFFER_TOO_SMALL",
+    -9: "NO_DEVICE", -10: "HIP", -11: "NO_MEMORY",
+}
+CODES = {v: k for k, v in ERRORS.items()}
+
+# Names the header declares; the library must export every one of them.
+EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
+           "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
+           "last_error_string"]
+
+
+class PrkvError(RuntimeError):
+    def __init__(self, code, func, msg):
+        self.code = code
+        self.name = ERRORS.get(code, str(code))
+        super().__init__(f"{func}: PRKV_ERR_{self.name}: {msg}")
+
+
+class StoreDesc(ctypes.Structure):
+    _fields_ = [
+        ("num_layers", ctypes.c_int32),
+        ("num_kv_heads", ctypes.c_int32),
+        ("head_dim", ctypes.c_int32),
+        ("max_facts", ctypes.c_int32),
+        ("capacity_rows", ctypes.c_int64),
+        ("max_position", ctypes.c_int32),
+        ("rope_style", ctypes.c_int32),
+        ("rope_theta", ctypes.c_double),
+    ]
+
+
+_lib = None
+_vp = ctypes.c_void_p
+_i32p = ctypes.POINTER(ctypes.c_int32)
+_i64p = ctypes.POINTER(ctypes.c_int64)
+
+
+def lib():
+    """Load libprkv.so once; raise if it has not been built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise ImportError(
+            f"{LIB_PATH} is missing: build it with `python -m pre_rope_kv_amd.build` "
+            "(there is no fallback path)")
+    L = ctypes.CDLL(LIB_PATH)
+    sig = {
+        "store_required_bytes": (ctypes.c_int, [ctypes.POINTER(StoreDesc),
+                                                ctypes.POINTER(ctypes.c_size_t),
+                                                ctypes.POINTER(ctypes.c_size_t)]),
+        "store_create": (ctypes.c_int, [ctypes.POINTER(StoreDesc), _vp, _vp, _vp, _vp,
+                                        ctypes.POINTER(_vp)]),
+        "store_put_fact": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
+        "store_fact_info": (ctypes.c_int, [_vp, ctypes.c_int32, _i64p, _i32p]),
+        "store_destroy": (None, [_vp]),
+        "build_slot_mapping": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
+                                              ctypes.c_int32, _vp, ctypes.c_int32,
+                                              ctypes.c_int64, _vp, _vp, _vp, ctypes.c_int64,
+                                              _i64p]),
+        "inject_topk": (ctypes.c_int, [_vp, ctypes.c_int64, _vp, _vp, _vp,
+                                       ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                       ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
+        "rope_table_fill": (ctypes.c_int, [ctypes.POINTER(StoreDesc), _vp, ctypes.c_size_t]),
+        "last_error_string": (ctypes.c_char_p, []),
+    }
+    for name, (res, args) in sig.items():
+        fn = getattr(L, name)
+        fn.restype = res
+        fn.argtypes = args
+    _lib = L
+    return L
+
+
+def _check(rc, func):
+    if rc != PRKV_OK:
+        msg = lib().last_error_string().decode(errors="replace")
+        raise PrkvError(rc, func, msg)
+
+
+def _ptr(x):
+    """Raw address of a torch tensor / numpy array / int / None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    if hasattr(x, "data_ptr"):
+        return x.data_ptr()
+    if isinstance(x, np.ndarray):
+        return x.ctypes.data
+    raise TypeError(f"cannot take the address of {type(x)}")
+
+
+def _stream(s):
+    if s is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(s, int):
+        return s
+    return s.cuda_stream
+
+
+def _i32(a):
+    a = np.ascontiguousarray(a, dtype=np.int32)
+    return a
+
+
+def desc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows, max_position,
+         rope_theta, rope_style=0):
+    return StoreDesc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows,
+                     max_position, rope_style, float(rope_theta))
+
+
+def store_required_bytes(d):
+    a, r = ctypes.c_size_t(), ctypes.c_size_t()
+    _check(lib().store_required_bytes(ctypes.byref(d), ctypes.byref(a), ctypes.byref(r)),
+           "store_required_bytes")
+    return a.value, r.value
+
+
+class Store:
+    """Owns a prkv_store handle (host metadata); device memory stays the caller's."""
+
+    def __init__(self, handle, d, keepalive=()):
+        self.handle = handle
+        self.desc = d
+        self._keep = keepalive
+
+    def close(self):
+        if self.handle:
+            lib().store_destroy(self.handle)
+            self.handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
+
+
+def store_create(d, k_arena=None, v_arena=None, rope_table=None, stream=None):
+    h = _vp()
+    dev = k_arena is not None or v_arena is not None or rope_table is not None
+    s = _stream(stream) if dev else None
+    _check(lib().store_create(ctypes.byref(d), _ptr(k_arena), _ptr(v_arena), _ptr(rope_table),
+                              s, ctypes.byref(h)), "store_create")
+    return Store(h, d, keepalive=(k_arena, v_arena, rope_table))
+
+
+def store_put_fact(st, fact_id, length, k_src=None, v_src=None, stream=None):
+    s = _stream(stream) if k_src is not None else None
+    _check(lib().store_put_fact(st.handle, int(fact_id), int(length), _ptr(k_src), _ptr(v_src),
+                                s), "store_put_fact")
+
+
+def store_fact_info(st, fact_id):
+    row, ln = ctypes.c_int64(), ctypes.c_int32()
+    _check(lib().store_fact_info(st.handle, int(fact_id), ctypes.byref(row), ctypes.byref(ln)),
+           "store_fact_info")
+    return row.value, ln.value
+
+
+def store_destroy(st):
+    st.close()
+
+
+def build_slot_mapping(st, req_fact_ptr, fact_ids, start_pos, block_tables, bt_len,
+                       block_size, num_blocks, out=None):
+    """Returns (src_row, pos, slot) int32 host arrays of length n_tokens.
+
+    block_tables: int32 [n_req][bt_stride].  out: optional preallocated
+    (src_row, pos, slot) arrays (e.g. pinned) with room for the tokens.
+    """
+    req_fact_ptr, fact_ids, start_pos, bt_len = (_i32(a) for a in
+                                                 (req_fact_ptr, fact_ids, start_pos, bt_len))
+    bt = _i32(block_tables)
+    n_req = len(req_fact_ptr) - 1
+    stride = bt.shape[1] if bt.ndim == 2 else 0
+    n = ctypes.c_int64()
+    if out is None:
+        rc = lib().build_slot_mapping(st.handle, n_req, _ptr(req_fact_ptr), _ptr(fact_ids),
+                                      _ptr(start_pos), _ptr(bt), stride, _ptr(bt_len),
+                                      int(block_size), int(num_blocks), None, None, None, 0,
+                                      ctypes.byref(n))
+        if rc != CODES["BUFFER_TOO_SMALL"]:
+            _check(rc, "build_slot_mapping")
+        cap = n.value
+        out = tuple(np.empty(cap, np.int32) for _ in range(3))
+    cap = min(len(o) for o in out)
+    rc = lib().build_slot_mapping(st.handle, n_req, _ptr(req_fact_ptr), _ptr(fact_ids),
+                                  _ptr(start_pos), _ptr(bt), stride, _ptr(bt_len),
+                                  int(block_size), int(num_blocks), _ptr(out[0]), _ptr(out[1]),
+                                  _ptr(out[2]), cap, ctypes.byref(n))
+    _check(rc, "build_slot_mapping")
+    return tuple(o[:n.value] for o in out)
+
+
+def inject_topk(st, n_tokens, d_src_row, d_pos, d_slot, k_cache_layers, v_cache_layers,
+                block_size, num_blocks, d_status=None, stream=None):
+    L = len(k_cache_layers)
+    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
+    vp = (_vp * len(v_cache_layers))(*[_ptr(t) for t in v_cache_layers])
+    if len(v_cache_layers) != L or L != st.desc.num_layers:
+        raise ValueError("need one K and one V cache pointer per layer")
+    _check(lib().inject_topk(st.handle, int(n_tokens), _ptr(d_src_row), _ptr(d_pos),
+                             _ptr(d_slot), kp, vp, int(block_size), int(num_blocks),
+                             _ptr(d_status), _stream(stream)), "inject_topk")
+
+
+def rope_table_fill(d):
+    _, nbytes = store_required_bytes(d)
+    out = np.empty(nbytes // 4, np.float32)
+    _check(lib().rope_table_fill(ctypes.byref(d), out.ctypes.data, nbytes), "rope_table_fill")
+    return out.reshape(d.max_position, d.head_dim // 2, 4)

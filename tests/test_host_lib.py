@@ -1,0 +1,251 @@
+"""CPU tests of libprkv.so's host half: exports, fact table, slot mapping,
+RoPE table and every error path that can be forced without a GPU.
+
+None of these make a HIP compute call: stores are metadata-only (NULL device
+pointers), and device-side entry points are only driven into argument errors
+that are raised before anything touches the HIP runtime.
+"""
+
+import ctypes
+import os
+import re
+
+import numpy as np
+import pytest
+
+from oracle import paged, rope
+from pre_rope_kv_amd import prkv, workloads
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(__file__)), "include", "prkv.h")
+
+
+def header_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?(?:int|void|char)\s*\*?\s*(\w+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_library_exports_every_header_function():
+    names = header_functions()
+    assert "inject_topk" in names and "build_slot_mapping" in names
+    L = prkv.lib()
+    for n in names:
+        assert hasattr(L, n), f"libprkv.so does not export {n}"
+    assert sorted(prkv.EXPORTS) == names
+
+
+def test_error_codes_match_header():
+    text = open(HEADER).read()
+    for name, code in re.findall(r"PRKV_ERR_(\w+)\s*=\s*(-\d+)", text):
+        assert prkv.ERRORS[int(code)] == name
+
+
+def _desc(**kw):
+    base = dict(num_layers=2, num_kv_heads=2, head_dim=64, max_facts=16, capacity_rows=100,
+                max_position=256, rope_theta=1e4)
+    base.update(kw)
+    return prkv.desc(**base)
+
+
+def test_required_bytes():
+    d = _desc()
+    arena, table = prkv.store_required_bytes(d)
+    assert arena == 2 * 100 * 2 * 64 * 2
+    assert table == 256 * 32 * 16
+
+
+@pytest.mark.parametrize("bad", [
+    dict(num_layers=0), dict(num_layers=129), dict(num_kv_heads=0), dict(head_dim=96),
+    dict(head_dim=8), dict(head_dim=2048), dict(max_facts=0), dict(capacity_rows=0),
+    dict(capacity_rows=2**31), dict(max_position=0), dict(rope_theta=1.0),
+    dict(rope_theta=float("nan")), dict(rope_style=1),
+])
+def test_bad_descriptor(bad):
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.store_create(_desc(**bad))
+    assert ei.value.name == "INVALID_ARG"
+
+
+def test_store_create_pointer_rules():
+    d = _desc()
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.lib()  # partial device pointers
+        h = ctypes.c_void_p()
+        prkv._check(prkv.lib().store_create(ctypes.byref(d), 4096, None, None, None,
+                                            ctypes.byref(h)), "store_create")
+    assert ei.value.name == "INVALID_ARG"
+    with pytest.raises(prkv.PrkvError) as ei:
+        h = ctypes.c_void_p()
+        prkv._check(prkv.lib().store_create(ctypes.byref(d), 4104, 4096, 4096, None,
+                                            ctypes.byref(h)), "store_create")
+    assert ei.value.name == "ALIGNMENT"
+
+
+def test_fact_table_and_put_errors():
+    st = prkv.store_create(_desc())
+    prkv.store_put_fact(st, 3, 10)
+    prkv.store_put_fact(st, 0, 5)
+    assert prkv.store_fact_info(st, 3) == (0, 10)
+    assert prkv.store_fact_info(st, 0) == (10, 5)
+    cases = [((3, 4), "DUPLICATE_FACT"), ((16, 4), "CAPACITY"), ((-1, 4), "CAPACITY"),
+             ((5, 0), "INVALID_ARG"), ((5, 86), "CAPACITY")]
+    for (fid, ln), name in cases:
+        with pytest.raises(prkv.PrkvError) as ei:
+            prkv.store_put_fact(st, fid, ln)
+        assert ei.value.name == name
+    # a failed put leaves the table unchanged
+    prkv.store_put_fact(st, 5, 85)
+    assert prkv.store_fact_info(st, 5) == (15, 85)
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.store_fact_info(st, 7)
+    assert ei.value.name == "UNKNOWN_FACT"
+    # sources given to a metadata-only store
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.store_put_fact(st, 9, 1, k_src=4096, v_src=4096, stream=0)
+    assert ei.value.name == "CAPACITY"  # capacity is checked first (100 rows used)
+
+
+def test_put_sources_need_device_store():
+    st = prkv.store_create(_desc())
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.store_put_fact(st, 1, 2, k_src=4096, v_src=4096, stream=0)
+    assert ei.value.name == "NO_DEVICE"
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.store_put_fact(st, 1, 2, k_src=4096, v_src=None, stream=0)
+    assert ei.value.name == "INVALID_ARG"
+
+
+def test_inject_rejects_metadata_only_store():
+    st = prkv.store_create(_desc())
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.inject_topk(st, 1, 4096, 4096, 4096, [4096, 4096], [4096, 4096], 16, 4, stream=0)
+    assert ei.value.name == "NO_DEVICE"
+
+
+def _load_workload_store(w):
+    sp = w.spec
+    d = prkv.desc(sp.num_layers, sp.num_kv_heads, sp.head_dim, w.max_facts, w.capacity_rows,
+                  sp.max_position, sp.rope_theta)
+    st = prkv.store_create(d)
+    for f in w.put_order:
+        prkv.store_put_fact(st, f, w.length_of(f))
+    return st
+
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_slot_mapping_matches_oracle(name):
+    w = workloads.make(name)
+    st = _load_workload_store(w)
+    for f in w.put_order[:50]:
+        assert prkv.store_fact_info(st, f) == w.fact_rows[f]
+    req_ptr, ids, start, bt, bt_len = w.csr()
+    src, pos, slot = prkv.build_slot_mapping(st, req_ptr, ids, start, bt, bt_len,
+                                             w.spec.block_size, w.num_blocks)
+    o_src, o_pos, o_slot = paged.token_mapping(w.requests(), w.fact_rows, w.spec.block_size)
+    assert len(src) == w.n_tokens
+    assert np.array_equal(src, np.array(o_src, np.int32))
+    assert np.array_equal(pos, np.array(o_pos, np.int32))
+    assert np.array_equal(slot, np.array(o_slot, np.int32))
+
+
+def _small_mapping_case():
+    d = _desc(max_facts=8, capacity_rows=64, max_position=64)
+    st = prkv.store_create(d)
+    prkv.store_put_fact(st, 7, 2)   # rows 0..1
+    prkv.store_put_fact(st, 3, 3)   # rows 2..4
+    return st
+
+
+def test_slot_mapping_small_golden():
+    st = _small_mapping_case()
+    bt = np.array([[5, 2, 7, 0], [3, 1, -1, -1]], np.int32)
+    src, pos, slot = prkv.build_slot_mapping(st, [0, 2, 4], [7, 3, 3, 7], [3, 0], bt, [4, 2],
+                                             4, 8)
+    assert src.tolist() == [0, 1, 2, 3, 4, 2, 3, 4, 0, 1]
+    assert pos.tolist() == [3, 4, 5, 6, 7, 0, 1, 2, 3, 4]
+    assert slot.tolist() == [23, 8, 9, 10, 11, 12, 13, 14, 15, 4]
+
+
+@pytest.mark.parametrize("case,name", [
+    (dict(ids=[7, 5]), "UNKNOWN_FACT"),
+    (dict(ids=[7, -2]), "UNKNOWN_FACT"),
+    (dict(bt_len=[1]), "OUT_OF_RANGE"),                 # table too short
+    (dict(bt=[[5, 9, 7, 0]]), "OUT_OF_RANGE"),          # block id >= num_blocks
+    (dict(bt=[[5, -1, 7, 0]]), "OUT_OF_RANGE"),         # negative block id
+    (dict(start=[60]), "OUT_OF_RANGE"),                 # position >= max_position
+    (dict(bt=[[5, 5, 7, 0]], start=[0]), "DUPLICATE_SLOT"),
+    (dict(ids=[7, 7, 3], bt=[[1, 1, 1, 1]], start=[0]), "DUPLICATE_SLOT"),
+    (dict(start=[-1]), "INVALID_ARG"),
+    (dict(bt_len=[5]), "INVALID_ARG"),                  # longer than the stride
+    (dict(ptr=[1, 2]), "INVALID_ARG"),
+    (dict(ptr=[0, 3, 2]), "INVALID_ARG"),
+    (dict(block_size=0), "INVALID_ARG"),
+    (dict(num_blocks=2**30, block_size=4), "INVALID_ARG"),
+])
+def test_slot_mapping_errors(case, name):
+    st = _small_mapping_case()
+    ids = case.get("ids", [7, 3])
+    ptr = case.get("ptr", [0, len(ids)])
+    bt = np.array(case.get("bt", [[5, 2, 7, 0]]), np.int32)
+    n_req = len(ptr) - 1
+    start = case.get("start", [3] * n_req)
+    bt_len = case.get("bt_len", [4] * n_req)
+    if len(bt) < n_req:
+        bt = np.repeat(bt, n_req, axis=0)
+    outs = tuple(np.full(32, -7, np.int32) for _ in range(3))
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.build_slot_mapping(st, ptr, ids, start, bt, bt_len, case.get("block_size", 4),
+                                case.get("num_blocks", 8), out=outs)
+    assert ei.value.name == name
+    for o in outs:
+        assert np.all(o == -7), "outputs must be untouched on error"
+
+
+def test_slot_mapping_buffer_too_small_reports_count():
+    st = _small_mapping_case()
+    outs = tuple(np.full(3, -7, np.int32) for _ in range(3))
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.build_slot_mapping(st, [0, 2], [7, 3], [3], np.array([[5, 2, 7, 0]], np.int32),
+                                [4], 4, 8, out=outs)
+    assert ei.value.name == "BUFFER_TOO_SMALL"
+    assert all(np.all(o == -7) for o in outs)
+
+
+def test_slot_mapping_empty_and_reuse():
+    st = _small_mapping_case()
+    src, pos, slot = prkv.build_slot_mapping(st, [0], [], [], np.zeros((0, 0), np.int32), [],
+                                             4, 8)
+    assert len(src) == 0
+    # after a duplicate-slot failure the next call is clean (scratch is reset)
+    with pytest.raises(prkv.PrkvError):
+        prkv.build_slot_mapping(st, [0, 3], [7, 7, 3], [0],
+                                np.array([[1, 1, 1, 1]], np.int32), [4], 4, 8)
+    src, pos, slot = prkv.build_slot_mapping(st, [0, 1], [7], [0],
+                                             np.array([[1, 1, 1, 1]], np.int32), [4], 4, 8)
+    assert slot.tolist() == [4, 5]
+
+
+@pytest.mark.parametrize("d_model,theta", [(64, 1e4), (128, 5e5), (16, 10.0)])
+def test_rope_table_hi_lo(d_model, theta):
+    d = prkv.desc(1, 1, d_model, 1, 1, 16384, theta)
+    t = prkv.rope_table_fill(d).astype(np.float64)
+    pos = np.arange(16384)
+    w = rope.rotation_factors(pos, d_model, theta)   # float64 cos + i sin
+    ch, cl, sh, sl = t[..., 0], t[..., 1], t[..., 2], t[..., 3]
+    # hi parts are the float32 roundings; hi + lo carries ~48 bits
+    assert np.array_equal(ch, w.real.astype(np.float32).astype(np.float64))
+    assert np.array_equal(sh, w.imag.astype(np.float32).astype(np.float64))
+    assert np.max(np.abs(ch + cl - w.real)) < 2.0 ** -46
+    assert np.max(np.abs(sh + sl - w.imag)) < 2.0 ** -46
+    # position 0 is the identity rotation exactly
+    assert np.all(ch[0] == 1) and np.all(cl[0] == 0) and np.all(sh[0] == 0) and np.all(sl[0] == 0)
+
+
+def test_same_fact_twice_is_legal():
+    st = _small_mapping_case()
+    src, pos, slot = prkv.build_slot_mapping(st, [0, 2], [7, 7], [0],
+                                             np.array([[1, 2]], np.int32), [2], 4, 8)
+    assert src.tolist() == [0, 1, 0, 1]
+    assert pos.tolist() == [0, 1, 2, 3]
+    assert slot.tolist() == [4, 5, 6, 7]
