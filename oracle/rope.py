@@ -15,6 +15,7 @@ Readings (the pages give no formula):
 * Positions are 0-based integers; position 0 is the identity.
 """
 
+import functools
 from decimal import Decimal, localcontext
 
 import numpy as np
@@ -27,7 +28,13 @@ def inv_freq(head_dim, base):
     the float64 nearest the exact power on every machine (a vectorised float64
     power is not correctly rounded on every CPU, and an ulp in theta_j moves
     the angle pos * theta_j by up to ~2e-12 at the positions used here).
+    The values depend only on (D, base) and are memoised.
     """
+    return _inv_freq(int(head_dim), float(base)).copy()
+
+
+@functools.lru_cache(maxsize=64)
+def _inv_freq(head_dim, base):
     if head_dim % 2:
         raise ValueError("head_dim must be even")
     with localcontext() as ctx:

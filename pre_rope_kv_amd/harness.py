@@ -1,0 +1,150 @@
+"""Device setup for a synthetic workload: what a serving engine's KV connector
+does around the library.
+
+Allocates the store arenas, the RoPE table and the paged cache with torch
+(device memory only), puts every resident fact through store_put_fact,
+builds the slot mapping with build_slot_mapping and copies it to the device,
+and launches inject_topk.  All arithmetic of the path runs in libprkv.so.
+"""
+
+from __future__ import annotations
+
+import math
+
+import numpy as np
+import torch
+
+from . import prkv, workloads
+
+GiB = 1 << 30
+
+
+def cache_bytes(spec, num_blocks):
+    return 2 * spec.num_layers * num_blocks * spec.block_size * spec.row_bytes
+
+
+def fit_num_blocks(spec, reserve_bytes, device="cuda", margin=6 * GiB):
+    """Largest block count <= spec.num_blocks whose K+V cache fits next to
+    `reserve_bytes` of other allocations, rounded down to a multiple of 1024."""
+    free, _ = torch.cuda.mem_get_info(device)
+    per_block = cache_bytes(spec, 1)
+    fit = (free - reserve_bytes - margin) // per_block
+    if fit >= spec.num_blocks:
+        return spec.num_blocks
+    return int(fit // 1024 * 1024)
+
+
+class DeviceWorkload:
+    """A workload resident on one GPU: store, cache, mapping."""
+
+    def __init__(self, w: workloads.Workload, device="cuda", gen_device=None, stream=None):
+        self.w = w
+        sp = w.spec
+        self.device = torch.device(device)
+        self.gen_device = gen_device or self.device
+        self.stream = stream or torch.cuda.current_stream(self.device)
+        self.desc = prkv.desc(sp.num_layers, sp.num_kv_heads, sp.head_dim, w.max_facts,
+                              w.capacity_rows, sp.max_position, sp.rope_theta)
+        arena_bytes, rope_bytes = prkv.store_required_bytes(self.desc)
+        shape = (sp.num_layers, w.capacity_rows, sp.num_kv_heads, sp.head_dim)
+        self.k_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
+        self.v_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
+        self.rope = torch.empty(rope_bytes // 4, dtype=torch.float32, device=self.device)
+        assert self.k_arena.numel() * 2 == arena_bytes
+        self.store = prkv.store_create(self.desc, self.k_arena, self.v_arena, self.rope,
+                                       stream=self.stream)
+        self._put_all()
+        cshape = (sp.num_layers, w.num_blocks, sp.block_size, sp.num_kv_heads, sp.head_dim)
+        self.k_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
+        self.v_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
+        self.reset_cache()
+        self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
+        self.build_mapping()
+
+    # -- store -------------------------------------------------------------
+    def _put_all(self, batch=64):
+        w = self.w
+        pending = []
+        with torch.cuda.stream(self.stream):
+            for f in w.put_order:
+                k, v = w.fact_kv(f, device=self.gen_device)
+                if k.device != self.device:
+                    k, v = k.to(self.device), v.to(self.device)
+                prkv.store_put_fact(self.store, f, w.length_of(f), k, v, stream=self.stream)
+                pending.append((k, v))
+                if len(pending) >= batch:
+                    self.stream.synchronize()
+                    pending.clear()
+        self.stream.synchronize()
+
+    # -- cache -------------------------------------------------------------
+    def reset_cache(self):
+        with torch.cuda.stream(self.stream):
+            self.k_cache.fill_(workloads.SENTINEL_BF16)
+            self.v_cache.fill_(workloads.SENTINEL_BF16)
+
+    def k_layers(self):
+        return [self.k_cache[l] for l in range(self.w.spec.num_layers)]
+
+    def v_layers(self):
+        return [self.v_cache[l] for l in range(self.w.spec.num_layers)]
+
+    # -- mapping -----------------------------------------------------------
+    def build_mapping(self):
+        w = self.w
+        req_ptr, ids, start, bt, bt_len = w.csr()
+        self.req_ptr, self.ids, self.start, self.bt, self.bt_len = req_ptr, ids, start, bt, bt_len
+        n = w.n_tokens
+        self.h_map = [torch.empty(max(n, 1), dtype=torch.int32, pin_memory=True)
+                      for _ in range(3)]
+        src, pos, slot = prkv.build_slot_mapping(
+            self.store, req_ptr, ids, start, bt, bt_len, w.spec.block_size, w.num_blocks,
+            out=tuple(t.numpy() for t in self.h_map))
+        self.n_tokens = len(src)
+        self.d_map = [t.to(self.device, non_blocking=True) for t in self.h_map]
+        self.stream.synchronize()
+        return src, pos, slot
+
+    def map_and_copy(self):
+        """Host slot mapping into pinned buffers + async H2D of the three arrays."""
+        w = self.w
+        prkv.build_slot_mapping(self.store, self.req_ptr, self.ids, self.start, self.bt,
+                                self.bt_len, w.spec.block_size, w.num_blocks,
+                                out=tuple(t.numpy() for t in self.h_map))
+        with torch.cuda.stream(self.stream):
+            for d, h in zip(self.d_map, self.h_map):
+                d.copy_(h, non_blocking=True)
+
+    # -- inject ------------------------------------------------------------
+    def inject(self):
+        prkv.inject_topk(self.store, self.n_tokens, self.d_map[0], self.d_map[1], self.d_map[2],
+                         self.k_layers(), self.v_layers(), self.w.spec.block_size,
+                         self.w.num_blocks, d_status=self.status, stream=self.stream)
+
+    def inject_args(self):
+        """Pre-marshalled arguments for tight timing loops."""
+        import ctypes
+        L = self.w.spec.num_layers
+        kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.k_layers()])
+        vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.v_layers()])
+        return (self.store.handle, self.n_tokens, self.d_map[0].data_ptr(),
+                self.d_map[1].data_ptr(), self.d_map[2].data_ptr(), kp, vp,
+                self.w.spec.block_size, self.w.num_blocks, self.status.data_ptr(),
+                self.stream.cuda_stream)
+
+    # -- reading back ------------------------------------------------------
+    def listed_blocks_host(self, blocks):
+        """K and V cache contents of the given blocks, all layers, as uint16 numpy."""
+        idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
+        k = self.k_cache.index_select(1, idx).cpu().numpy().view(np.uint16)
+        v = self.v_cache.index_select(1, idx).cpu().numpy().view(np.uint16)
+        return k, v
+
+    def count_non_sentinel(self, chunk_elems=1 << 28):
+        """Number of cache elements (K and V, all layers) != the sentinel."""
+        total = 0
+        for cache in (self.k_cache, self.v_cache):
+            flat = cache.view(-1)
+            for s in range(0, flat.numel(), chunk_elems):
+                total += int((flat[s:s + chunk_elems] != workloads.SENTINEL_BF16).sum().item())
+        return total
