@@ -36,27 +36,151 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
+                    help="turn rocprofv3 output of this script into profiles/<kernel>_<workload>.md")
     return ap.parse_args()
 
 
+KERNEL_SOURCE = os.path.join(ROOT, "pre_rope_kv_amd", "csrc", "prkv_inject.hip")
+KERNEL_NAME = "inject_kernel"
+
+
+def kernel_source_sha():
+    import hashlib
+    with open(KERNEL_SOURCE, "rb") as fh:
+        return hashlib.sha256(fh.read()).hexdigest()[:16]
+
+
+def profile_path(workload):
+    return os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}.md")
+
+
+def read_profile_traffic(workload):
+    """HBM bytes per launch from the committed counter summary, or None when
+    there is none or the kernel source changed since it was taken."""
+    path = profile_path(workload)
+    if not os.path.exists(path):
+        return None
+    fields = {}
+    with open(path) as fh:
+        for line in fh:
+            if line.startswith("- ") and ": " in line:
+                k, v = line[2:].split(": ", 1)
+                fields[k.strip()] = v.strip().strip("`")
+    if fields.get("kernel_source_sha256") != kernel_source_sha():
+        return None
+    try:
+        return int(fields["traffic_bytes_per_launch"])
+    except (KeyError, ValueError):
+        return None
+
+
+def summarize_profile(workload, trace_dir, fetch_dir, write_dir, commands):
+    """Write the rocprofv3 summary for the inject kernel.
+
+    Counter calibration: the 4 GiB device-to-device memcpy of copy_ceiling_gbps
+    (__amd_rocclr_copyBuffer, known to read 4 GiB and write 4 GiB) is looked up
+    in the same counter runs; FETCH_SIZE and WRITE_SIZE of the inject kernel
+    are scaled by (4 GiB / what the counter reads for that copy).
+    """
+    import csv
+    import glob
+    import statistics
+
+    def rows(d, suffix):
+        files = glob.glob(os.path.join(d, f"*{suffix}"))
+        if not files:
+            raise FileNotFoundError(f"no *{suffix} under {d}")
+        with open(files[0]) as fh:
+            return list(csv.DictReader(fh))
+
+    stats = [r for r in rows(trace_dir, "kernel_stats.csv") if r["Name"].startswith(KERNEL_NAME)]
+    trace = [r for r in rows(trace_dir, "kernel_trace.csv")
+             if r["Kernel_Name"].startswith(KERNEL_NAME)]
+    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
+    copy_kib = 4 * 1024 * 1024
+
+    def counter(d, name):
+        rs = rows(d, "counter_collection.csv")
+        inj = [float(r["Counter_Value"]) for r in rs if r["Kernel_Name"].startswith(KERNEL_NAME)
+               and r["Counter_Name"] == name]
+        cal = [float(r["Counter_Value"]) for r in rs
+               if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")
+               and r["Kernel_Name"].strip() == "__amd_rocclr_copyBuffer"
+               and r["Counter_Name"] == name and float(r["Counter_Value"]) > copy_kib / 4]
+        return statistics.mean(inj), statistics.mean(cal), len(inj), len(cal)
+
+    f_inj, f_cal, nf, ncf = counter(fetch_dir, "FETCH_SIZE")
+    w_inj, w_cal, nw, ncw = counter(write_dir, "WRITE_SIZE")
+    f_scale, w_scale = copy_kib / f_cal, copy_kib / w_cal
+    fetch_b = f_inj * f_scale * 1024
+    write_b = w_inj * w_scale * 1024
+    from pre_rope_kv_amd import workloads
+    w = workloads.make(workload)
+    alg = w.n_tokens * w.spec.bytes_per_token
+    st = stats[0]
+    lines = [
+        f"# {KERNEL_NAME} on {workload} (MI355X, gfx950)",
+        "",
+        "rocprofv3 summaries of `bench.py` on one MI355X; raw CSVs stay in the run's",
+        "output directory.  Commands (from the repository root):",
+        "",
+    ] + [f"    {c}" for c in commands] + [
+        "",
+        "## Kernel trace (--kernel-trace --stats)",
+        "",
+        f"- calls: {st['Calls']}",
+        f"- average_ms: {float(st['AverageNs']) / 1e6:.4f}",
+        f"- min_ms: {float(st['MinNs']) / 1e6:.4f}",
+        f"- max_ms: {float(st['MaxNs']) / 1e6:.4f}",
+        f"- median_ms_from_trace: {statistics.median(durs):.4f}",
+        f"- share_of_gpu_time_in_run_pct: {float(st['Percentage']):.2f}",
+        "",
+        "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs)",
+        "",
+        "Calibration: the 4 GiB device-to-device memcpy (`__amd_rocclr_copyBuffer`)",
+        "in the same runs reads 4 GiB and writes 4 GiB by construction.",
+        "",
+        f"- fetch_size_kib_per_launch_raw: {f_inj:.0f} (mean of {nf} launches)",
+        f"- fetch_size_kib_for_4GiB_copy: {f_cal:.0f} (mean of {ncf}); scale {f_scale:.4f}",
+        f"- write_size_kib_per_launch_raw: {w_inj:.0f} (mean of {nw} launches)",
+        f"- write_size_kib_for_4GiB_copy: {w_cal:.0f} (mean of {ncw}); scale {w_scale:.4f}",
+        f"- fetch_bytes_per_launch: {fetch_b:.0f}",
+        f"- write_bytes_per_launch: {write_b:.0f}",
+        f"- traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+        f"- algorithmic_bytes_per_launch: {alg}",
+        f"- traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
+        f"- kernel_source_sha256: `{kernel_source_sha()}`",
+        "",
+    ]
+    with open(profile_path(workload), "w") as fh:
+        fh.write("\n".join(lines))
+    print(profile_path(workload))
+
+
 def copy_ceiling_gbps(torch, nbytes=4 << 30, reps=10):
-    """Device-to-device copy rate (read + write bytes / time) for context."""
+    """Read + write bytes / time of two plain copies of `nbytes`, for context:
+    a device-to-device memcpy, and an elementwise int16 negate kernel (whose
+    FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-traffic counters)."""
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
     dst = torch.empty_like(src)
     src.fill_(1)
-    for _ in range(2):
-        dst.copy_(src)
-    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    s.record()
-    for _ in range(reps):
-        dst.copy_(src)
-    e.record()
-    torch.cuda.synchronize()
-    ms = s.elapsed_time(e) / reps
+    out = {}
+    for name, fn in (("memcpy", lambda: dst.copy_(src)),
+                     ("elementwise_neg", lambda: torch.neg(src, out=dst))):
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(reps):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        out[name] = 2 * nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
-    return 2 * nbytes / (ms * 1e-3) / 1e9
+    return out
 
 
 def cpu_baseline(w, budget_s):
@@ -111,6 +235,22 @@ def cpu_baseline(w, budget_s):
 
 def main():
     args = parse()
+    if args.summarize_profile:
+        trace_dir, fetch_dir, write_dir = args.summarize_profile
+        cmds = [
+            f"rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o inject -f csv -- "
+            "python -u bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-e2e",
+            f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"inject_kernel|copyBuffer\" "
+            f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py --steps 3 --warmup 1 "
+            "--no-cpu-baseline --no-e2e",
+            f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"inject_kernel|copyBuffer\" "
+            f"-T -d {write_dir} -o write -f csv -- python -u bench.py --steps 3 --warmup 1 "
+            "--no-cpu-baseline --no-e2e",
+            f"python bench.py --workload {args.workload} --summarize-profile {trace_dir} "
+            f"{fetch_dir} {write_dir}",
+        ]
+        summarize_profile(args.workload, trace_dir, fetch_dir, write_dir, cmds)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
@@ -162,6 +302,7 @@ def main():
 
     n_tok = dw.n_tokens
     alg_bytes = n_tok * spec.bytes_per_token
+    traffic = read_profile_traffic(spec.name) if w is w0 else None
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
 
     e2e = None
@@ -202,13 +343,13 @@ def main():
         },
         "hbm_gbps": achieved,
         "pct_of_peak": 100.0 * achieved / PEAK_HBM_GBPS,
-        "pct_of_copy_ceiling": 100.0 * achieved / ceiling,
+        "pct_of_copy_ceiling": 100.0 * achieved / max(ceiling.values()),
         "copy_ceiling_gbps": ceiling,
         "kernel_ms": {"mean": kernel_ms, "p10": per_ms[len(per_ms) // 10],
                       "median": per_ms[len(per_ms) // 2], "p90": per_ms[(9 * len(per_ms)) // 10]},
         "roofline": {
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
-            "frac": achieved / PEAK_HBM_GBPS, "traffic": None,
+            "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
             "kernel": "inject_kernel<128>",
             "bytes_per_launch": alg_bytes,
         },
