@@ -36,6 +36,9 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--flush", action="store_true",
+                    help="evict the 256 MB Infinity Cache with a 1 GiB fill before every timed "
+                         "launch and time launches one by one (for workloads far below 1 GiB)")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 output of this script into profiles/<kernel>_<workload>.md")
     return ap.parse_args()
@@ -183,6 +186,14 @@ def copy_ceiling_gbps(torch, nbytes=4 << 30, reps=10):
     return out
 
 
+def device_info(torch):
+    import socket
+    p = torch.cuda.get_device_properties(0)
+    return {"name": p.name, "gcn_arch": getattr(p, "gcnArchName", ""),
+            "cus": p.multi_processor_count, "hbm_gib": round(p.total_memory / 2**30, 1),
+            "host": socket.gethostname()}
+
+
 def cpu_baseline(w, budget_s):
     """The CPU oracle, as it stands, on a bounded sample of the same workload:
     facts of the requests in order, all layers, until the budget is spent."""
@@ -287,18 +298,38 @@ def main():
     torch.cuda.synchronize()
     assert int(dw.status.item()) == 0
 
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    evs[0].record(stream)
-    for i in range(args.steps):
-        step()
-        evs[i + 1].record(stream)
-    torch.cuda.synchronize()
-    wall_s = time.perf_counter() - t0
-    per_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
-    kernel_ms = evs[0].elapsed_time(evs[args.steps]) / args.steps
-    ms_per_step = max(wall_s * 1e3 / args.steps, kernel_ms)
+    if args.flush:
+        # launches timed one by one, each after a 1 GiB fill that evicts the MALL
+        scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for i in range(args.steps):
+            with torch.cuda.stream(stream):
+                scratch.fill_(i)
+            starts[i].record(stream)
+            step()
+            ends[i].record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        per_ms = sorted(starts[i].elapsed_time(ends[i]) for i in range(args.steps))
+        kernel_ms = sum(per_ms) / len(per_ms)
+        ms_per_step = kernel_ms
+        del scratch
+    else:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        evs[0].record(stream)
+        for i in range(args.steps):
+            step()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        wall_s = time.perf_counter() - t0
+        per_ms = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(args.steps))
+        kernel_ms = evs[0].elapsed_time(evs[args.steps]) / args.steps
+        ms_per_step = max(wall_s * 1e3 / args.steps, kernel_ms)
 
     n_tok = dw.n_tokens
     alg_bytes = n_tok * spec.bytes_per_token
@@ -356,6 +387,9 @@ def main():
         "cpu_baseline": cpu,
         "e2e": e2e,
         "setup_s": setup_s,
+        "timing": "per-launch events after a 1 GiB MALL flush" if args.flush
+                  else "back-to-back launches, events around the batch",
+        "device": device_info(torch),
     }
     print(json.dumps(out), flush=True)
 

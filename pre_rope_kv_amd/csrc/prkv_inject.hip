@@ -14,8 +14,12 @@
 // rotation is a few fp32 VALU operations per element, far below the ridge.
 //
 // Work layout
-//  - A workgroup is 4 waves (256 lanes) and owns a tile of 4*TPW tokens and
-//    a contiguous share ("split") of each token's chunk range.
+//  - A workgroup is 4 waves (256 lanes) and owns a tile of 4 consecutive
+//    tokens, one per wave, and a contiguous share ("split") of each token's
+//    chunk range; small batches use several splits per token so the grid
+//    still covers the chip.  (Measured on MI355X: one token per wave beats
+//    2, 4 or 8 per wave, and 4-wave groups beat 8- or 16-wave groups on the
+//    large batches.)
 //  - A token's work is L*H*D/16 "chunks"; chunk (l, h, c) covers 8 RoPE
 //    pairs: 16 bytes at element h*D + 8c (first half of the head) and 16
 //    bytes at h*D + D/2 + 8c (second half).  A lane owns whole pairs, so no
@@ -74,8 +78,7 @@ struct InjectParams {
   int32_t max_position;
   int32_t num_layers;
   int32_t num_heads;
-  int64_t n_tiles;           // tiles of 4*TPW tokens
-  int32_t tokens_per_wave;   // TPW
+  int64_t n_tiles;           // tiles of kWavesPerGroup tokens
   int32_t n_splits;          // workgroups per tile
   int32_t iters_per_split;   // 64-chunk iterations per split
 };
@@ -135,8 +138,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   constexpr int HALF = D / 2;   // pairs per head
   extern __shared__ f32x4 smem[];
 
-  const int tpw = p.tokens_per_wave;
-  const int tile_tokens = kWavesPerGroup * tpw;
+  constexpr int tile_tokens = kWavesPerGroup;   // one token per wave
   const int split = blockIdx.x % p.n_splits;
   const int64_t tile_stride = gridDim.x / p.n_splits;
   int* meta = reinterpret_cast<int*>(smem + tile_tokens * HALF);  // row, pos, slot
@@ -190,16 +192,14 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     }
     __syncthreads();
 
-    // 3. Each wave streams its tokens through every layer of its split.
-    for (int ti = 0; ti < tpw; ++ti) {
-      const int i = wave * tpw + ti;
-      const int row = __builtin_amdgcn_readfirstlane(meta[3 * i + 0]);
-      if (row < 0) continue;
-      const int slot = __builtin_amdgcn_readfirstlane(meta[3 * i + 2]);
+    // 3. Each wave streams its token through every layer of its split.
+    const int row = __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
+    if (row >= 0) {
+      const int slot = __builtin_amdgcn_readfirstlane(meta[3 * wave + 2]);
 
       f32x4 cs[8];
 #pragma unroll
-      for (int k = 0; k < 8; ++k) cs[k] = smem[i * HALF + k * CPH + c];
+      for (int k = 0; k < 8; ++k) cs[k] = smem[wave * HALF + k * CPH + c];
 
       for (int it = it0; it < it1; it += kUnroll) {
         u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
@@ -376,17 +376,13 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
     vc.p[l] = static_cast<uint16_t*>(v_cache_layers[l]);
   }
 
-  // Launch shape: tiles of 4*TPW tokens; split each token's chunk range
-  // across workgroups until the grid holds enough waves to cover the chip.
+  // Launch shape: tiles of 4 tokens; split each token's chunk range across
+  // workgroups until the grid holds enough waves to cover the chip.
   const int D = d.head_dim;
   const int64_t chunks = int64_t(d.num_layers) * d.num_kv_heads * (D / 16);
   const int iters = int((chunks + kWave - 1) / kWave);
   const int64_t want_waves = int64_t(compute_units()) * 16;
-  int tpw = 4;
-  while (tpw > 1 && (n_tokens + 4 * tpw - 1) / (4 * tpw) * 4 < want_waves) tpw /= 2;
-  // LDS: 8*D bytes of cos/sin per token, keep a tile under 32 KiB
-  while (tpw > 1 && int64_t(kWavesPerGroup) * tpw * D * 8 > 32768) tpw /= 2;
-  const int64_t tiles = (n_tokens + kWavesPerGroup * tpw - 1) / (kWavesPerGroup * tpw);
+  const int64_t tiles = (n_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
   int n_splits = 1;
   while (n_splits < iters && tiles * n_splits * kWavesPerGroup < want_waves) n_splits *= 2;
   if (n_splits > iters) n_splits = iters;
@@ -397,7 +393,7 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
   const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
                                                                     : (int64_t(1) << 20) / n_splits;
   const int64_t grid = grid_tiles * n_splits;
-  const size_t lds = size_t(kWavesPerGroup) * tpw * (size_t(D / 2) * 16 + 12);
+  const size_t lds = size_t(kWavesPerGroup) * (size_t(D / 2) * 16 + 12);
 
   InjectParams p;
   p.k_arena = static_cast<const uint16_t*>(st->k_arena);
@@ -414,7 +410,6 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
   p.num_layers = d.num_layers;
   p.num_heads = d.num_kv_heads;
   p.n_tiles = tiles;
-  p.tokens_per_wave = tpw;
   p.n_splits = n_splits;
   p.iters_per_split = per;
 
