@@ -155,7 +155,8 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
  * [num_blocks][block_size][H][D] bf16 tensor.  d_status: optional device
  * int32; if non-NULL the kernel ORs 1 (row out of range), 2 (position out of
  * range) or 4 (slot out of range) into it for any token it skipped; tokens
- * out of range are never read or written.  n_tokens == 0 is a no-op.
+ * out of range are never read or written, and a row of -1 skips a token
+ * silently.  n_tokens == 0 is a no-op.
  * Asynchronous on `stream`; never synchronizes.  Slots must be distinct
  * (build_slot_mapping guarantees it); otherwise the result is undefined. */
 int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row,
@@ -163,6 +164,67 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
                 void* const* k_cache_layers, void* const* v_cache_layers,
                 int32_t block_size, int64_t num_blocks, int32_t* d_status,
                 void* stream);
+
+/* Device-resident description of a batch of requests (all pointers are
+ * device memory, int32): request r has facts fact_ids[req_fact_ptr[r] ..
+ * req_fact_ptr[r+1]) in rank order, a prefix of start_pos[r] tokens, and
+ * block table block_tables[r*bt_stride .. + bt_len[r]).  max_facts bounds
+ * req_fact_ptr[n_req]; max_tokens bounds the injected token count and sizes
+ * the workspace. */
+typedef struct prkv_device_batch {
+  int32_t n_req;
+  int32_t bt_stride;
+  int32_t max_facts;
+  int32_t pad_;
+  int64_t max_tokens;
+  const int32_t* req_fact_ptr;  /* [n_req + 1] */
+  const int32_t* fact_ids;      /* [req_fact_ptr[n_req]] */
+  const int32_t* start_pos;     /* [n_req] */
+  const int32_t* block_tables;  /* [n_req][bt_stride] */
+  const int32_t* bt_len;        /* [n_req] */
+} prkv_device_batch;
+
+/* Copy the store's fact table into caller-owned device memory for
+ * inject_topk_device: [max_facts] x (int32 first row or -1 when absent,
+ * int32 length), table_bytes >= 8 * max_facts, 8-byte aligned.  The copy is
+ * complete when the call returns.  Call again after further puts.
+ * Source: InferScale review, Figure 2 caption (top-k ids resolved to their
+ * KV by fact_id on the GPU). */
+int store_upload_fact_table(const prkv_store* st, void* d_table, size_t table_bytes,
+                            void* stream);
+
+/* Workspace bytes inject_topk_device needs for the given bounds.  Layout
+ * (all offsets 256-byte aligned): int64 token count at 0, int32 fact count
+ * at 8; per-fact plan (16 bytes each) at 256; then the per-token arrays
+ * src_row, pos, slot (int32 [max_tokens] each) -- the same mapping
+ * build_slot_mapping produces on the host, valid after the call's kernels
+ * have run (a row of -1 marks a token that failed validation). */
+int inject_device_workspace_bytes(int32_t max_facts, int64_t max_tokens, size_t* bytes);
+
+/* The whole retrieve-and-inject step on the device, from a batch resident in
+ * HBM: resolve fact ids through the device fact table, place each request's
+ * facts after its prefix in rank order, map positions to slots through its
+ * block table, then gather, rotate and scatter exactly as inject_topk.
+ * Source: as build_slot_mapping and inject_topk (InferScale review, "If this
+ * is right" bullet 2, KV-connector axiom of section 3.4, "What carries the
+ * argument", "Referee Report" Summary).
+ * Three kernels on `stream` (plan, per-token mapping, inject); asynchronous,
+ * never synchronizes.  d_workspace: caller-owned device memory of
+ * inject_device_workspace_bytes(batch->max_facts, batch->max_tokens), 256-byte
+ * aligned; d_fact_table from store_upload_fact_table.  Invalid input found on
+ * the device never faults: the token is skipped and d_status (optional) gets
+ * 2 (position out of range), 4 (block table too short or block id out of
+ * range), 8 (unknown fact id), 16 (more than max_tokens tokens; the excess is
+ * dropped) or 32 (more than max_facts facts).  Duplicate slots are NOT
+ * detected on the device (block tables from one allocator never overlap);
+ * build_slot_mapping checks them on the host.  Host-side argument errors
+ * return INVALID_ARG / ALIGNMENT / BUFFER_TOO_SMALL / NO_DEVICE with nothing
+ * enqueued. */
+int inject_topk_device(const prkv_store* st, const void* d_fact_table,
+                       const prkv_device_batch* batch, void* const* k_cache_layers,
+                       void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
+                       void* d_workspace, size_t workspace_bytes, int32_t* d_status,
+                       void* stream);
 
 /* Fill a HOST buffer with the RoPE table store_create would upload:
  * [max_position][D/2][4] float32 = (cos_hi, cos_lo, sin_hi, sin_lo) with

@@ -72,13 +72,13 @@ struct InjectParams {
   const int32_t* pos;
   const int32_t* slot;
   int32_t* status;
+  const int64_t* n_tokens_dev;  // when set, the token count is min(*n_tokens_dev, n_tokens)
   int64_t n_tokens;
   int64_t capacity_rows;
   int64_t num_slots;
   int32_t max_position;
   int32_t num_layers;
   int32_t num_heads;
-  int64_t n_tiles;           // tiles of kWavesPerGroup tokens
   int32_t n_splits;          // workgroups per tile
   int32_t iters_per_split;   // 64-chunk iterations per split
 };
@@ -139,6 +139,12 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   extern __shared__ f32x4 smem[];
 
   constexpr int tile_tokens = kWavesPerGroup;   // one token per wave
+  int64_t n_tokens = p.n_tokens;
+  if (p.n_tokens_dev) {
+    const int64_t dev = *p.n_tokens_dev;
+    n_tokens = dev < n_tokens ? (dev < 0 ? 0 : dev) : n_tokens;
+  }
+  const int64_t n_tiles = (n_tokens + tile_tokens - 1) / tile_tokens;
   const int split = blockIdx.x % p.n_splits;
   const int64_t tile_stride = gridDim.x / p.n_splits;
   int* meta = reinterpret_cast<int*>(smem + tile_tokens * HALF);  // row, pos, slot
@@ -156,22 +162,23 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   const int64_t row_elems = int64_t(H) * D;
   const int64_t layer_elems = p.capacity_rows * row_elems;
 
-  for (int64_t tile = blockIdx.x / p.n_splits; tile < p.n_tiles; tile += tile_stride) {
+  for (int64_t tile = blockIdx.x / p.n_splits; tile < n_tiles; tile += tile_stride) {
     const int64_t tok0 = tile * tile_tokens;
     __syncthreads();  // LDS of the previous tile is no longer read
 
-    // 1. Wave-wide gather of the tile's (row, pos, slot); out-of-range tokens
-    //    are marked row = -1 and skipped.
+    // 1. Wave-wide gather of the tile's (row, pos, slot); a row of -1 marks a
+    //    token to skip, other out-of-range tokens are reported and skipped.
     for (int i = threadIdx.x; i < tile_tokens; i += kThreads) {
       const int64_t t = tok0 + i;
       int row = -1, pos = 0, slot = 0;
-      if (t < p.n_tokens) {
+      if (t < n_tokens) {
         row = p.src_row[t];
         pos = p.pos[t];
         slot = p.slot[t];
-        const int bad = ((row < 0 || row >= p.capacity_rows) ? 1 : 0) |
-                        ((pos < 0 || pos >= p.max_position) ? 2 : 0) |
-                        ((slot < 0 || slot >= p.num_slots) ? 4 : 0);
+        const int bad = row == -1 ? 0
+                        : ((row < 0 || row >= p.capacity_rows) ? 1 : 0) |
+                          ((pos < 0 || pos >= p.max_position) ? 2 : 0) |
+                          ((slot < 0 || slot >= p.num_slots) ? 4 : 0);
         if (bad) {
           if (p.status && split == 0) atomicOr(p.status, bad);
           row = -1;
@@ -242,6 +249,154 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   }
 }
 
+
+// ---------------------------------------------------------------------------
+// Device-side slot mapping (fact ids and block tables resident in HBM).
+//
+// plan_kernel (one workgroup): per fact of the batch, in request and rank
+// order, look up (first row, length) in the device fact table and scan the
+// lengths: tok_start = number of injected tokens before the fact.
+// materialize_kernel (one wave per fact): find the fact's request, place it
+// after the request's prefix and earlier facts (dynamic top-k assembly),
+// and write each token's (arena row, position, slot) with full validation;
+// a token that fails is written with row -1 (skipped by the inject kernel).
+// ---------------------------------------------------------------------------
+
+struct FactPlan {
+  int32_t tok_start, row0, len, pad;
+};
+
+struct DeviceBatch {
+  const int32_t* req_fact_ptr;
+  const int32_t* fact_ids;
+  const int32_t* start_pos;
+  const int32_t* block_tables;
+  const int32_t* bt_len;
+  const int2* fact_table;      // [store max_facts] (first row or -1, length)
+  FactPlan* plan;              // workspace
+  int64_t* n_tokens_out;       // workspace header
+  int32_t* n_facts_out;        // workspace header
+  int32_t* src_row;            // workspace, [max_tokens]
+  int32_t* pos;
+  int32_t* slot;
+  int32_t* status;
+  int64_t max_tokens;
+  int64_t num_blocks;
+  int32_t n_req;
+  int32_t bt_stride;
+  int32_t max_facts_batch;
+  int32_t store_max_facts;
+  int32_t block_size;
+  int32_t max_position;
+};
+
+constexpr int kPlanThreads = 1024;
+
+__device__ __forceinline__ void flag(int32_t* status, int bits) {
+  if (status) atomicOr(status, bits);
+}
+
+__global__ __launch_bounds__(kPlanThreads) void plan_kernel(DeviceBatch b) {
+  __shared__ int wave_sums[kPlanThreads / kWave];
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  int n_facts = b.n_req > 0 ? b.req_fact_ptr[b.n_req] : 0;
+  if (n_facts < 0 || n_facts > b.max_facts_batch) {
+    if (tid == 0) flag(b.status, 32);
+    n_facts = n_facts < 0 ? 0 : b.max_facts_batch;
+  }
+  int64_t carry = 0;
+  for (int base = 0; base < n_facts; base += kPlanThreads) {
+    const int i = base + tid;
+    int len = 0, row0 = -1;
+    if (i < n_facts) {
+      const int f = b.fact_ids[i];
+      if (f >= 0 && f < b.store_max_facts) {
+        const int2 e = b.fact_table[f];
+        if (e.x >= 0 && e.y > 0) {
+          row0 = e.x;
+          len = e.y;
+        }
+      }
+      if (len == 0) flag(b.status, 8);
+    }
+    int x = len;  // inclusive scan within the wave
+#pragma unroll
+    for (int d = 1; d < kWave; d <<= 1) {
+      const int y = __shfl_up(x, d, kWave);
+      if (lane >= d) x += y;
+    }
+    if (lane == kWave - 1) wave_sums[wave] = x;
+    __syncthreads();
+    if (wave == 0) {
+      int s = lane < kPlanThreads / kWave ? wave_sums[lane] : 0;
+#pragma unroll
+      for (int d = 1; d < kPlanThreads / kWave; d <<= 1) {
+        const int y = __shfl_up(s, d, kWave);
+        if (lane >= d) s += y;
+      }
+      if (lane < kPlanThreads / kWave) wave_sums[lane] = s;
+    }
+    __syncthreads();
+    const int64_t excl = carry + (wave > 0 ? wave_sums[wave - 1] : 0) + x - len;
+    if (i < n_facts) {
+      FactPlan pl;
+      pl.tok_start = int32_t(excl < b.max_tokens ? excl : b.max_tokens);
+      pl.row0 = row0;
+      pl.len = len;
+      pl.pad = 0;
+      b.plan[i] = pl;
+    }
+    carry += wave_sums[kPlanThreads / kWave - 1];
+    __syncthreads();  // wave_sums is reused by the next chunk
+  }
+  if (tid == 0) {
+    if (carry > b.max_tokens) flag(b.status, 16);
+    *b.n_tokens_out = carry < b.max_tokens ? carry : b.max_tokens;
+    *b.n_facts_out = n_facts;
+  }
+}
+
+__global__ __launch_bounds__(kThreads) void materialize_kernel(DeviceBatch b) {
+  const int fi = blockIdx.x * kWavesPerGroup + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  if (fi >= *b.n_facts_out) return;
+  const FactPlan pl = b.plan[fi];
+  if (pl.len <= 0) return;
+  // request of fact fi: the last r with req_fact_ptr[r] <= fi
+  int lo = 0, hi = b.n_req - 1;
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (b.req_fact_ptr[mid] <= fi) lo = mid; else hi = mid - 1;
+  }
+  const int r = lo;
+  int first = b.req_fact_ptr[r];
+  if (first < 0 || first > fi) first = fi;
+  const int64_t pos0 = int64_t(b.start_pos[r]) + (pl.tok_start - b.plan[first].tok_start);
+  const int32_t* bt = b.block_tables + int64_t(r) * b.bt_stride;
+  const int nb = b.bt_len[r];
+  for (int t = lane; t < pl.len; t += kWave) {
+    const int64_t tok = int64_t(pl.tok_start) + t;
+    if (tok >= b.max_tokens) break;
+    const int64_t ps = pos0 + t;
+    int row = pl.row0 + t, slot = 0, bad = 0;
+    if (ps < 0 || ps >= b.max_position) {
+      bad = 2;
+    } else {
+      const int64_t bi = ps / b.block_size;
+      const int64_t blk = bi < nb && bi < b.bt_stride ? int64_t(bt[bi]) : -1;
+      if (blk < 0 || blk >= b.num_blocks) bad = 4;
+      else slot = int32_t(blk * b.block_size + ps % b.block_size);
+    }
+    if (bad) {
+      flag(b.status, bad);
+      row = -1;
+    }
+    b.src_row[tok] = row;
+    b.pos[tok] = bad ? 0 : int32_t(ps);
+    b.slot[tok] = slot;
+  }
+}
+
 int hip_fail(hipError_t e, const char* what) {
   return prkv::fail(PRKV_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
 }
@@ -269,6 +424,106 @@ hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& v
                   int64_t grid, size_t lds, hipStream_t s) {
   hipLaunchKernelGGL(inject_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), lds, s, p, kc, vc);
   return hipGetLastError();
+}
+
+
+// Workspace of inject_topk_device: header (n_tokens int64 at 0, n_facts
+// int32 at 8), the per-fact plan at 256, then src_row, pos and slot arrays of
+// max_tokens int32 each, every part 256-byte aligned.
+struct Workspace {
+  size_t plan, src_row, pos, slot, total;
+  Workspace(int64_t max_facts, int64_t max_tokens) {
+    auto up = [](size_t v) { return (v + 255u) / 256u * 256u; };
+    plan = 256;
+    src_row = plan + up(size_t(max_facts) * sizeof(FactPlan));
+    pos = src_row + up(size_t(max_tokens) * 4u);
+    slot = pos + up(size_t(max_tokens) * 4u);
+    total = slot + up(size_t(max_tokens) * 4u);
+  }
+};
+
+int check_cache_args(const prkv_store* st, int32_t block_size, int64_t num_blocks,
+                     void* const* k_cache_layers, void* const* v_cache_layers) {
+  if (!st) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (!st->device_backed()) return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store");
+  if (block_size < 1 || num_blocks < 1)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "block_size and num_blocks must be >= 1");
+  const int64_t num_slots = num_blocks * int64_t(block_size);
+  if (num_blocks > INT32_MAX || num_slots > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds 2^31-1");
+  if (!k_cache_layers || !v_cache_layers)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "cache pointer arrays are NULL");
+  for (int l = 0; l < st->desc.num_layers; ++l) {
+    if (!k_cache_layers[l] || !v_cache_layers[l])
+      return prkv::fail(PRKV_ERR_INVALID_ARG, "cache pointer of layer %d is NULL", l);
+    if (!aligned16(k_cache_layers[l]) || !aligned16(v_cache_layers[l]))
+      return prkv::fail(PRKV_ERR_ALIGNMENT, "cache pointer of layer %d not 16-byte aligned", l);
+  }
+  return PRKV_OK;
+}
+
+// Enqueues the inject kernel for up to n_tokens tokens (the exact count is
+// *n_tokens_dev when that is set).  Arguments are already validated.
+int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_tokens_dev,
+                  const int32_t* d_src_row, const int32_t* d_pos, const int32_t* d_slot,
+                  void* const* k_cache_layers, void* const* v_cache_layers, int32_t block_size,
+                  int64_t num_blocks, int32_t* d_status, hipStream_t s) {
+  const prkv_store_desc& d = st->desc;
+  LayerPtrs kc{}, vc{};
+  for (int l = 0; l < d.num_layers; ++l) {
+    kc.p[l] = static_cast<uint16_t*>(k_cache_layers[l]);
+    vc.p[l] = static_cast<uint16_t*>(v_cache_layers[l]);
+  }
+  // Launch shape: tiles of 4 tokens; split each token's chunk range across
+  // workgroups until the grid holds enough waves to cover the chip.
+  const int D = d.head_dim;
+  const int64_t chunks = int64_t(d.num_layers) * d.num_kv_heads * (D / 16);
+  const int iters = int((chunks + kWave - 1) / kWave);
+  const int64_t want_waves = int64_t(compute_units()) * 16;
+  const int64_t tiles = (n_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
+  int n_splits = 1;
+  while (n_splits < iters && tiles * n_splits * kWavesPerGroup < want_waves) n_splits *= 2;
+  if (n_splits > iters) n_splits = iters;
+  int per = (iters + n_splits - 1) / n_splits;
+  per = (per + kUnroll - 1) / kUnroll * kUnroll;
+  n_splits = (iters + per - 1) / per;
+  // at most 2^20 workgroups; each loops over tiles with a grid stride
+  const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
+                                                                    : (int64_t(1) << 20) / n_splits;
+  const int64_t grid = grid_tiles * n_splits;
+  const size_t lds = size_t(kWavesPerGroup) * (size_t(D / 2) * 16 + 12);
+
+  InjectParams p;
+  p.k_arena = static_cast<const uint16_t*>(st->k_arena);
+  p.v_arena = static_cast<const uint16_t*>(st->v_arena);
+  p.rope = static_cast<const f32x4*>(st->rope);
+  p.src_row = d_src_row;
+  p.pos = d_pos;
+  p.slot = d_slot;
+  p.status = d_status;
+  p.n_tokens_dev = n_tokens_dev;
+  p.n_tokens = n_tokens;
+  p.capacity_rows = d.capacity_rows;
+  p.num_slots = num_blocks * int64_t(block_size);
+  p.max_position = d.max_position;
+  p.num_layers = d.num_layers;
+  p.num_heads = d.num_kv_heads;
+  p.n_splits = n_splits;
+  p.iters_per_split = per;
+
+  hipError_t e;
+  switch (D) {
+    case 16: e = launch<16>(p, kc, vc, grid, lds, s); break;
+    case 32: e = launch<32>(p, kc, vc, grid, lds, s); break;
+    case 64: e = launch<64>(p, kc, vc, grid, lds, s); break;
+    case 128: e = launch<128>(p, kc, vc, grid, lds, s); break;
+    case 256: e = launch<256>(p, kc, vc, grid, lds, s); break;
+    case 512: e = launch<512>(p, kc, vc, grid, lds, s); break;
+    case 1024: e = launch<1024>(p, kc, vc, grid, lds, s); break;
+    default: return prkv::fail(PRKV_ERR_INVALID_ARG, "head_dim %d unsupported", D);
+  }
+  if (e != hipSuccess) return hip_fail(e, "inject launch");
+  return PRKV_OK;
 }
 
 }  // namespace
@@ -348,85 +603,128 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
                 void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
                 int32_t* d_status, void* stream) {
   prkv::clear_error();
-  if (!st) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
-  if (!st->device_backed()) return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store");
+  if (int rc = check_cache_args(st, block_size, num_blocks, k_cache_layers, v_cache_layers))
+    return rc;
   if (n_tokens < 0) return prkv::fail(PRKV_ERR_INVALID_ARG, "n_tokens < 0");
-  if (block_size < 1 || num_blocks < 1)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "block_size and num_blocks must be >= 1");
   const int64_t num_slots = num_blocks * int64_t(block_size);
-  if (num_blocks > INT32_MAX || num_slots > INT32_MAX)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "num_blocks * block_size exceeds 2^31-1");
   if (n_tokens > num_slots)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "n_tokens %lld exceeds the cache's %lld slots",
                       (long long)n_tokens, (long long)num_slots);
   if (n_tokens == 0) return PRKV_OK;
-  if (!d_src_row || !d_pos || !d_slot || !k_cache_layers || !v_cache_layers)
+  if (!d_src_row || !d_pos || !d_slot)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "NULL pointer argument");
   if ((reinterpret_cast<uintptr_t>(d_src_row) | reinterpret_cast<uintptr_t>(d_pos) |
        reinterpret_cast<uintptr_t>(d_slot) | reinterpret_cast<uintptr_t>(d_status)) & 3u)
     return prkv::fail(PRKV_ERR_ALIGNMENT, "int32 arrays must be 4-byte aligned");
-  const prkv_store_desc& d = st->desc;
-  LayerPtrs kc{}, vc{};
-  for (int l = 0; l < d.num_layers; ++l) {
-    if (!k_cache_layers[l] || !v_cache_layers[l])
-      return prkv::fail(PRKV_ERR_INVALID_ARG, "cache pointer of layer %d is NULL", l);
-    if (!aligned16(k_cache_layers[l]) || !aligned16(v_cache_layers[l]))
-      return prkv::fail(PRKV_ERR_ALIGNMENT, "cache pointer of layer %d not 16-byte aligned", l);
-    kc.p[l] = static_cast<uint16_t*>(k_cache_layers[l]);
-    vc.p[l] = static_cast<uint16_t*>(v_cache_layers[l]);
+  return launch_inject(st, n_tokens, nullptr, d_src_row, d_pos, d_slot, k_cache_layers,
+                       v_cache_layers, block_size, num_blocks, d_status,
+                       static_cast<hipStream_t>(stream));
+}
+
+int store_upload_fact_table(const prkv_store* st, void* d_table, size_t table_bytes,
+                            void* stream) {
+  prkv::clear_error();
+  if (!st) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (!d_table) return prkv::fail(PRKV_ERR_INVALID_ARG, "d_table is NULL");
+  if (reinterpret_cast<uintptr_t>(d_table) & 7u)
+    return prkv::fail(PRKV_ERR_ALIGNMENT, "d_table must be 8-byte aligned");
+  const size_t need = size_t(st->desc.max_facts) * 8u;
+  if (table_bytes < need)
+    return prkv::fail(PRKV_ERR_BUFFER_TOO_SMALL, "fact table needs %zu bytes, got %zu", need,
+                      table_bytes);
+  std::vector<int32_t> host;
+  try {
+    host.resize(size_t(st->desc.max_facts) * 2u);
+  } catch (const std::bad_alloc&) {
+    return prkv::fail(PRKV_ERR_NO_MEMORY, "fact table staging");
   }
+  for (int32_t f = 0; f < st->desc.max_facts; ++f) {
+    host[2 * size_t(f)] = int32_t(st->first_row[f]);   // -1 when absent
+    host[2 * size_t(f) + 1] = st->length[f];
+  }
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e = hipMemcpyAsync(d_table, host.data(), need, hipMemcpyHostToDevice, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "fact table upload");
+  return PRKV_OK;
+}
 
-  // Launch shape: tiles of 4 tokens; split each token's chunk range across
-  // workgroups until the grid holds enough waves to cover the chip.
-  const int D = d.head_dim;
-  const int64_t chunks = int64_t(d.num_layers) * d.num_kv_heads * (D / 16);
-  const int iters = int((chunks + kWave - 1) / kWave);
-  const int64_t want_waves = int64_t(compute_units()) * 16;
-  const int64_t tiles = (n_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
-  int n_splits = 1;
-  while (n_splits < iters && tiles * n_splits * kWavesPerGroup < want_waves) n_splits *= 2;
-  if (n_splits > iters) n_splits = iters;
-  int per = (iters + n_splits - 1) / n_splits;
-  per = (per + kUnroll - 1) / kUnroll * kUnroll;
-  n_splits = (iters + per - 1) / per;
-  // at most 2^20 workgroups; each loops over tiles with a grid stride
-  const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
-                                                                    : (int64_t(1) << 20) / n_splits;
-  const int64_t grid = grid_tiles * n_splits;
-  const size_t lds = size_t(kWavesPerGroup) * (size_t(D / 2) * 16 + 12);
+int inject_device_workspace_bytes(int32_t max_facts_batch, int64_t max_tokens, size_t* bytes) {
+  prkv::clear_error();
+  if (!bytes) return prkv::fail(PRKV_ERR_INVALID_ARG, "bytes is NULL");
+  if (max_facts_batch < 0 || max_tokens < 0 || max_tokens > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "bad bounds");
+  *bytes = Workspace(max_facts_batch, max_tokens).total;
+  return PRKV_OK;
+}
 
-  InjectParams p;
-  p.k_arena = static_cast<const uint16_t*>(st->k_arena);
-  p.v_arena = static_cast<const uint16_t*>(st->v_arena);
-  p.rope = static_cast<const f32x4*>(st->rope);
-  p.src_row = d_src_row;
-  p.pos = d_pos;
-  p.slot = d_slot;
-  p.status = d_status;
-  p.n_tokens = n_tokens;
-  p.capacity_rows = d.capacity_rows;
-  p.num_slots = num_slots;
-  p.max_position = d.max_position;
-  p.num_layers = d.num_layers;
-  p.num_heads = d.num_kv_heads;
-  p.n_tiles = tiles;
-  p.n_splits = n_splits;
-  p.iters_per_split = per;
+int inject_topk_device(const prkv_store* st, const void* d_fact_table,
+                       const prkv_device_batch* batch, void* const* k_cache_layers,
+                       void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
+                       void* d_workspace, size_t workspace_bytes, int32_t* d_status,
+                       void* stream) {
+  prkv::clear_error();
+  if (int rc = check_cache_args(st, block_size, num_blocks, k_cache_layers, v_cache_layers))
+    return rc;
+  if (!batch) return prkv::fail(PRKV_ERR_INVALID_ARG, "batch is NULL");
+  const prkv_device_batch& b = *batch;
+  if (b.n_req < 0 || b.max_facts < 0 || b.max_tokens < 0 || b.bt_stride < 0)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "negative batch size");
+  const int64_t num_slots = num_blocks * int64_t(block_size);
+  if (b.max_tokens > num_slots)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "max_tokens %lld exceeds the cache's %lld slots",
+                      (long long)b.max_tokens, (long long)num_slots);
+  if (b.n_req == 0 || b.max_facts == 0 || b.max_tokens == 0) return PRKV_OK;
+  if (!d_fact_table || !b.req_fact_ptr || !b.fact_ids || !b.start_pos || !b.bt_len ||
+      (!b.block_tables && b.bt_stride > 0) || !d_workspace)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((reinterpret_cast<uintptr_t>(d_fact_table) & 7u) ||
+      (reinterpret_cast<uintptr_t>(d_workspace) & 255u) ||
+      ((reinterpret_cast<uintptr_t>(b.req_fact_ptr) | reinterpret_cast<uintptr_t>(b.fact_ids) |
+        reinterpret_cast<uintptr_t>(b.start_pos) | reinterpret_cast<uintptr_t>(b.bt_len) |
+        reinterpret_cast<uintptr_t>(b.block_tables) | reinterpret_cast<uintptr_t>(d_status)) &
+       3u))
+    return prkv::fail(PRKV_ERR_ALIGNMENT,
+                      "fact table 8-byte, workspace 256-byte, int32 arrays 4-byte aligned");
+  const Workspace ws(b.max_facts, b.max_tokens);
+  if (workspace_bytes < ws.total)
+    return prkv::fail(PRKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", ws.total,
+                      workspace_bytes);
+
+  char* base = static_cast<char*>(d_workspace);
+  DeviceBatch db;
+  db.req_fact_ptr = b.req_fact_ptr;
+  db.fact_ids = b.fact_ids;
+  db.start_pos = b.start_pos;
+  db.block_tables = b.block_tables;
+  db.bt_len = b.bt_len;
+  db.fact_table = static_cast<const int2*>(d_fact_table);
+  db.plan = reinterpret_cast<FactPlan*>(base + ws.plan);
+  db.n_tokens_out = reinterpret_cast<int64_t*>(base);
+  db.n_facts_out = reinterpret_cast<int32_t*>(base + 8);
+  db.src_row = reinterpret_cast<int32_t*>(base + ws.src_row);
+  db.pos = reinterpret_cast<int32_t*>(base + ws.pos);
+  db.slot = reinterpret_cast<int32_t*>(base + ws.slot);
+  db.status = d_status;
+  db.max_tokens = b.max_tokens;
+  db.num_blocks = num_blocks;
+  db.n_req = b.n_req;
+  db.bt_stride = b.bt_stride;
+  db.max_facts_batch = b.max_facts;
+  db.store_max_facts = st->desc.max_facts;
+  db.block_size = block_size;
+  db.max_position = st->desc.max_position;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
-  hipError_t e;
-  switch (D) {
-    case 16: e = launch<16>(p, kc, vc, grid, lds, s); break;
-    case 32: e = launch<32>(p, kc, vc, grid, lds, s); break;
-    case 64: e = launch<64>(p, kc, vc, grid, lds, s); break;
-    case 128: e = launch<128>(p, kc, vc, grid, lds, s); break;
-    case 256: e = launch<256>(p, kc, vc, grid, lds, s); break;
-    case 512: e = launch<512>(p, kc, vc, grid, lds, s); break;
-    case 1024: e = launch<1024>(p, kc, vc, grid, lds, s); break;
-    default: return prkv::fail(PRKV_ERR_INVALID_ARG, "head_dim %d unsupported", D);
-  }
-  if (e != hipSuccess) return hip_fail(e, "inject launch");
-  return PRKV_OK;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "plan launch");
+  const int64_t mgrid = (int64_t(b.max_facts) + kWavesPerGroup - 1) / kWavesPerGroup;
+  hipLaunchKernelGGL(materialize_kernel, dim3(unsigned(mgrid)), dim3(kThreads), 0, s, db);
+  e = hipGetLastError();
+  if (e != hipSuccess) return hip_fail(e, "materialize launch");
+  return launch_inject(st, b.max_tokens, db.n_tokens_out, db.src_row, db.pos, db.slot,
+                       k_cache_layers, v_cache_layers, block_size, num_blocks, d_status, s);
 }
 
 }  // extern "C"

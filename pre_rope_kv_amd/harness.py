@@ -37,7 +37,8 @@ def fit_num_blocks(spec, reserve_bytes, device="cuda", margin=6 * GiB):
 class DeviceWorkload:
     """A workload resident on one GPU: store, cache, mapping."""
 
-    def __init__(self, w: workloads.Workload, device="cuda", gen_device=None, stream=None):
+    def __init__(self, w: workloads.Workload, device="cuda", gen_device=None, stream=None,
+                 host_mapping=True):
         self.w = w
         sp = w.spec
         self.device = torch.device(device)
@@ -59,7 +60,9 @@ class DeviceWorkload:
         self.v_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
         self.reset_cache()
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
-        self.build_mapping()
+        self.n_tokens = w.n_tokens
+        if host_mapping:
+            self.build_mapping()
 
     # -- store -------------------------------------------------------------
     def _put_all(self, batch=64):
@@ -114,6 +117,54 @@ class DeviceWorkload:
         with torch.cuda.stream(self.stream):
             for d, h in zip(self.d_map, self.h_map):
                 d.copy_(h, non_blocking=True)
+
+    # -- device-resident batch (device-side slot mapping) --------------------
+    def setup_device_batch(self, max_tokens=None, max_facts=None):
+        """Upload the batch description, the fact table and a workspace."""
+        w = self.w
+        req_ptr, ids, start, bt, bt_len = w.csr()
+        dev = self.device
+        self.d_req_ptr = torch.from_numpy(req_ptr).to(dev)
+        self.d_ids = torch.from_numpy(ids).to(dev)
+        self.d_start = torch.from_numpy(start).to(dev)
+        self.d_bt = torch.from_numpy(np.ascontiguousarray(bt)).to(dev)
+        self.d_bt_len = torch.from_numpy(bt_len).to(dev)
+        self.fact_table = torch.empty(2 * w.max_facts, dtype=torch.int32, device=dev)
+        prkv.store_upload_fact_table(self.store, self.fact_table, stream=self.stream)
+        self.max_facts = int(max_facts if max_facts is not None else len(ids))
+        longest = max(w.length_of(f) for f in w.put_order)
+        self.max_tokens = int(max_tokens if max_tokens is not None else len(ids) * longest)
+        self.ws_bytes = prkv.inject_device_workspace_bytes(self.max_facts, self.max_tokens)
+        self.workspace = torch.zeros(self.ws_bytes, dtype=torch.uint8, device=dev)
+        self.ws_layout = prkv.workspace_layout(self.max_facts, self.max_tokens)
+        self.batch = prkv.device_batch(len(req_ptr) - 1, bt.shape[1], self.max_facts,
+                                       self.max_tokens, self.d_req_ptr, self.d_ids, self.d_start,
+                                       self.d_bt, self.d_bt_len)
+        self.stream.synchronize()
+
+    def inject_device(self):
+        prkv.inject_topk_device(self.store, self.fact_table, self.batch, self.k_layers(),
+                                self.v_layers(), self.w.spec.block_size, self.w.num_blocks,
+                                self.workspace, self.ws_bytes, d_status=self.status,
+                                stream=self.stream)
+
+    def inject_device_args(self):
+        """Pre-marshalled arguments of inject_topk_device for timing loops."""
+        import ctypes
+        L = self.w.spec.num_layers
+        kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.k_layers()])
+        vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in self.v_layers()])
+        return (self.store.handle, self.fact_table.data_ptr(), ctypes.byref(self.batch), kp, vp,
+                self.w.spec.block_size, self.w.num_blocks, self.workspace.data_ptr(),
+                self.ws_bytes, self.status.data_ptr(), self.stream.cuda_stream)
+
+    def device_mapping(self):
+        """(n_tokens, src_row, pos, slot) the device path wrote into its workspace."""
+        ws = self.workspace.cpu().numpy()
+        lay = self.ws_layout
+        n = int(ws[lay["n_tokens"]:lay["n_tokens"] + 8].view(np.int64)[0])
+        arr = {k: ws[lay[k]:lay[k] + 4 * n].view(np.int32) for k in ("src_row", "pos", "slot")}
+        return n, arr["src_row"], arr["pos"], arr["slot"]
 
     # -- inject ------------------------------------------------------------
     def inject(self):

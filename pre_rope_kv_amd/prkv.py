@@ -28,7 +28,8 @@ CODES = {v: k for k, v in ERRORS.items()}
 # Names the header declares; the library must export every one of them.
 EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
            "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
-           "last_error_string"]
+           "last_error_string", "store_upload_fact_table", "inject_device_workspace_bytes",
+           "inject_topk_device"]
 
 
 class PrkvError(RuntimeError):
@@ -48,6 +49,22 @@ class StoreDesc(ctypes.Structure):
         ("max_position", ctypes.c_int32),
         ("rope_style", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+    ]
+
+
+class DeviceBatch(ctypes.Structure):
+    """prkv_device_batch: device pointers describing a batch of requests."""
+    _fields_ = [
+        ("n_req", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int32),
+        ("max_facts", ctypes.c_int32),
+        ("pad_", ctypes.c_int32),
+        ("max_tokens", ctypes.c_int64),
+        ("req_fact_ptr", ctypes.c_void_p),
+        ("fact_ids", ctypes.c_void_p),
+        ("start_pos", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("bt_len", ctypes.c_void_p),
     ]
 
 
@@ -84,6 +101,13 @@ def lib():
                                        ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                        ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
         "rope_table_fill": (ctypes.c_int, [ctypes.POINTER(StoreDesc), _vp, ctypes.c_size_t]),
+        "store_upload_fact_table": (ctypes.c_int, [_vp, _vp, ctypes.c_size_t, _vp]),
+        "inject_device_workspace_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int64,
+                                                         ctypes.POINTER(ctypes.c_size_t)]),
+        "inject_topk_device": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(DeviceBatch),
+                                              ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                              ctypes.c_int32, ctypes.c_int64, _vp,
+                                              ctypes.c_size_t, _vp, _vp]),
         "last_error_string": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -234,3 +258,51 @@ def rope_table_fill(d):
     out = np.empty(nbytes // 4, np.float32)
     _check(lib().rope_table_fill(ctypes.byref(d), out.ctypes.data, nbytes), "rope_table_fill")
     return out.reshape(d.max_position, d.head_dim // 2, 4)
+
+
+def store_upload_fact_table(st, d_table, stream=None):
+    """d_table: device int32 tensor with >= 2 * max_facts entries."""
+    nbytes = d_table.numel() * d_table.element_size() if hasattr(d_table, "numel") else None
+    if nbytes is None:
+        raise TypeError("d_table must be a device tensor")
+    _check(lib().store_upload_fact_table(st.handle, _ptr(d_table), nbytes, _stream(stream)),
+           "store_upload_fact_table")
+
+
+def inject_device_workspace_bytes(max_facts, max_tokens):
+    n = ctypes.c_size_t()
+    _check(lib().inject_device_workspace_bytes(int(max_facts), int(max_tokens), ctypes.byref(n)),
+           "inject_device_workspace_bytes")
+    return n.value
+
+
+def workspace_layout(max_facts, max_tokens):
+    """Byte offsets of the workspace parts, as include/prkv.h documents them."""
+    def up(v):
+        return (v + 255) // 256 * 256
+    plan = 256
+    src_row = plan + up(max_facts * 16)
+    pos = src_row + up(max_tokens * 4)
+    slot = pos + up(max_tokens * 4)
+    return {"n_tokens": 0, "n_facts": 8, "plan": plan, "src_row": src_row, "pos": pos,
+            "slot": slot, "total": slot + up(max_tokens * 4)}
+
+
+def device_batch(n_req, bt_stride, max_facts, max_tokens, req_fact_ptr, fact_ids, start_pos,
+                 block_tables, bt_len):
+    return DeviceBatch(int(n_req), int(bt_stride), int(max_facts), 0, int(max_tokens),
+                       _ptr(req_fact_ptr), _ptr(fact_ids), _ptr(start_pos),
+                       _ptr(block_tables), _ptr(bt_len))
+
+
+def inject_topk_device(st, d_fact_table, batch, k_cache_layers, v_cache_layers, block_size,
+                       num_blocks, d_workspace, workspace_bytes, d_status=None, stream=None):
+    L = len(k_cache_layers)
+    if len(v_cache_layers) != L or L != st.desc.num_layers:
+        raise ValueError("need one K and one V cache pointer per layer")
+    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
+    vp = (_vp * L)(*[_ptr(t) for t in v_cache_layers])
+    _check(lib().inject_topk_device(st.handle, _ptr(d_fact_table), ctypes.byref(batch), kp, vp,
+                                    int(block_size), int(num_blocks), _ptr(d_workspace),
+                                    int(workspace_bytes), _ptr(d_status), _stream(stream)),
+           "inject_topk_device")

@@ -88,14 +88,33 @@ def compare(img_k, img_v, gk, gv, mask):
     return rep
 
 
-def run_full(w, gen_device="cuda", prior_gpu=None, prior_img=None):
+def inject_via(dw, path):
+    """Run the inject on the given path: host slot mapping + inject_topk, or
+    the device-resident batch through inject_topk_device; for the latter also
+    check the device-built mapping against the oracle's, bit for bit."""
+    if path == "host":
+        dw.inject()
+        torch.cuda.synchronize()
+        return
+    dw.setup_device_batch()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    n, src, pos, slot = dw.device_mapping()
+    o_src, o_pos, o_slot = paged.token_mapping(dw.w.requests(), dw.w.fact_rows,
+                                               dw.w.spec.block_size)
+    assert n == len(o_src)
+    assert np.array_equal(src, np.array(o_src, np.int32))
+    assert np.array_equal(pos, np.array(o_pos, np.int32))
+    assert np.array_equal(slot, np.array(o_slot, np.int32))
+
+
+def run_full(w, gen_device="cuda", prior_gpu=None, prior_img=None, path="host"):
     _say(f"workload {w.spec.name}: L={w.spec.num_layers} H={w.spec.num_kv_heads} "
-         f"D={w.spec.head_dim} bs={w.spec.block_size} tokens={w.n_tokens}")
+         f"D={w.spec.head_dim} bs={w.spec.block_size} tokens={w.n_tokens} path={path}")
     dw = harness.DeviceWorkload(w, gen_device=gen_device)
     if prior_gpu is not None:
         prior_gpu(dw)
-    dw.inject()
-    torch.cuda.synchronize()
+    inject_via(dw, path)
     assert int(dw.status.item()) == 0
     blocks = w.listed_blocks()
     gk, gv = dw.listed_blocks_host(blocks)
@@ -151,7 +170,8 @@ def custom_workload(name, L, H, D, bs, facts, requests, theta=1e4, num_blocks=51
 # the five workloads
 # ---------------------------------------------------------------------------
 
-def test_tiny_with_attention_equivalence():
+@pytest.mark.parametrize("path", ["host", "device"])
+def test_tiny_with_attention_equivalence(path):
     """Tiny workload, full compare, then Theorem 3 on the device's cache:
     attention over the injected paged cache equals attention over the same
     prompt encoded in place (within the bound implied by <= 2 ulp K)."""
@@ -188,7 +208,7 @@ def test_tiny_with_attention_equivalence():
             flat_v[0, s] = torch.from_numpy(v.view(np.int16)).to(flat_v.device)
 
     dw, rep, (img_k, img_v, gk, gv) = run_full(w, gen_device="cpu", prior_gpu=prior_gpu,
-                                               prior_img=prior_img)
+                                               prior_img=prior_img, path=path)
     # nothing outside the listed blocks was written
     expect = 2 * sp.num_layers * (n_fact + P + Q) * sp.num_kv_heads * sp.head_dim
     assert dw.count_non_sentinel() == expect
@@ -247,16 +267,17 @@ def test_tiny_with_attention_equivalence():
     assert d_gpu < 0.1
 
 
+@pytest.mark.parametrize("path", ["host", "device"])
 @pytest.mark.parametrize("name", ["llama3_8b_k5", "llama3_8b_k50"])
-def test_llama8b_single_request_full(name):
+def test_llama8b_single_request_full(name, path):
     w = workloads.make(name)
-    dw, rep, _ = run_full(w)
+    dw, rep, _ = run_full(w, path=path)
     sp = w.spec
     expect = 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
     assert dw.count_non_sentinel() == expect
 
 
-def _full_size(name, n_sample_tokens, seed):
+def _full_size(name, n_sample_tokens, seed, path="host"):
     spec = workloads.SPECS[name]
     # reserve: arenas + table + slack; the cache takes the rest (up to the spec)
     w0 = workloads.make(name)
@@ -265,8 +286,7 @@ def _full_size(name, n_sample_tokens, seed):
     w = w0 if nb == spec.num_blocks else workloads.make(name, num_blocks=nb)
     _say(f"{name}: num_blocks {nb} (spec {spec.num_blocks}), tokens {w.n_tokens}")
     dw = harness.DeviceWorkload(w)
-    dw.inject()
-    torch.cuda.synchronize()
+    inject_via(dw, path)
     assert int(dw.status.item()) == 0
     src, pos, slot = (np.asarray(a) for a in
                       paged.token_mapping(w.requests(), w.fact_rows, spec.block_size))
@@ -304,12 +324,14 @@ def _full_size(name, n_sample_tokens, seed):
     assert dw.count_non_sentinel() == expect, "writes outside the injected slots"
 
 
-def test_llama8b_batch64_full_size_sampled():
-    _full_size("llama3_8b_batch64_k50", 512, seed=3)
+@pytest.mark.parametrize("path", ["host", "device"])
+def test_llama8b_batch64_full_size_sampled(path):
+    _full_size("llama3_8b_batch64_k50", 512, seed=3, path=path)
 
 
-def test_llama70b_batch16_full_size_sampled():
-    _full_size("llama3_70b_batch16_k50", 256, seed=4)
+@pytest.mark.parametrize("path", ["host", "device"])
+def test_llama70b_batch16_full_size_sampled(path):
+    _full_size("llama3_70b_batch16_k50", 256, seed=4, path=path)
 
 
 # ---------------------------------------------------------------------------
@@ -334,12 +356,13 @@ EDGE = [
 ]
 
 
+@pytest.mark.parametrize("path", ["host", "device"])
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
-def test_edge_case(case):
+def test_edge_case(case, path):
     name, L, H, D, bs, facts, reqs = case
     nb = 2048 if name == "far_positions" else 512
     w = custom_workload(name, L, H, D, bs, facts, reqs, theta=5e5, num_blocks=nb)
-    dw, rep, (img_k, img_v, gk, gv) = run_full(w, gen_device="cuda")
+    dw, rep, (img_k, img_v, gk, gv) = run_full(w, gen_device="cuda", path=path)
     if name == "prefix0_len1":
         # position 0 is the identity: K at slot of pos 0 equals the pre-RoPE K bit for bit
         k0, _ = w.fact_kv(0, device="cuda")

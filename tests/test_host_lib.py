@@ -249,3 +249,35 @@ def test_same_fact_twice_is_legal():
     assert src.tolist() == [0, 1, 0, 1]
     assert pos.tolist() == [0, 1, 2, 3]
     assert slot.tolist() == [4, 5, 6, 7]
+
+
+@pytest.mark.parametrize("facts,tokens", [(1, 1), (50, 2000), (3200, 192000), (0, 0), (7, 13)])
+def test_device_workspace_size_matches_layout(facts, tokens):
+    assert prkv.inject_device_workspace_bytes(facts, tokens) == \
+        prkv.workspace_layout(facts, tokens)["total"]
+
+
+def test_device_workspace_size_rejects_bad_bounds():
+    for facts, tokens in ((-1, 5), (5, -1), (5, 2**31)):
+        with pytest.raises(prkv.PrkvError) as ei:
+            prkv.inject_device_workspace_bytes(facts, tokens)
+        assert ei.value.name == "INVALID_ARG"
+
+
+def test_upload_fact_table_argument_errors():
+    st = prkv.store_create(_desc(max_facts=16))
+    L = prkv.lib()
+    for ptr, nbytes, name in ((None, 256, "INVALID_ARG"), (4100, 256, "ALIGNMENT"),
+                              (4096, 8 * 16 - 8, "BUFFER_TOO_SMALL")):
+        with pytest.raises(prkv.PrkvError) as ei:
+            prkv._check(L.store_upload_fact_table(st.handle, ptr, nbytes, None), "upload")
+        assert ei.value.name == name
+
+
+def test_inject_device_rejects_metadata_store_and_bad_batches():
+    st = prkv.store_create(_desc())
+    b = prkv.device_batch(1, 4, 2, 10, 4096, 4096, 4096, 4096, 4096)
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.inject_topk_device(st, 4096, b, [4096, 4096], [4096, 4096], 16, 4, 4096, 1 << 20,
+                                stream=0)
+    assert ei.value.name == "NO_DEVICE"
