@@ -25,6 +25,7 @@ sys.path.insert(0, ROOT)
 
 METRIC = "injected KV tokens/s (all layers) + achieved HBM GB/s and % of peak, 1 MI355X"
 PEAK_HBM_GBPS = 8000.0
+PEAK_PCIE_GBPS = 64.0  # PCIe 5.0 x16, one direction
 DEFAULT_WORKLOAD = "llama3_8b_batch64_k50"
 
 
@@ -38,6 +39,9 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--store", choices=("device", "host"), default="device",
+                    help="where the fact store's arenas live: HBM, or pinned host DRAM read "
+                         "by the kernel over PCIe (zero-copy)")
     ap.add_argument("--flush", action="store_true",
                     help="evict the 256 MB Infinity Cache with a 1 GiB fill before every timed "
                          "launch and time launches one by one (for workloads far below 1 GiB)")
@@ -281,11 +285,12 @@ def main():
 
     spec = workloads.SPECS[args.workload]
     w0 = workloads.make(args.workload)
-    reserve = 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes + (1 << 30)
+    reserve = (2 * w0.capacity_rows * spec.num_layers * spec.row_bytes
+               if args.store == "device" else 0) + (1 << 30)
     nb = harness.fit_num_blocks(spec, reserve)
     w = w0 if nb == spec.num_blocks else workloads.make(args.workload, num_blocks=nb)
     t_setup = time.perf_counter()
-    dw = harness.DeviceWorkload(w)
+    dw = harness.DeviceWorkload(w, store_location=args.store)
     dw.setup_device_batch()
     setup_s = time.perf_counter() - t_setup
     stream = dw.stream
@@ -349,7 +354,7 @@ def main():
     n_tok = dw.n_tokens
     alg_bytes = n_tok * spec.bytes_per_token
     achieved = alg_bytes / (kernel_ms * 1e-3) / 1e9
-    traffic = read_profile_traffic(spec.name) if w is w0 else None
+    traffic = read_profile_traffic(spec.name) if (w is w0 and args.store == "device") else None
 
     e2e = None
     if not args.no_e2e:
@@ -381,7 +386,9 @@ def main():
         "dtype": "f32",
         "data": "synthetic",
         "config": {
-            "workload": spec.name, "storage": "bf16", "layers": spec.num_layers,
+            "workload": spec.name, "storage": "bf16",
+            "store": "HBM" if args.store == "device" else "host DRAM, pinned, read over PCIe",
+            "layers": spec.num_layers,
             "kv_heads": spec.num_kv_heads, "head_dim": spec.head_dim,
             "requests": spec.n_requests, "k": spec.k, "tokens": n_tok,
             "block_size": spec.block_size, "num_blocks": w.num_blocks,
@@ -396,12 +403,19 @@ def main():
         "step_ms": {"mean": step_ms, "median": step_per_ms[len(step_per_ms) // 2]},
         "kernel_ms": {"mean": kernel_ms, "p10": per_ms[len(per_ms) // 10],
                       "median": per_ms[len(per_ms) // 2], "p90": per_ms[(9 * len(per_ms)) // 10]},
-        "roofline": {
+        "roofline": ({
             "bound": "hbm", "achieved": achieved, "peak": PEAK_HBM_GBPS, "unit": "GB/s",
             "frac": achieved / PEAK_HBM_GBPS, "traffic": traffic,
-            "kernel": "inject_kernel<128>",
+            "kernel": f"inject_kernel<{spec.head_dim}>",
             "bytes_per_launch": alg_bytes,
-        },
+        } if args.store == "device" else {
+            # reads of the retrieved rows cross PCIe (host -> device); writes stay in HBM
+            "bound": "pcie", "achieved": (alg_bytes / 2) / (kernel_ms * 1e-3) / 1e9,
+            "peak": PEAK_PCIE_GBPS, "unit": "GB/s",
+            "frac": (alg_bytes / 2) / (kernel_ms * 1e-3) / 1e9 / PEAK_PCIE_GBPS,
+            "traffic": None, "kernel": f"inject_kernel<{spec.head_dim}>",
+            "bytes_per_launch": alg_bytes // 2,
+        }),
         "cpu_baseline": cpu,
         "e2e": e2e,
         "setup_s": setup_s,

@@ -84,7 +84,11 @@ int store_required_bytes(const prkv_store_desc* desc, size_t* arena_bytes_each,
  * Source: InferScale review, "Referee Report" Summary ("stored pre-RoPE
  * alongside semantic embeddings", GPU-resident) and Figure 2 (one fact_id
  * names the fact's embedding and its pre-RoPE K/V).
- * k_arena, v_arena: device, arena_bytes_each each.  rope_table: device,
+ * k_arena, v_arena: arena_bytes_each each, in device memory, or in pinned
+ * host memory mapped for the device (hipHostMalloc) to keep the store in host
+ * DRAM ("If this is right" bullet 4: offloading the store to host DRAM costs
+ * milliseconds); the inject kernel then reads only the retrieved rows, over
+ * PCIe, directly from host memory.  rope_table: device,
  * rope_table_bytes; filled here (float64 angles split into float32 hi + lo)
  * with a copy on `stream` that this call waits for.  Passing all three
  * pointers as NULL creates a metadata-only store: facts can be reserved and

@@ -38,7 +38,7 @@ class DeviceWorkload:
     """A workload resident on one GPU: store, cache, mapping."""
 
     def __init__(self, w: workloads.Workload, device="cuda", gen_device=None, stream=None,
-                 host_mapping=True):
+                 host_mapping=True, store_location="device"):
         self.w = w
         sp = w.spec
         self.device = torch.device(device)
@@ -48,8 +48,17 @@ class DeviceWorkload:
                               w.capacity_rows, sp.max_position, sp.rope_theta)
         arena_bytes, rope_bytes = prkv.store_required_bytes(self.desc)
         shape = (sp.num_layers, w.capacity_rows, sp.num_kv_heads, sp.head_dim)
-        self.k_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
-        self.v_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
+        self.store_location = store_location
+        if store_location == "device":
+            self.k_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
+            self.v_arena = torch.empty(shape, dtype=torch.int16, device=self.device)
+        elif store_location == "host":
+            # pinned host memory mapped for the device: the inject kernel reads
+            # the retrieved rows over PCIe directly (zero-copy)
+            self.k_arena = torch.empty(shape, dtype=torch.int16, pin_memory=True)
+            self.v_arena = torch.empty(shape, dtype=torch.int16, pin_memory=True)
+        else:
+            raise ValueError(store_location)
         self.rope = torch.empty(rope_bytes // 4, dtype=torch.float32, device=self.device)
         assert self.k_arena.numel() * 2 == arena_bytes
         self.store = prkv.store_create(self.desc, self.k_arena, self.v_arena, self.rope,

@@ -420,3 +420,23 @@ def test_permuted_fact_order_moves_positions():
         w = custom_workload("perm" + "".join(map(str, order)), 2, 8, 128, 16, facts,
                             [(order, 21)])
         dw, rep, _ = run_full(w)
+
+
+@pytest.mark.parametrize("path", ["host", "device"])
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k5"])
+def test_host_dram_store(name, path):
+    """Arenas in pinned host memory: the kernel reads the retrieved rows over
+    PCIe; the result must be the same as from an HBM-resident store."""
+    w = workloads.make(name)
+    gen = "cpu" if name.startswith("tiny") else "cuda"
+    _say(f"host-DRAM store: {name} path={path}")
+    dw = harness.DeviceWorkload(w, gen_device=gen, store_location="host")
+    assert not dw.k_arena.is_cuda and dw.k_arena.is_pinned()
+    inject_via(dw, path)
+    assert int(dw.status.item()) == 0
+    blocks = w.listed_blocks()
+    gk, gv = dw.listed_blocks_host(blocks)
+    img_k, img_v, n = oracle_images(w, gen)
+    compare(img_k, img_v, gk, gv, written_mask(w, blocks))
+    sp = w.spec
+    assert dw.count_non_sentinel() == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
