@@ -39,6 +39,8 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--no-retrieve", action="store_true",
+                    help="skip timing retrieve_topk and retrieve + inject")
     ap.add_argument("--store", choices=("device", "host"), default="device",
                     help="where the fact store's arenas live: HBM, or pinned host DRAM read "
                          "by the kernel over PCIe (zero-copy)")
@@ -368,6 +370,42 @@ def main():
         e2e = {"ms_per_step": e2e_ms, "tokens_per_s": n_tok / (e2e_ms * 1e-3),
                "what": "host build_slot_mapping + pinned H2D of the mapping + inject_topk"}
 
+    retrieval = None
+    if not args.no_retrieve:
+        # retrieval embeddings per store, queries built around the drawn facts
+        embs = [w.store_embeddings(si, "cuda") for si in range(spec.n_requests)]
+        emb = torch.cat(embs, 0).contiguous()
+        q = w.query_embeddings("cuda", emb=embs)
+        del embs
+        ws_b = prkv.retrieve_workspace_bytes(spec.n_requests, spec.facts_per_store)
+        rws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+        d_rs = torch.as_tensor(w.req_store(), device="cuda")
+        rargs = (emb.data_ptr(), spec.n_requests, spec.facts_per_store, spec.emb_dim,
+                 q.data_ptr(), d_rs.data_ptr(), spec.n_requests, spec.k, dw.d_ids.data_ptr(),
+                 None, rws.data_ptr(), ws_b, dw.status.data_ptr(), stream.cuda_stream)
+
+        def step_retrieve():
+            call(lib.retrieve_topk, rargs, "retrieve_topk")
+
+        def step_both():
+            step_retrieve()
+            step_device()
+
+        _, _, r_ms = timed(step_retrieve)
+        _, _, b_ms = timed(step_both)
+        assert int(dw.status.item()) == 0, "retrieve + inject reported skipped tokens"
+        emb_bytes = spec.n_requests * spec.facts_per_store * spec.emb_dim * 2
+        retrieval = {
+            "what": "retrieve_topk: exact inner-product top-k over each request's store "
+                    f"({spec.facts_per_store} facts x {spec.emb_dim} bf16), then "
+                    "inject_topk_device on the retrieved ids",
+            "retrieve_ms": r_ms,
+            "retrieve_embedding_gbps": emb_bytes / (r_ms * 1e-3) / 1e9,
+            "retrieve_and_inject_ms": b_ms,
+            "retrieve_and_inject_tokens_per_s": n_tok / (b_ms * 1e-3),
+        }
+        del emb, q, rws
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -417,6 +455,7 @@ def main():
             "bytes_per_launch": alg_bytes // 2,
         }),
         "cpu_baseline": cpu,
+        "retrieval": retrieval,
         "e2e": e2e,
         "setup_s": setup_s,
         "timing": "per-launch events after a 1 GiB MALL flush" if args.flush

@@ -230,6 +230,29 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
                        void* d_workspace, size_t workspace_bytes, int32_t* d_status,
                        void* stream);
 
+/* Exact top-k retrieval by inner product, the step before injection.
+ * Source: InferScale review, "Referee Report" Summary (facts retrieved at
+ * serving time through a GPU index, then resolved to their KV) and Figure 2
+ * caption (each fact has a retrieval embedding in the GPU vector store under
+ * its fact_id); "Circularity Check": the index backend changes latency, not
+ * the facts found -- exact search stands in for the approximate index.
+ * d_fact_emb: device bf16 [n_stores][facts_per_store][dim]; d_query_emb:
+ * device bf16 [n_req][dim]; d_req_store: device int32 [n_req], the store each
+ * request searches.  dim: multiple of 512 in [512, 4096]; 1 <= k <= 64 and
+ * k <= facts_per_store.  Scores are inner products of the bf16 values
+ * accumulated in float64 (products are exact).  Output d_fact_ids: device
+ * int32 [n_req][k], global ids store * facts_per_store + fact, best first
+ * (higher score, then smaller id); d_scores: optional device double
+ * [n_req][k].  A request with an out-of-range store gets ids -1 and sets
+ * bit 64 in d_status.  d_workspace: device, retrieve_workspace_bytes,
+ * 8-byte aligned.  Two kernels on `stream`, asynchronous.  The ids can be
+ * passed straight to inject_topk_device (req_fact_ptr[r] = r * k). */
+int retrieve_workspace_bytes(int32_t n_req, int32_t facts_per_store, size_t* bytes);
+int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_store,
+                  int32_t dim, const void* d_query_emb, const int32_t* d_req_store,
+                  int32_t n_req, int32_t k, int32_t* d_fact_ids, double* d_scores,
+                  void* d_workspace, size_t workspace_bytes, int32_t* d_status, void* stream);
+
 /* Fill a HOST buffer with the RoPE table store_create would upload:
  * [max_position][D/2][4] float32 = (cos_hi, cos_lo, sin_hi, sin_lo) with
  * cos_hi = fl32(cos a), cos_lo = fl32(cos a - cos_hi), a = pos * theta_j in

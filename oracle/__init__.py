@@ -18,6 +18,8 @@ LLM Serving", Pith review of arXiv 2607.27090):
   Theorem 6 / section 5.1): rotation by position is a relocation.
 * "Core claim" / Theorem 3: injecting KV at the intended positions equals
   prompt-injecting the same tokens (checked with brute-force attention).
+* "Referee Report", Summary and Figure 2: facts are retrieved by their
+  embeddings before injection (exact top-k by inner product, `retrieve`).
 
 Precision: every floating-point step is float64; the single rounding to
 bfloat16 is round-to-nearest-even.  The pages fix neither the rotation
@@ -29,4 +31,4 @@ Pinning: each function is pinned by tests that do not reuse its code
 invariants).  No function here is "parity unpinned".
 """
 
-from . import attention, bf16, inject, paged, rope  # noqa: F401
+from . import attention, bf16, inject, paged, retrieve, rope  # noqa: F401

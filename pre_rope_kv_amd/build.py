@@ -20,6 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libprkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
+DEVICE_SOURCES = ["prkv_inject.hip", "prkv_retrieve.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",
@@ -42,23 +43,26 @@ def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     host_o = os.path.join(BUILD, "prkv_host.o")
-    dev_o = os.path.join(BUILD, "prkv_inject.o")
     _run(["g++", "-std=c++17", "-O2", "-fPIC", "-Wall", "-Wextra", "-I", INCLUDE,
           "-c", os.path.join(CSRC, "prkv_host.cpp"), "-o", host_o], verbose)
-    _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, "prkv_inject.hip"),
-          "-o", dev_o], verbose)
+    objs = [host_o]
+    for src in DEVICE_SOURCES:
+        obj = os.path.join(BUILD, src.replace(".hip", ".o"))
+        _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "-c", os.path.join(CSRC, src), "-o", obj],
+             verbose)
+        objs.append(obj)
     tmp = LIB + ".tmp"
-    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, host_o, dev_o,
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
           f"-Wl,-rpath,{ROCM}/lib"], verbose)
     os.replace(tmp, LIB)
     return LIB
 
 
-def device_asm(out_path):
-    """Write the gfx950 assembly of the device half (for inspection only)."""
+def device_asm(out_path, source="prkv_inject.hip"):
+    """Write the gfx950 assembly of one device source (for inspection only)."""
     hipcc = os.path.join(ROCM, "bin", "hipcc")
     _run([hipcc, *HIP_FLAGS, "-I", INCLUDE, "--cuda-device-only", "-S",
-          os.path.join(CSRC, "prkv_inject.hip"), "-o", out_path], False)
+          os.path.join(CSRC, source), "-o", out_path], False)
 
 
 if __name__ == "__main__":

@@ -1,0 +1,305 @@
+// Exact top-k retrieval on gfx950: inner products of a request's query
+// embedding with every fact embedding of the request's store, then the k best
+// facts in rank order.  Output is the fact-id list the inject path consumes.
+//
+// Source (page "InferScale: GPU-Native KV Injection for Personalized LLM
+// Serving", Pith review of arXiv 2607.27090): "Referee Report", Summary --
+// facts are retrieved at serving time through a GPU index and their ids then
+// resolve to pre-RoPE KV; Figure 2 caption -- each fact has a retrieval
+// embedding in the GPU vector store under the same fact_id; "Circularity
+// Check" -- the index backend changes latency, not which facts are found.
+// Exact search stands in for the approximate index.
+//
+// score_kernel: one wave per group of facts of one request.  The query is
+// read once per wave; lane l owns elements [8l + 512j, 8l + 512j + 8) of the
+// embedding, so every 16-byte load of a fact row is coalesced.  Products of
+// two bf16 values are exact; they are accumulated in float64 and reduced
+// across the wave with a butterfly, so a score differs from the exact inner
+// product by ~1e-16 relative.  HBM bound (the embeddings are read once);
+// no MFMA: one query per store is a matrix-vector product.
+//
+// topk_kernel: one 1024-lane workgroup per request.  Each wave streams
+// 64-score chunks, sorts a chunk with an in-register bitonic network and
+// merges it into its running top-64 (elementwise best of the list and the
+// reversed chunk, then a bitonic merge); the 16 wave lists are merged in LDS.
+// Order: higher score first, then smaller fact id, so ties are deterministic.
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+#include "prkv_internal.h"
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+constexpr int kScoreWaves = 4;
+constexpr int kFactsPerWave = 8;
+constexpr int kTopkThreads = 1024;
+constexpr int kMaxK = 64;
+
+struct ScoreParams {
+  const uint16_t* fact_emb;   // [n_stores][F][dim]
+  const uint16_t* query_emb;  // [n_req][dim]
+  const int32_t* req_store;   // [n_req]
+  double* scores;             // [n_req][F]
+  int32_t* status;
+  int32_t n_req, n_stores, facts_per_store, dim, groups_per_req;
+};
+
+__device__ __forceinline__ double bf16_lo(unsigned w) {
+  return double(__uint_as_float(w << 16));
+}
+__device__ __forceinline__ double bf16_hi(unsigned w) {
+  return double(__uint_as_float(w & 0xffff0000u));
+}
+
+template <int CHUNKS>  // dim / 512
+__global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams p) {
+  const int gw = blockIdx.x * kScoreWaves + threadIdx.x / kWave;
+  const int lane = threadIdx.x % kWave;
+  const int r = gw / p.groups_per_req;
+  if (r >= p.n_req) return;
+  const int f0 = (gw - r * p.groups_per_req) * kFactsPerWave;
+  const int s = p.req_store[r];
+  if (s < 0 || s >= p.n_stores) {
+    if (lane == 0 && f0 == 0 && p.status) atomicOr(p.status, 64);
+    return;
+  }
+  u32x4 q[CHUNKS];
+  const uint16_t* qrow = p.query_emb + int64_t(r) * p.dim + lane * 8;
+#pragma unroll
+  for (int j = 0; j < CHUNKS; ++j) q[j] = *reinterpret_cast<const u32x4*>(qrow + 512 * j);
+  const uint16_t* base = p.fact_emb + (int64_t(s) * p.facts_per_store) * p.dim + lane * 8;
+  const int f1 = min(f0 + kFactsPerWave, p.facts_per_store);
+  for (int f = f0; f < f1; ++f) {
+    const uint16_t* row = base + int64_t(f) * p.dim;
+    u32x4 e[CHUNKS];
+#pragma unroll
+    for (int j = 0; j < CHUNKS; ++j)
+      e[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 512 * j));
+    double acc = 0.0;
+#pragma unroll
+    for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+      for (int d = 0; d < 4; ++d) {
+        acc = __builtin_fma(bf16_lo(q[j][d]), bf16_lo(e[j][d]), acc);
+        acc = __builtin_fma(bf16_hi(q[j][d]), bf16_hi(e[j][d]), acc);
+      }
+    }
+#pragma unroll
+    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+    if (lane == 0) p.scores[int64_t(r) * p.facts_per_store + f] = acc;
+  }
+}
+
+// Order key: larger is better.  Monotone map of a double to uint64.
+__device__ __forceinline__ uint64_t order_key(double x) {
+  const uint64_t b = __double_as_longlong(x);
+  if (x != x) return 0;  // NaN ranks last
+  return (b >> 63) ? ~b : (b | 0x8000000000000000ull);
+}
+
+__device__ __forceinline__ double key_value(uint64_t k) {
+  const uint64_t b = (k >> 63) ? (k & 0x7fffffffffffffffull) : ~k;
+  return __longlong_as_double(int64_t(b));
+}
+
+struct Cand {
+  uint64_t key;
+  int32_t id;
+};
+
+__device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
+  return a.key > b.key || (a.key == b.key && a.id < b.id);
+}
+
+__device__ __forceinline__ Cand shfl_xor_cand(const Cand& c, int m) {
+  Cand o;
+  const uint32_t lo = __shfl_xor(uint32_t(c.key), m, kWave);
+  const uint32_t hi = __shfl_xor(uint32_t(c.key >> 32), m, kWave);
+  o.key = (uint64_t(hi) << 32) | lo;
+  o.id = __shfl_xor(c.id, m, kWave);
+  return o;
+}
+
+// Bitonic compare-exchange step so that, within blocks of size `blk`, lanes
+// end up ordered best-first (blocks alternate direction below 64).
+__device__ __forceinline__ Cand cx(const Cand& v, int lane, int stride, int blk) {
+  const Cand o = shfl_xor_cand(v, stride);
+  const bool lower = (lane & stride) == 0;
+  const bool best_first = (lane & blk) == 0;
+  const bool take_better = lower == best_first;
+  const bool ob = better(o, v);
+  return (take_better ? ob : !ob) ? o : v;
+}
+
+__device__ __forceinline__ Cand sort64(Cand v, int lane) {
+#pragma unroll
+  for (int blk = 2; blk <= kWave; blk <<= 1)
+#pragma unroll
+    for (int st = blk >> 1; st > 0; st >>= 1) v = cx(v, lane, st, blk == kWave ? 2 * kWave : blk);
+  return v;
+}
+
+// a, b sorted best-first: returns the 64 best of both, sorted best-first.
+__device__ __forceinline__ Cand merge64(Cand a, Cand b, int lane) {
+  // b reversed: lane i takes b[63 - i]
+  Cand br;
+  {
+    const int src = kWave - 1 - lane;
+    const uint32_t lo = __shfl(uint32_t(b.key), src, kWave);
+    const uint32_t hi = __shfl(uint32_t(b.key >> 32), src, kWave);
+    br.key = (uint64_t(hi) << 32) | lo;
+    br.id = __shfl(b.id, src, kWave);
+  }
+  Cand v = better(br, a) ? br : a;  // bitonic sequence holding the 64 best
+#pragma unroll
+  for (int st = kWave / 2; st > 0; st >>= 1) v = cx(v, lane, st, 2 * kWave);
+  return v;
+}
+
+struct TopkParams {
+  const double* scores;  // [n_req][F]
+  const int32_t* req_store;
+  int32_t* fact_ids;     // [n_req][k]
+  double* out_scores;    // [n_req][k], optional
+  int32_t n_req, n_stores, facts_per_store, k;
+};
+
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+  __shared__ uint64_t s_key[kTopkThreads];
+  __shared__ int32_t s_id[kTopkThreads];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nw = kTopkThreads / kWave;
+  const int s = p.req_store[r];
+  const bool ok = s >= 0 && s < p.n_stores;
+  const double* sc = p.scores + int64_t(r) * p.facts_per_store;
+  const Cand worst = {0, INT32_MAX};
+  Cand best = worst;
+  const int F = ok ? p.facts_per_store : 0;
+  for (int c0 = wave * kWave; c0 < F; c0 += nw * kWave) {
+    const int f = c0 + lane;
+    Cand v = worst;
+    if (f < F) {
+      v.key = order_key(sc[f]);
+      v.id = f;
+    }
+    v = sort64(v, lane);
+    best = merge64(best, v, lane);
+  }
+  s_key[threadIdx.x] = best.key;
+  s_id[threadIdx.x] = best.id;
+  __syncthreads();
+  if (wave == 0) {
+    Cand acc = {s_key[lane], s_id[lane]};
+    for (int w = 1; w < nw; ++w) {
+      const Cand other = {s_key[w * kWave + lane], s_id[w * kWave + lane]};
+      acc = merge64(acc, other, lane);
+    }
+    if (lane < p.k) {
+      const int64_t o = int64_t(r) * p.k + lane;
+      const bool real = ok && acc.id != INT32_MAX;
+      p.fact_ids[o] = real ? s * p.facts_per_store + acc.id : -1;
+      if (p.out_scores) p.out_scores[o] = real ? key_value(acc.key) : 0.0;
+    }
+  }
+}
+
+template <int CHUNKS>
+hipError_t launch_scores(const ScoreParams& p, hipStream_t s) {
+  const int64_t waves = int64_t(p.n_req) * p.groups_per_req;
+  const int64_t grid = (waves + kScoreWaves - 1) / kScoreWaves;
+  hipLaunchKernelGGL(score_kernel<CHUNKS>, dim3(unsigned(grid)), dim3(kWave * kScoreWaves), 0,
+                     s, p);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+extern "C" {
+
+int retrieve_workspace_bytes(int32_t n_req, int32_t facts_per_store, size_t* bytes) {
+  prkv::clear_error();
+  if (!bytes) return prkv::fail(PRKV_ERR_INVALID_ARG, "bytes is NULL");
+  if (n_req < 0 || facts_per_store < 0)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "negative size");
+  *bytes = size_t(n_req) * size_t(facts_per_store) * sizeof(double);
+  return PRKV_OK;
+}
+
+int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_store,
+                  int32_t dim, const void* d_query_emb, const int32_t* d_req_store,
+                  int32_t n_req, int32_t k, int32_t* d_fact_ids, double* d_scores,
+                  void* d_workspace, size_t workspace_bytes, int32_t* d_status, void* stream) {
+  prkv::clear_error();
+  if (n_req < 0 || n_stores < 1 || facts_per_store < 1)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "bad sizes (n_req %d, n_stores %d, facts %d)", n_req,
+                      n_stores, facts_per_store);
+  if (k < 1 || k > kMaxK || k > facts_per_store)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "k %d not in [1, min(64, facts_per_store)]", k);
+  if (dim < 512 || dim % 512 != 0 || dim > 4096)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "dim %d must be a multiple of 512 in [512, 4096]",
+                      dim);
+  if (int64_t(n_stores) * facts_per_store > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "n_stores * facts_per_store exceeds 2^31-1");
+  if (n_req == 0) return PRKV_OK;
+  if (!d_fact_emb || !d_query_emb || !d_req_store || !d_fact_ids || !d_workspace)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "NULL pointer argument");
+  if ((reinterpret_cast<uintptr_t>(d_fact_emb) | reinterpret_cast<uintptr_t>(d_query_emb)) & 15u)
+    return prkv::fail(PRKV_ERR_ALIGNMENT, "embeddings must be 16-byte aligned");
+  if ((reinterpret_cast<uintptr_t>(d_workspace) | reinterpret_cast<uintptr_t>(d_scores)) & 7u ||
+      (reinterpret_cast<uintptr_t>(d_req_store) | reinterpret_cast<uintptr_t>(d_fact_ids) |
+       reinterpret_cast<uintptr_t>(d_status)) & 3u)
+    return prkv::fail(PRKV_ERR_ALIGNMENT, "workspace/scores 8-byte, int32 arrays 4-byte aligned");
+  const size_t need = size_t(n_req) * size_t(facts_per_store) * sizeof(double);
+  if (workspace_bytes < need)
+    return prkv::fail(PRKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
+                      workspace_bytes);
+  ScoreParams sp;
+  sp.fact_emb = static_cast<const uint16_t*>(d_fact_emb);
+  sp.query_emb = static_cast<const uint16_t*>(d_query_emb);
+  sp.req_store = d_req_store;
+  sp.scores = static_cast<double*>(d_workspace);
+  sp.status = d_status;
+  sp.n_req = n_req;
+  sp.n_stores = n_stores;
+  sp.facts_per_store = facts_per_store;
+  sp.dim = dim;
+  sp.groups_per_req = (facts_per_store + kFactsPerWave - 1) / kFactsPerWave;
+  if (int64_t(n_req) * sp.groups_per_req / kScoreWaves + 1 > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "grid too large");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  hipError_t e;
+  switch (dim / 512) {
+    case 1: e = launch_scores<1>(sp, s); break;
+    case 2: e = launch_scores<2>(sp, s); break;
+    case 3: e = launch_scores<3>(sp, s); break;
+    case 4: e = launch_scores<4>(sp, s); break;
+    case 5: e = launch_scores<5>(sp, s); break;
+    case 6: e = launch_scores<6>(sp, s); break;
+    case 7: e = launch_scores<7>(sp, s); break;
+    case 8: e = launch_scores<8>(sp, s); break;
+    default: return prkv::fail(PRKV_ERR_INVALID_ARG, "dim %d unsupported", dim);
+  }
+  if (e != hipSuccess)
+    return prkv::fail(PRKV_ERR_HIP, "score launch: %s", hipGetErrorString(e));
+  TopkParams tp;
+  tp.scores = static_cast<const double*>(d_workspace);
+  tp.req_store = d_req_store;
+  tp.fact_ids = d_fact_ids;
+  tp.out_scores = d_scores;
+  tp.n_req = n_req;
+  tp.n_stores = n_stores;
+  tp.facts_per_store = facts_per_store;
+  tp.k = k;
+  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(n_req)), dim3(kTopkThreads), 0, s, tp);
+  e = hipGetLastError();
+  if (e != hipSuccess) return prkv::fail(PRKV_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
+  return PRKV_OK;
+}
+
+}  // extern "C"

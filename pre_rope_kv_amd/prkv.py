@@ -29,7 +29,7 @@ CODES = {v: k for k, v in ERRORS.items()}
 EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
            "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
            "last_error_string", "store_upload_fact_table", "inject_device_workspace_bytes",
-           "inject_topk_device"]
+           "inject_topk_device", "retrieve_workspace_bytes", "retrieve_topk"]
 
 
 class PrkvError(RuntimeError):
@@ -108,6 +108,11 @@ def lib():
                                               ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                               ctypes.c_int32, ctypes.c_int64, _vp,
                                               ctypes.c_size_t, _vp, _vp]),
+        "retrieve_workspace_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.POINTER(ctypes.c_size_t)]),
+        "retrieve_topk": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
+                                         _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
+                                         _vp, ctypes.c_size_t, _vp, _vp]),
         "last_error_string": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -306,3 +311,20 @@ def inject_topk_device(st, d_fact_table, batch, k_cache_layers, v_cache_layers, 
                                     int(block_size), int(num_blocks), _ptr(d_workspace),
                                     int(workspace_bytes), _ptr(d_status), _stream(stream)),
            "inject_topk_device")
+
+
+def retrieve_workspace_bytes(n_req, facts_per_store):
+    n = ctypes.c_size_t()
+    _check(lib().retrieve_workspace_bytes(int(n_req), int(facts_per_store), ctypes.byref(n)),
+           "retrieve_workspace_bytes")
+    return n.value
+
+
+def retrieve_topk(d_fact_emb, n_stores, facts_per_store, dim, d_query_emb, d_req_store, n_req,
+                  k, d_fact_ids, d_workspace, workspace_bytes, d_scores=None, d_status=None,
+                  stream=None):
+    _check(lib().retrieve_topk(_ptr(d_fact_emb), int(n_stores), int(facts_per_store), int(dim),
+                               _ptr(d_query_emb), _ptr(d_req_store), int(n_req), int(k),
+                               _ptr(d_fact_ids), _ptr(d_scores), _ptr(d_workspace),
+                               int(workspace_bytes), _ptr(d_status), _stream(stream)),
+           "retrieve_topk")

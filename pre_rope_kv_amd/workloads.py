@@ -53,6 +53,7 @@ class Spec:
     query_len: int = 0        # query tokens given blocks after the facts
     num_q_heads: int = 0      # only for the attention-equivalence check
     max_position: int = 16384
+    emb_dim: int = 1536       # retrieval embedding width
 
     @property
     def row_bytes(self):
@@ -183,6 +184,60 @@ class Workload:
         kv = torch.randn(shape, generator=g, device=device, dtype=torch.float32)
         kv = kv.to(torch.bfloat16).view(torch.int16)
         return kv[0].contiguous(), kv[1].contiguous()
+
+    # ---- retrieval embeddings -------------------------------------------
+    def _gen(self, device, *key):
+        import torch
+        st = np.random.SeedSequence([self.spec.store_seed, *key]).generate_state(2, np.uint32)
+        g = torch.Generator(device=device)
+        g.manual_seed((int(st[0]) | (int(st[1]) << 32)) & ((1 << 63) - 1))
+        return g
+
+    def _topic(self, r, device):
+        """Unit direction standing for what request r asks about."""
+        import torch
+        E = self.spec.emb_dim
+        u = torch.randn(E, generator=self._gen(device, 3_000_017, r), device=device,
+                        dtype=torch.float32)
+        return u / torch.linalg.vector_norm(u)
+
+    def store_embeddings(self, store, device="cpu"):
+        """Retrieval embeddings of one store's facts, int16 bf16 bits [F][E].
+
+        Every fact: N(0, 1/E) per element (norm close to 1).  The facts the
+        store's request drew are made relevant to that request's topic u:
+        the i-th drawn fact gets + a_i u with a_i = 0.5 - 0.25 i / k, so a
+        query along u finds exactly those facts (their scores are >= 0.25,
+        every other fact's is N(0, 1/E), about 0.026 per sigma)."""
+        import torch
+        sp = self.spec
+        E = sp.emb_dim
+        x = torch.randn((sp.facts_per_store, E), generator=self._gen(device, 2_000_003, store),
+                        device=device, dtype=torch.float32) / math.sqrt(E)
+        if store < len(self.retrieved):
+            ids = self.retrieved[store]
+            u = self._topic(store, device)
+            for i, f in enumerate(ids):
+                x[f - store * sp.facts_per_store] += (0.5 - 0.25 * i / len(ids)) * u
+        return x.to(torch.bfloat16).view(torch.int16).contiguous()
+
+    def query_embeddings(self, device="cpu", emb=None):
+        """One query per request, int16 bf16 bits [n_req][E]: the request's
+        topic direction plus N(0, 0.05^2 / E) noise.  (`emb` is accepted for
+        callers that hold the store embeddings; it is not needed.)"""
+        import torch
+        sp = self.spec
+        E = sp.emb_dim
+        out = torch.empty((sp.n_requests, E), dtype=torch.float32, device=device)
+        for r in range(sp.n_requests):
+            noise = torch.randn(E, generator=self._gen(device, 4_000_037, r), device=device,
+                                dtype=torch.float32)
+            out[r] = self._topic(r, device) + 0.05 / math.sqrt(E) * noise
+        return out.to(torch.bfloat16).view(torch.int16).contiguous()
+
+    def req_store(self):
+        """Store searched by each request: request r owns store r."""
+        return np.arange(self.spec.n_requests, dtype=np.int32)
 
     def extras_kv(self, tag, shape, device="cpu"):
         """Extra seeded N(0,1) bf16 tensor (prefix / query content), int16 bits."""

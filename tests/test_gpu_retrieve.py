@@ -1,0 +1,167 @@
+"""GPU exact top-k retrieval against the oracle, and retrieve -> inject end
+to end.
+
+Scores are float64 sums of exact bf16 products on both sides; the ranking is
+compared id for id.  Where two oracle scores are closer than 1e-12 (a near
+tie that float64 rounding may order either way) only the set is compared and
+the order is checked to be valid.
+"""
+
+import dataclasses
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import retrieve
+from pre_rope_kv_amd import harness, prkv, workloads
+
+from test_gpu_parity import (_release_device_memory, compare, oracle_images,  # noqa: F401
+                             written_mask, _say)
+
+pytestmark = pytest.mark.gpu
+
+TIE = 1e-12
+
+
+def run_retrieve(emb, q, req_store, F, k, dim, n_stores):
+    """emb: device int16 [n_stores*F][dim]; q: device int16 [n_req][dim]."""
+    n_req = q.shape[0]
+    ids = torch.full((n_req * k,), -7, dtype=torch.int32, device="cuda")
+    sc = torch.zeros(n_req * k, dtype=torch.float64, device="cuda")
+    ws_bytes = prkv.retrieve_workspace_bytes(n_req, F)
+    ws = torch.empty(max(ws_bytes, 8), dtype=torch.uint8, device="cuda")
+    status = torch.zeros(1, dtype=torch.int32, device="cuda")
+    d_rs = torch.as_tensor(req_store, dtype=torch.int32, device="cuda")
+    prkv.retrieve_topk(emb, n_stores, F, dim, q, d_rs, n_req, k, ids, ws, ws_bytes, d_scores=sc,
+                       d_status=status)
+    torch.cuda.synchronize()
+    return ids.view(n_req, k).cpu().numpy(), sc.view(n_req, k).cpu().numpy(), int(status.item())
+
+
+def check_against_oracle(emb_h, q_h, req_store, F, k, ids, sc):
+    """emb_h [n_stores][F][dim], q_h [n_req][dim] (uint16 bits)."""
+    for r in range(q_h.shape[0]):
+        s = int(req_store[r])
+        score = retrieve.scores(q_h[r], emb_h[s])
+        want = retrieve.topk(score, k)
+        got = ids[r] - s * F
+        assert np.allclose(sc[r], score[want], rtol=0, atol=1e-13 * (1 + np.abs(score[want])))
+        if np.array_equal(got, want):
+            continue
+        # near ties only: same set of best scores, order valid
+        boundary = score[want[-1]]
+        gs = score[got]
+        assert np.all(np.diff(gs) <= TIE), "GPU ranking not in score order"
+        assert set(got[gs > boundary + TIE]) == set(want[score[want] > boundary + TIE])
+        assert np.all(np.abs(gs - score[want]) <= TIE)
+
+
+def _embeddings(w, device="cuda"):
+    embs = [w.store_embeddings(s, device) for s in range(w.spec.n_requests)]
+    return embs, torch.cat(embs, 0).contiguous()
+
+
+@pytest.mark.parametrize("name", workloads.ORDER)
+def test_retrieve_matches_oracle(name):
+    w = workloads.make(name)
+    sp = w.spec
+    embs, emb = _embeddings(w)
+    q = w.query_embeddings("cuda", emb=embs)
+    ids, sc, st = run_retrieve(emb, q, w.req_store(), sp.facts_per_store, sp.k, sp.emb_dim,
+                               sp.n_requests)
+    assert st == 0
+    emb_h = emb.cpu().numpy().view(np.uint16).reshape(sp.n_requests, sp.facts_per_store, -1)
+    check_against_oracle(emb_h, q.cpu().numpy().view(np.uint16), w.req_store(),
+                         sp.facts_per_store, sp.k, ids, sc)
+    # the synthetic queries are built around the drawn facts: same set retrieved
+    same = sum(set(ids[r]) == set(w.retrieved[r]) for r in range(sp.n_requests))
+    _say(f"{name}: {same}/{sp.n_requests} requests retrieve exactly their drawn facts")
+    assert same == sp.n_requests
+
+
+@pytest.mark.parametrize("F,k,dim", [(1, 1, 512), (1003, 64, 512), (777, 7, 4096),
+                                     (64, 64, 1024), (5000, 50, 2560)])
+def test_retrieve_shapes(F, k, dim):
+    g = torch.Generator(device="cuda")
+    g.manual_seed(F * 131 + k * 7 + dim)
+    n_stores, n_req = 3, 5
+    emb = (torch.randn((n_stores * F, dim), generator=g, device="cuda") / dim ** 0.5)
+    emb = emb.to(torch.bfloat16).view(torch.int16)
+    q = (torch.randn((n_req, dim), generator=g, device="cuda") / dim ** 0.5)
+    q = q.to(torch.bfloat16).view(torch.int16)
+    req_store = np.array([0, 2, 1, 2, 0], np.int32)
+    ids, sc, st = run_retrieve(emb, q, req_store, F, k, dim, n_stores)
+    assert st == 0
+    check_against_oracle(emb.cpu().numpy().view(np.uint16).reshape(n_stores, F, dim),
+                         q.cpu().numpy().view(np.uint16), req_store, F, k, ids, sc)
+
+
+def test_retrieve_exact_ties_order_by_id():
+    """Duplicate embeddings score identically: the smaller fact id ranks first."""
+    F, dim, k = 300, 512, 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(5)
+    base = (torch.randn((F, dim), generator=g, device="cuda") / dim ** 0.5).to(torch.bfloat16)
+    base[150:] = base[:150]          # fact f and f+150 are identical
+    q = base[10:11].clone()          # query equals fact 10 (and 160)
+    emb = base.view(torch.int16).contiguous()
+    ids, sc, st = run_retrieve(emb, q.view(torch.int16), np.array([0], np.int32), F, k, dim, 1)
+    assert ids[0][0] == 10 and ids[0][1] == 160
+    check_against_oracle(emb.cpu().numpy().view(np.uint16)[None], q.view(torch.int16).cpu()
+                         .numpy().view(np.uint16), [0], F, k, ids, sc)
+
+
+def test_retrieve_bad_store_reports():
+    F, dim, k = 50, 512, 5
+    emb = torch.zeros((F, dim), dtype=torch.int16, device="cuda")
+    q = torch.zeros((2, dim), dtype=torch.int16, device="cuda")
+    ids, sc, st = run_retrieve(emb, q, np.array([0, 3], np.int32), F, k, dim, 1)
+    assert st == 64
+    assert np.all(ids[1] == -1)
+    assert list(ids[0]) == [0, 1, 2, 3, 4]   # all scores 0: id order
+
+
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k50", "llama3_8b_batch64_k50"])
+def test_retrieve_then_inject(name):
+    """retrieve_topk writes the fact ids straight into the device batch;
+    inject_topk_device then injects them.  Expected: the oracle's own top-k
+    (from the embeddings) injected by the oracle."""
+    w = workloads.make(name)
+    sp = w.spec
+    gen = "cpu" if name.startswith("tiny") else "cuda"
+    embs, emb = _embeddings(w)
+    q = w.query_embeddings("cuda", emb=embs)
+    emb_h = emb.cpu().numpy().view(np.uint16).reshape(sp.n_requests, sp.facts_per_store, -1)
+    q_h = q.cpu().numpy().view(np.uint16)
+    oracle_ids = [[int(r * sp.facts_per_store + f)
+                   for f in retrieve.topk(retrieve.scores(q_h[r], emb_h[r]), sp.k)]
+                  for r in range(sp.n_requests)]
+    dw = harness.DeviceWorkload(w, gen_device=gen, host_mapping=False)
+    dw.setup_device_batch()
+    dw.d_ids.fill_(-1)
+    ws_bytes = prkv.retrieve_workspace_bytes(sp.n_requests, sp.facts_per_store)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    d_rs = torch.as_tensor(w.req_store(), device="cuda")
+    prkv.retrieve_topk(emb, sp.n_requests, sp.facts_per_store, sp.emb_dim, q, d_rs,
+                       sp.n_requests, sp.k, dw.d_ids, ws, ws_bytes, d_status=dw.status)
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    w_oracle = dataclasses.replace(w, retrieved=oracle_ids)
+    assert w_oracle.n_tokens == w.n_tokens
+    blocks = w.listed_blocks()
+    if name.startswith("llama3_8b_batch64"):
+        # full size: compare 16 requests' blocks against the oracle
+        sub = dataclasses.replace(w_oracle, retrieved=oracle_ids[:16],
+                                  prefix=w.prefix[:16], block_tables=w.block_tables[:16],
+                                  spec=dataclasses.replace(sp, n_requests=16))
+        blocks = sub.listed_blocks()
+        img_k, img_v, _ = oracle_images(sub, gen)
+        gk, gv = dw.listed_blocks_host(blocks)
+        compare(img_k, img_v, gk, gv, written_mask(sub, blocks))
+    else:
+        img_k, img_v, _ = oracle_images(w_oracle, gen)
+        gk, gv = dw.listed_blocks_host(blocks)
+        compare(img_k, img_v, gk, gv, written_mask(w_oracle, blocks))
+    assert dw.count_non_sentinel() == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim

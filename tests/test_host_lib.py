@@ -281,3 +281,24 @@ def test_inject_device_rejects_metadata_store_and_bad_batches():
         prkv.inject_topk_device(st, 4096, b, [4096, 4096], [4096, 4096], 16, 4, 4096, 1 << 20,
                                 stream=0)
     assert ei.value.name == "NO_DEVICE"
+
+
+@pytest.mark.parametrize("kw,name", [
+    (dict(k=0), "INVALID_ARG"), (dict(k=65), "INVALID_ARG"), (dict(k=101), "INVALID_ARG"),
+    (dict(dim=1000), "INVALID_ARG"), (dict(dim=4608), "INVALID_ARG"),
+    (dict(n_stores=0), "INVALID_ARG"), (dict(fact_emb=None), "INVALID_ARG"),
+    (dict(fact_emb=4104), "ALIGNMENT"), (dict(ws_bytes=8), "BUFFER_TOO_SMALL"),
+])
+def test_retrieve_argument_errors(kw, name):
+    a = dict(fact_emb=4096, n_stores=2, F=100, dim=1536, query=8192, req_store=12288, n_req=2,
+             k=5, ids=16384, ws=20480, ws_bytes=2 * 100 * 8)
+    a.update(kw)
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.retrieve_topk(a["fact_emb"], a["n_stores"], a["F"], a["dim"], a["query"],
+                           a["req_store"], a["n_req"], a["k"], a["ids"], a["ws"], a["ws_bytes"],
+                           stream=0)
+    assert ei.value.name == name
+
+
+def test_retrieve_workspace_bytes():
+    assert prkv.retrieve_workspace_bytes(64, 2000) == 64 * 2000 * 8

@@ -8,7 +8,7 @@ the pins constrain the oracle rather than restate it.
 import numpy as np
 import pytest
 
-from oracle import bf16, paged, rope
+from oracle import bf16, paged, retrieve, rope
 
 import test_oracle_pins as pins
 
@@ -95,7 +95,27 @@ def _slot_swapped(pos, block_table, block_size):
     return int(block_table[pos % len(block_table)]) * block_size + pos // len(block_table)
 
 
+def _topk_ties_by_larger_id(score, k):
+    score = np.asarray(score, dtype=np.float64)
+    idx = np.arange(len(score))
+    return np.lexsort((-idx, -score))[:k]
+
+
+def _topk_ascending(score, k):
+    score = np.asarray(score, dtype=np.float64)
+    return np.lexsort((np.arange(len(score)), score))[:k]
+
+
+def _scores_drop_last_dim(q_bits, emb_bits):
+    q = bf16.bf16_bits_to_f64(q_bits)
+    e = bf16.bf16_bits_to_f64(emb_bits)
+    return e[:, :-1] @ q[:-1]
+
+
 MUTANTS = [
+    ("topk ties by larger id", retrieve, "topk", _topk_ties_by_larger_id),
+    ("topk ascending", retrieve, "topk", _topk_ascending),
+    ("scores drop a term", retrieve, "scores", _scores_drop_last_dim),
     ("rope sign flipped", rope, "rotate", _rotate_sign_flipped),
     ("rope interleaved pairing", rope, "rotate", _rotate_interleaved),
     ("rope frequency exponent", rope, "inv_freq", _inv_freq_wrong_exponent),

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 
 import oracle
-from oracle import attention, bf16, inject, paged, rope
+from oracle import attention, bf16, inject, paged, retrieve, rope
 
 GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
 
@@ -483,7 +483,64 @@ def test_theorem3_injected_equals_in_place():
     check_theorem3_injected_equals_in_place()
 
 
+# --------------------------------------------------------------------------
+# retrieval (exact top-k by inner product)
+# --------------------------------------------------------------------------
+
+def check_retrieve_scores_exact():
+    # bf16 products are exact in float64; math.fsum gives the correctly
+    # rounded sum, so the float64 dot product may differ only by its own
+    # rounding (<= E * 2^-53 * sum |products|)
+    import math as _m
+    rng = np.random.default_rng(16)
+    for E in (8, 512, 1536):
+        q = bf16.f64_to_bf16_bits(rng.standard_normal(E) / np.sqrt(E))
+        e = bf16.f64_to_bf16_bits(rng.standard_normal((7, E)) / np.sqrt(E))
+        got = retrieve.scores(q, e)
+        qf, ef = bf16.bf16_bits_to_f64(q), bf16.bf16_bits_to_f64(e)
+        for f in range(7):
+            prods = [float(a) * float(b) for a, b in zip(qf, ef[f])]
+            exact = _m.fsum(prods)
+            bound = E * 2.0 ** -53 * sum(abs(p) for p in prods)
+            assert abs(got[f] - exact) <= bound, (E, f, got[f], exact)
+
+
+def check_retrieve_topk_golden():
+    # hand-worked: scores 0.5, 0.9, 0.9, 0.1, 0.9 -> best three are the 0.9s in id order
+    s = [0.5, 0.9, 0.9, 0.1, 0.9]
+    assert list(retrieve.topk(s, 3)) == [1, 2, 4]
+    assert list(retrieve.topk(s, 4)) == [1, 2, 4, 0]
+    assert list(retrieve.topk([-1.0, -0.5, -2.0], 2)) == [1, 0]
+
+
+def check_retrieve_topk_brute_force():
+    rng = np.random.default_rng(17)
+    for _ in range(100):
+        F = int(rng.integers(1, 300))
+        k = int(rng.integers(1, F + 1))
+        s = np.round(rng.standard_normal(F), int(rng.integers(0, 3)))  # rounding makes ties
+        want = sorted(range(F), key=lambda f: (-s[f], f))[:k]
+        got = list(retrieve.topk(s, k))
+        assert got == want
+        if k < F:
+            rest = np.setdiff1d(np.arange(F), got)
+            assert s[got].min() >= s[rest].max()
+
+
+def test_retrieve_scores_exact():
+    check_retrieve_scores_exact()
+
+
+def test_retrieve_topk_golden():
+    check_retrieve_topk_golden()
+
+
+def test_retrieve_topk_brute_force():
+    check_retrieve_topk_brute_force()
+
+
 ALL_CHECKS = [
+    check_retrieve_scores_exact, check_retrieve_topk_golden, check_retrieve_topk_brute_force,
     check_bf16_golden, check_bf16_exhaustive_roundtrip, check_bf16_midpoints,
     check_bf16_matches_torch, check_rope_golden, check_rope_matrix_form,
     check_rope_scalar_d2, check_rope_position_zero_identity, check_rope_norm_per_pair,
