@@ -15,6 +15,7 @@ Prints one JSON line.  Only one GPU: --gpus above 1 exits with a message.
 """
 
 import argparse
+import ctypes
 import json
 import os
 import sys
@@ -39,6 +40,8 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--no-attend", action="store_true",
+                    help="skip timing the query-prefill attention over the injected cache")
     ap.add_argument("--no-retrieve", action="store_true",
                     help="skip timing retrieve_topk and retrieve + inject")
     ap.add_argument("--store", choices=("device", "host"), default="device",
@@ -406,6 +409,53 @@ def main():
         }
         del emb, q, rws
 
+    attn = None
+    if not args.no_attend and spec.head_dim in (64, 128):
+        # query prefill over the injected cache: the last q_len positions of each
+        # request's context act as its query (16 tokens, 4 query heads per KV head)
+        import math
+        q_len, hq = 16, 4 * spec.num_kv_heads
+        with torch.cuda.stream(stream):
+            dw.k_cache.zero_()
+            dw.v_cache.zero_()
+        step_kernel()   # facts back in the (otherwise zero) cache
+        ctxs = [int(w.prefix[r]) + sum(w.length_of(f) for f in ids)
+                for r, ids in enumerate(w.retrieved)]
+        g = torch.Generator(device="cuda")
+        g.manual_seed(11)
+        qt = torch.randn((spec.n_requests, q_len, hq, spec.head_dim), generator=g,
+                         device="cuda").to(torch.bfloat16).view(torch.int16)
+        q_start = torch.as_tensor([c - q_len for c in ctxs], dtype=torch.int32, device="cuda")
+        out = torch.empty((spec.num_layers, spec.n_requests, q_len, hq, spec.head_dim),
+                          dtype=torch.float32, device="cuda")
+        ab = prkv.attn_batch(spec.n_requests, q_len, hq, dw.d_bt.shape[1], qt, q_start, dw.d_bt,
+                             dw.d_bt_len, out)
+        akp = (ctypes.c_void_p * spec.num_layers)(*[t.data_ptr() for t in dw.k_layers()])
+        avp = (ctypes.c_void_p * spec.num_layers)(*[t.data_ptr() for t in dw.v_layers()])
+        aargs = (dw.store.handle, ctypes.byref(ab), akp, avp, spec.block_size, w.num_blocks,
+                 1.0 / math.sqrt(spec.head_dim), dw.status.data_ptr(), stream.cuda_stream)
+
+        def step_attend():
+            call(lib.attend_paged, aargs, "attend_paged")
+
+        _, a_per, a_ms = timed(step_attend)
+        assert int(dw.status.item()) == 0
+        assert bool(torch.isfinite(out).all()), "attention produced non-finite values"
+        kv_bytes = sum(ctxs) * spec.num_layers * spec.num_kv_heads * spec.head_dim * 2 * 2
+        flops = sum(ctxs) * spec.num_layers * hq * q_len * spec.head_dim * 4
+        attn = {
+            "what": f"attend_paged: {q_len} query tokens x {hq} query heads per request over "
+                    "its whole context in the paged cache, all layers, one launch",
+            "ms": a_ms,
+            "kv_bytes": kv_bytes,
+            "hbm_gbps": kv_bytes / (a_ms * 1e-3) / 1e9,
+            "pct_of_hbm_peak": 100.0 * kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "tflops": flops / (a_ms * 1e-3) / 1e12,
+            "pct_of_bf16_mfma_peak": 100.0 * flops / (a_ms * 1e-3) / 1e12 / 2500.0,
+            "bound": "hbm (about 64 flop per byte of cache read, below the MFMA ridge)",
+        }
+        del out, qt
+
     cpu = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -456,6 +506,7 @@ def main():
         }),
         "cpu_baseline": cpu,
         "retrieval": retrieval,
+        "attention": attn,
         "e2e": e2e,
         "setup_s": setup_s,
         "timing": "per-launch events after a 1 GiB MALL flush" if args.flush

@@ -253,6 +253,41 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
                   int32_t n_req, int32_t k, int32_t* d_fact_ids, double* d_scores,
                   void* d_workspace, size_t workspace_bytes, int32_t* d_status, void* stream);
 
+/* Query-prefill attention over the paged cache, the step after injection:
+ * only the query is prefilled and it attends to the prefix, the injected
+ * facts and itself.  Source: InferScale review, "The pith" (only the query
+ * is prefilled), "Core claim" / Theorem 3 (KV injected at the intended
+ * positions is equivalent to prompt-injecting the same tokens), reference
+ * [1] (grouped-query attention).
+ * For every layer l, request r, query token i (position q_start[r] + i) and
+ * query head h (KV head h / (num_q_heads / H)):
+ *   out[l][r][i][h] = softmax_j(scale * <RoPE(q), K_l[j]>) V_l[j] over the
+ *   positions j <= q_start[r] + i, K/V read from the paged cache through the
+ *   request's block table (every such position must have been written:
+ *   prefix, injected facts and the query's own K/V).
+ * q: pre-RoPE, rotated in the kernel with the store's table.  K and V of the
+ * cache are bf16; q and the probabilities are carried as bf16 hi + lo pairs
+ * into the matrix cores, so the result is accurate to fp32 rounding.
+ * Limits: head_dim 64 or 128; q_len * (num_q_heads / H) <= 64; bt_stride
+ * <= 2048 (the table is staged in LDS).  Positions
+ * whose block is missing from the table are masked and set bit 4 of
+ * d_status.  One kernel launch on `stream`, asynchronous. */
+typedef struct prkv_attn_batch {
+  int32_t n_req;
+  int32_t q_len;               /* query tokens per request */
+  int32_t num_q_heads;         /* multiple of the store's num_kv_heads */
+  int32_t bt_stride;
+  const uint16_t* q;           /* device [n_req][q_len][num_q_heads][D] bf16 */
+  const int32_t* q_start;      /* device [n_req]: position of the first query token */
+  const int32_t* block_tables; /* device [n_req][bt_stride] */
+  const int32_t* bt_len;       /* device [n_req] */
+  float* out;                  /* device [L][n_req][q_len][num_q_heads][D] */
+} prkv_attn_batch;
+
+int attend_paged(const prkv_store* st, const prkv_attn_batch* batch,
+                 void* const* k_cache_layers, void* const* v_cache_layers, int32_t block_size,
+                 int64_t num_blocks, float softmax_scale, int32_t* d_status, void* stream);
+
 /* Fill a HOST buffer with the RoPE table store_create would upload:
  * [max_position][D/2][4] float32 = (cos_hi, cos_lo, sin_hi, sin_lo) with
  * cos_hi = fl32(cos a), cos_lo = fl32(cos a - cos_hi), a = pos * theta_j in

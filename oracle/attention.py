@@ -29,17 +29,13 @@ def causal_gqa(q, q_pos, k, v, k_pos, scale=None):
     if scale is None:
         scale = 1.0 / math.sqrt(d)
     out = np.zeros((tq, hq, d), dtype=np.float64)
+    k_pos = np.asarray(k_pos)
     for i in range(tq):
+        seen = k_pos <= q_pos[i]
         for h in range(hq):
             g = h // group
-            scores = []
-            values = []
-            for j in range(k.shape[0]):
-                if k_pos[j] <= q_pos[i]:
-                    scores.append(float(np.dot(q[i, h], k[j, g])) * scale)
-                    values.append(v[j, g])
-            m = max(scores)
-            w = np.array([math.exp(s - m) for s in scores])
+            scores = (k[seen, g, :] @ q[i, h]) * scale
+            w = np.exp(scores - scores.max())
             w /= w.sum()
-            out[i, h] = np.sum(w[:, None] * np.array(values), axis=0)
+            out[i, h] = w @ v[seen, g, :]
     return out

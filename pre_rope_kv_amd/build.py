@@ -20,7 +20,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libprkv.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
-DEVICE_SOURCES = ["prkv_inject.hip", "prkv_retrieve.hip"]
+DEVICE_SOURCES = ["prkv_inject.hip", "prkv_retrieve.hip", "prkv_attend.hip"]
 
 HIP_FLAGS = [
     f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-ffp-contract=off",

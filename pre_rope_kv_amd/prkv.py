@@ -29,7 +29,7 @@ CODES = {v: k for k, v in ERRORS.items()}
 EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
            "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
            "last_error_string", "store_upload_fact_table", "inject_device_workspace_bytes",
-           "inject_topk_device", "retrieve_workspace_bytes", "retrieve_topk"]
+           "inject_topk_device", "retrieve_workspace_bytes", "retrieve_topk", "attend_paged"]
 
 
 class PrkvError(RuntimeError):
@@ -65,6 +65,21 @@ class DeviceBatch(ctypes.Structure):
         ("start_pos", ctypes.c_void_p),
         ("block_tables", ctypes.c_void_p),
         ("bt_len", ctypes.c_void_p),
+    ]
+
+
+class AttnBatch(ctypes.Structure):
+    """prkv_attn_batch: device pointers of a query-prefill attention batch."""
+    _fields_ = [
+        ("n_req", ctypes.c_int32),
+        ("q_len", ctypes.c_int32),
+        ("num_q_heads", ctypes.c_int32),
+        ("bt_stride", ctypes.c_int32),
+        ("q", ctypes.c_void_p),
+        ("q_start", ctypes.c_void_p),
+        ("block_tables", ctypes.c_void_p),
+        ("bt_len", ctypes.c_void_p),
+        ("out", ctypes.c_void_p),
     ]
 
 
@@ -113,6 +128,9 @@ def lib():
         "retrieve_topk": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
                                          _vp, _vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp,
                                          _vp, ctypes.c_size_t, _vp, _vp]),
+        "attend_paged": (ctypes.c_int, [_vp, ctypes.POINTER(AttnBatch), ctypes.POINTER(_vp),
+                                        ctypes.POINTER(_vp), ctypes.c_int32, ctypes.c_int64,
+                                        ctypes.c_float, _vp, _vp]),
         "last_error_string": (ctypes.c_char_p, []),
     }
     for name, (res, args) in sig.items():
@@ -328,3 +346,20 @@ def retrieve_topk(d_fact_emb, n_stores, facts_per_store, dim, d_query_emb, d_req
                                _ptr(d_fact_ids), _ptr(d_scores), _ptr(d_workspace),
                                int(workspace_bytes), _ptr(d_status), _stream(stream)),
            "retrieve_topk")
+
+
+def attn_batch(n_req, q_len, num_q_heads, bt_stride, q, q_start, block_tables, bt_len, out):
+    return AttnBatch(int(n_req), int(q_len), int(num_q_heads), int(bt_stride), _ptr(q),
+                     _ptr(q_start), _ptr(block_tables), _ptr(bt_len), _ptr(out))
+
+
+def attend_paged(st, batch, k_cache_layers, v_cache_layers, block_size, num_blocks,
+                 softmax_scale, d_status=None, stream=None):
+    L = len(k_cache_layers)
+    if len(v_cache_layers) != L or L != st.desc.num_layers:
+        raise ValueError("need one K and one V cache pointer per layer")
+    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
+    vp = (_vp * L)(*[_ptr(t) for t in v_cache_layers])
+    _check(lib().attend_paged(st.handle, ctypes.byref(batch), kp, vp, int(block_size),
+                              int(num_blocks), float(softmax_scale), _ptr(d_status),
+                              _stream(stream)), "attend_paged")

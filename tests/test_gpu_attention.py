@@ -1,0 +1,180 @@
+"""GPU query-prefill attention over the injected paged cache (attend_paged),
+Theorem 3 end to end.
+
+Each request's whole context goes through the inject path: a prefix "fact"
+at position 0, the retrieved facts, then the query's own K/V as a last
+"fact", so every position the query attends to was written by inject.  The
+expected output is the oracle's brute-force float64 attention over the same
+prompt encoded in place (each key rotated at its absolute position, the
+query rotated in float64).
+
+Tolerance, from the arithmetic: the kernel's q and probabilities enter the
+matrix cores as bf16 hi + lo pairs (relative error ~2^-16 per product) with
+fp32 accumulation over <= ~2k keys, so against attention over the SAME cache
+contents the error is ~1e-5 (bound used: 2e-4).  Against the in-place
+prompt, K may also differ by 1 bf16 ulp in a few elements (the inject bar),
+which moves a score by <= ~4e-4; bound used: 3e-3.
+"""
+
+import math
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import attention, bf16, inject, rope
+from pre_rope_kv_amd import harness, prkv, workloads
+
+from test_gpu_parity import _release_device_memory, _say, custom_workload  # noqa: F401
+
+pytestmark = pytest.mark.gpu
+
+TOL_SAME_CACHE = 2e-4
+TOL_IN_PLACE = 3e-3
+
+
+def context_workload(name, L, H, D, bs, prefix, fact_lens, q_len, n_req=1, seed=0):
+    """Request r: [prefix fact, its facts..., query fact], start position 0."""
+    rng = np.random.default_rng(seed)
+    facts, reqs, fid = {}, [], 0
+    for r in range(n_req):
+        ids = []
+        for ln in [prefix] + [int(x) for x in fact_lens[r]] + [q_len]:
+            facts[fid] = ln
+            ids.append(fid)
+            fid += 1
+        reqs.append((ids, 0))
+    # put order shuffled so rows are scattered in the arena
+    order = list(facts)
+    rng.shuffle(order)
+    w = custom_workload(name, L, H, D, bs, {f: facts[f] for f in order}, reqs, theta=5e5,
+                        num_blocks=max(512, 4 * sum(facts.values()) // bs))
+    return w
+
+
+def expected(w, q_bits, q_len, hq, layers, gen):
+    """Oracle attention over the prompt encoded in place: [len(layers)][n_req][Q][Hq][D]."""
+    sp = w.spec
+    out = np.zeros((len(layers), sp.n_requests, q_len, hq, sp.head_dim))
+    for r, ids in enumerate(w.retrieved):
+        ks, vs = [], []
+        for f in ids:
+            k, v = w.fact_kv(f, device=gen)
+            ks.append(k.cpu().numpy().view(np.uint16))
+            vs.append(v.cpu().numpy().view(np.uint16))
+        k_all = np.concatenate(ks, 1)          # [L][ctx][H][D]
+        v_all = np.concatenate(vs, 1)
+        ctx = k_all.shape[1]
+        pos = np.arange(ctx)
+        q_pos = np.arange(ctx - q_len, ctx)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta)
+        for li, l in enumerate(layers):
+            kk = bf16.bf16_bits_to_f64(inject.rotate_k_bits(k_all[l], pos[:, None], sp.rope_theta))
+            vv = bf16.bf16_bits_to_f64(v_all[l])
+            out[li, r] = attention.causal_gqa(q_rot, q_pos, kk, vv, pos,
+                                               1.0 / math.sqrt(sp.head_dim))
+    return out
+
+
+def from_cache(dw, q_bits, q_len, layers):
+    """Oracle attention over the GPU cache's own K/V (isolates the kernel)."""
+    sp = dw.w.spec
+    out = np.zeros((len(layers), sp.n_requests, q_len, q_bits.shape[2], sp.head_dim))
+    kf = dw.k_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
+    vf = dw.v_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
+    for r, ids in enumerate(dw.w.retrieved):
+        ctx = sum(dw.w.length_of(f) for f in ids)
+        bt = dw.w.block_tables[r]
+        slots = torch.as_tensor([int(bt[p // sp.block_size]) * sp.block_size + p % sp.block_size
+                                 for p in range(ctx)], device=kf.device)
+        pos = np.arange(ctx)
+        q_pos = np.arange(ctx - q_len, ctx)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta)
+        for li, l in enumerate(layers):
+            kk = bf16.bf16_bits_to_f64(kf[l, slots].cpu().numpy().view(np.uint16))
+            vv = bf16.bf16_bits_to_f64(vf[l, slots].cpu().numpy().view(np.uint16))
+            out[li, r] = attention.causal_gqa(q_rot, q_pos, kk, vv, pos,
+                                               1.0 / math.sqrt(sp.head_dim))
+    return out
+
+
+def run_attention(w, q_len, hq, gen="cuda", layers=None, seed=1, mutate_bt=None):
+    sp = w.spec
+    dw = harness.DeviceWorkload(w, gen_device=gen)
+    dw.inject()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    g = torch.Generator(device="cpu")
+    g.manual_seed(seed)
+    q_bits = torch.randn((sp.n_requests, q_len, hq, sp.head_dim), generator=g) \
+        .to(torch.bfloat16).view(torch.int16)
+    ctxs = [sum(w.length_of(f) for f in ids) for ids in w.retrieved]
+    q_start = torch.as_tensor([c - q_len for c in ctxs], dtype=torch.int32, device="cuda")
+    bt = torch.from_numpy(np.ascontiguousarray(dw.bt)).cuda()
+    bt_len = torch.from_numpy(dw.bt_len).cuda()
+    if mutate_bt is not None:
+        mutate_bt(bt, bt_len)
+    q = q_bits.cuda()
+    out = torch.full((sp.num_layers, sp.n_requests, q_len, hq, sp.head_dim), float("nan"),
+                     dtype=torch.float32, device="cuda")
+    batch = prkv.attn_batch(sp.n_requests, q_len, hq, bt.shape[1], q, q_start, bt, bt_len, out)
+    dw.status.zero_()
+    prkv.attend_paged(dw.store, batch, dw.k_layers(), dw.v_layers(), sp.block_size, w.num_blocks,
+                      1.0 / math.sqrt(sp.head_dim), d_status=dw.status)
+    torch.cuda.synchronize()
+    layers = list(range(sp.num_layers)) if layers is None else layers
+    got = out[layers].cpu().numpy().astype(np.float64)
+    return dw, q_bits.numpy().view(np.uint16), got, layers
+
+
+def check(dw, q_bits, got, q_len, hq, layers, gen):
+    assert np.all(np.isfinite(got))
+    same = from_cache(dw, q_bits, q_len, layers)
+    place = expected(dw.w, q_bits, q_len, hq, layers, gen)
+    e_same = float(np.max(np.abs(got - same)))
+    e_place = float(np.max(np.abs(got - place)))
+    _say(f"attention: max |gpu - oracle over gpu cache| = {e_same:.3g}, "
+         f"max |gpu - oracle in place| = {e_place:.3g}, mean {np.mean(np.abs(got - place)):.3g}")
+    assert e_same <= TOL_SAME_CACHE
+    assert e_place <= TOL_IN_PLACE
+
+
+def test_attention_tiny_shape():
+    # tiny workload's shape: 1 layer, 2 KV heads, D 64, 8 query heads, 4 query tokens
+    w = context_workload("attn_tiny", 1, 2, 64, 16, 32, [[17, 9, 30, 8, 21]], 4)
+    dw, qb, got, layers = run_attention(w, 4, 8, gen="cpu")
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, 4, 8, layers, "cpu")
+
+
+@pytest.mark.parametrize("bs", [16, 32])
+def test_attention_llama_shape(bs):
+    # Llama-3-8B per-layer shape (8 KV heads, 32 query heads, D 128), 16 query tokens
+    rng = np.random.default_rng(bs)
+    lens = [rng.integers(20, 61, size=10), rng.integers(20, 61, size=3)]
+    w = context_workload(f"attn_llama_bs{bs}", 3, 8, 128, bs, 64, lens, 16, n_req=2, seed=bs)
+    dw, qb, got, layers = run_attention(w, 16, 32)
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, 16, 32, layers, "cuda")
+
+
+def test_attention_long_context_k50():
+    # one request with 50 facts (~2k keys), two of its layers checked
+    rng = np.random.default_rng(50)
+    w = context_workload("attn_k50", 4, 8, 128, 16, 64, [rng.integers(20, 61, size=50)], 16,
+                         seed=50)
+    dw, qb, got, layers = run_attention(w, 16, 32, layers=[0, 3])
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, 16, 32, layers, "cuda")
+
+
+def test_attention_missing_block_is_masked_and_reported():
+    rng = np.random.default_rng(7)
+    w = context_workload("attn_missing", 2, 8, 128, 16, 64, [rng.integers(20, 61, size=4)], 16)
+
+    def drop_last(bt, bt_len):
+        bt_len[0] -= 1
+
+    dw, qb, got, layers = run_attention(w, 16, 32, mutate_bt=drop_last)
+    assert int(dw.status.item()) == 4
+    assert np.all(np.isfinite(got))
