@@ -29,8 +29,16 @@
  *    layer-major; a fact owns the same contiguous row range in every layer.
  *  - Paged cache, one K and one V tensor per layer:
  *    [num_blocks][block_size][H][D] bf16; slot = block * block_size + offset.
- *  - RoPE: half-split pairing (element j pairs with j + D/2),
- *    theta_j = rope_theta^(-2j/D), x' = (x_j + i x_{j+D/2}) * exp(+i pos theta_j).
+ *  - RoPE: pair j (j = 0 .. D/2-1) is the complex number z_j = x_a + i x_b
+ *    with (a, b) = (j, j + D/2) for half-split pairing (GPT-NeoX style) or
+ *    (2j, 2j + 1) for interleaved pairing (GPT-J style); rotation to position
+ *    p is z_j' = z_j * exp(+i p f_j) with f_j = rope_theta^(-2j/D), or f_j
+ *    rescaled by the Llama 3.1 long-context rule when the descriptor asks for
+ *    it (see prkv_store_desc).
+ *  - Keys in the store are either pre-RoPE (rotated at injection to their
+ *    serving position) or already rotated at chunk-local positions 0, 1, ...
+ *    within their fact (relocated at injection by R(s), s = the fact's
+ *    serving start; R_a^T R_b = R_{b-a}, Theorem 6).
  */
 #ifndef PRKV_H
 #define PRKV_H
@@ -57,9 +65,33 @@ enum prkv_status {
   PRKV_ERR_NO_MEMORY = -11      /* host allocation failed                   */
 };
 
-enum prkv_rope_style { PRKV_ROPE_HALF_SPLIT = 0 };
+/* Pairing of the head dimensions into rotated pairs. */
+enum prkv_rope_style {
+  PRKV_ROPE_HALF_SPLIT = 0,   /* (j, j + D/2): GPT-NeoX / Hugging Face Llama  */
+  PRKV_ROPE_INTERLEAVED = 1   /* (2j, 2j + 1): GPT-J / original Llama          */
+};
 
-/* Shape of a store and of the model it serves. */
+/* Frequency rule.  LLAMA3 is the long-context rescaling published with
+ * Llama 3.1 (one of the models the InferScale review evaluates, "Referee
+ * Report" Summary): with wavelength w_j = 2 pi / f_j, W = original_max_position,
+ * f_j is kept where w_j < W / high_freq_factor, divided by scaling_factor
+ * where w_j > W / low_freq_factor, and in between blended as
+ * (1 - m) f_j / scaling_factor + m f_j, m = (W / w_j - low_freq_factor) /
+ * (high_freq_factor - low_freq_factor).  Llama 3.1 uses factor 8, low 1,
+ * high 4, W = 8192, rope_theta = 5e5. */
+enum prkv_rope_scaling { PRKV_SCALING_NONE = 0, PRKV_SCALING_LLAMA3 = 1 };
+
+/* What the store's K rows hold.  PRE_ROPE: keys before rotary encoding
+ * (InferScale review, "What carries the argument").  CHUNK_LOCAL: keys
+ * already rotated at positions 0 .. len-1 of their own fact (a fact encoded
+ * on its own); injection applies the relocation R(s), s = the fact's first
+ * serving position, which equals rotating the pre-RoPE key to s + t in exact
+ * arithmetic (Theorem 6) but not bit for bit, since the stored key was
+ * already rounded to bf16 once. */
+enum prkv_key_layout { PRKV_KEYS_PRE_ROPE = 0, PRKV_KEYS_CHUNK_LOCAL = 1 };
+
+/* Shape of a store and of the model it serves.  Zero-initialised trailing
+ * fields select the defaults (pre-RoPE keys, no frequency scaling). */
 typedef struct prkv_store_desc {
   int32_t num_layers;    /* L, 1..128                                         */
   int32_t num_kv_heads;  /* H >= 1                                            */
@@ -67,8 +99,15 @@ typedef struct prkv_store_desc {
   int32_t max_facts;     /* fact ids are 0 .. max_facts-1                     */
   int64_t capacity_rows; /* rows per layer in each arena, <= 2^31-1           */
   int32_t max_position;  /* positions must be < max_position                  */
-  int32_t rope_style;    /* PRKV_ROPE_HALF_SPLIT                              */
+  int32_t rope_style;    /* prkv_rope_style                                   */
   double rope_theta;     /* RoPE base, > 1                                    */
+  int32_t key_layout;    /* prkv_key_layout                                   */
+  int32_t rope_scaling;  /* prkv_rope_scaling                                 */
+  double scaling_factor;   /* LLAMA3: >= 1                                    */
+  double low_freq_factor;  /* LLAMA3: > 0                                     */
+  double high_freq_factor; /* LLAMA3: > low_freq_factor                       */
+  int32_t original_max_position; /* LLAMA3: W >= 1                            */
+  int32_t reserved_;     /* must be 0                                         */
 } prkv_store_desc;
 
 typedef struct prkv_store prkv_store; /* opaque host-side store handle */
@@ -131,7 +170,9 @@ void store_destroy(prkv_store* st);
  *   position p lives in slot block_tables[r*bt_stride + p/block_size] *
  *   block_size + p % block_size, for p/block_size < bt_len[r].
  * Outputs (host int32, `capacity` entries each), in request, fact, token
- * order: src_row (arena row), pos (position), slot (cache slot); *n_tokens
+ * order: src_row (arena row), pos (rotation position: the token's serving
+ * position for a PRE_ROPE store, its fact's first serving position, i.e. the
+ * relocation offset, for a CHUNK_LOCAL store), slot (cache slot); *n_tokens
  * is the token count.  If capacity is too small, BUFFER_TOO_SMALL is returned
  * with *n_tokens set to the count needed and the outputs untouched.
  * Errors: INVALID_ARG, UNKNOWN_FACT, OUT_OF_RANGE (position >= max_position,
@@ -146,7 +187,7 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
                        int64_t* n_tokens);
 
 /* Gather, rotate and scatter: for every token t and layer l,
- *   Kcache_l[slot[t]] = RoPE(pos[t]) applied to Karena[l][src_row[t]]
+ *   Kcache_l[slot[t]] = R(pos[t]) applied to Karena[l][src_row[t]]
  *   Vcache_l[slot[t]] = Varena[l][src_row[t]]            (bit copy)
  * Source: InferScale review, "What carries the argument" (keys stored
  * pre-RoPE are re-rotated to serving-time positions on injection into the
@@ -290,8 +331,9 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* batch,
 
 /* Fill a HOST buffer with the RoPE table store_create would upload:
  * [max_position][D/2][4] float32 = (cos_hi, cos_lo, sin_hi, sin_lo) with
- * cos_hi = fl32(cos a), cos_lo = fl32(cos a - cos_hi), a = pos * theta_j in
- * float64.  out_bytes must be >= rope_table_bytes. */
+ * cos_hi = fl32(cos a), cos_lo = fl32(cos a - cos_hi), a = pos * f_j in
+ * float64 (f_j after the descriptor's frequency rule).  out_bytes must be
+ * >= rope_table_bytes. */
 int rope_table_fill(const prkv_store_desc* desc, float* out, size_t out_bytes);
 
 /* Text of the last error on this thread ("" if none). */

@@ -52,3 +52,17 @@ def token_mapping(requests, fact_rows, block_size):
                 pos_out.append(p)
                 slot_out.append(slot_of(p, block_table, block_size))
     return src_row, pos_out, slot_out
+
+
+def rotation_positions(requests, fact_rows, chunk_local=False):
+    """Per injected token (same order as token_mapping): the position its key
+    is rotated by.  Pre-RoPE keys: the token's serving position.  Keys stored
+    rotated at chunk-local positions 0 .. len-1: the fact's first serving
+    position (the relocation offset), the same for every token of the fact."""
+    out = []
+    for fact_ids, prefix_len, _ in requests:
+        lengths = [fact_rows[int(f)][1] for f in fact_ids]
+        for positions in fact_positions(prefix_len, lengths):
+            for p in positions:
+                out.append(positions[0] if chunk_local else p)
+    return out

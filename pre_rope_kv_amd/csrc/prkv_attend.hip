@@ -10,9 +10,11 @@
 //
 // Work unit: one workgroup per (layer, request, KV head).  Its rows are the
 // q_len query tokens x the `group` query heads sharing that KV head (at most
-// 64 rows, 16 per wave).  Keys stream in tiles of 64 positions: the K rows of
-// the tile are gathered through the block table into LDS (row-major, padded)
-// and V is transposed into LDS on the way in.  Per tile each wave computes
+// 64 rows, 16 per wave).  Keys stream in tiles of 128 positions: the K rows
+// of the tile are gathered through the block table (kept in LDS) into
+// registers while the previous tile is computed, then written to LDS
+// (row-major, padded), V transposed on the way in.  Per 64-key step of a tile
+// each wave computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; the accumulator then holds, per
 //                  lane, 16 scores of the lane's own query row)
 //   online softmax in fp32 (exp2, running max and sum per row)
@@ -26,8 +28,8 @@
 // work (about 64 flop/B), below the MFMA ridge: it is bound by reading the
 // cache, and the doubled MFMAs cost nothing.
 //
-// The query is rotated in-kernel with the store's RoPE table (compensated
-// fp32, as in injection).  Keys outside [0, q_start + q_len), keys after the
+// The query is rotated in-kernel with the store's RoPE table and pairing
+// (compensated fp32, as in injection).  Keys outside [0, q_start + q_len), keys after the
 // row's own position (causal), and keys whose block is missing from the
 // table (reported in status bit 4) are masked.
 
@@ -48,6 +50,8 @@ constexpr int kTile = 128;      // keys staged per tile (two compute steps)
 constexpr int kMaxRows = 64;    // query rows per workgroup
 constexpr int kThreads = kMaxRows / 16 * kWave;
 constexpr int kBtLds = 2048;    // block-table entries kept in LDS
+constexpr int kVLanes = 8;      // lanes per run in the V staging
+constexpr int kVPad = 8;        // pad bytes per V^T row in LDS
 
 struct LayerCPtrs {
   const uint16_t* p[prkv::kMaxLayers];
@@ -71,13 +75,13 @@ __device__ __forceinline__ bf16x8 load8(const unsigned char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
-template <int D>
+template <int D, int STYLE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(AttnParams p, LayerCPtrs kc,
                                                           LayerCPtrs vc) {
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
   constexpr int KROW = D * 2 + 16;      // bytes per K row in LDS (padded)
-  constexpr int VROW = kTile * 2 + 8;   // bytes per V^T row in LDS (padded)
+  constexpr int VROW = kTile * 2 + kVPad;  // bytes per V^T row in LDS (padded)
   constexpr int DC = D / 8;             // 16-byte chunks per head row
   __shared__ __align__(16) unsigned char s_k[kTile * KROW];
   __shared__ __align__(16) unsigned char s_vt[D * VROW];
@@ -112,15 +116,30 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
     const bool pos_ok = qpos >= 0 && qpos < p.max_position;
+    const f32x4* rrow = p.rope + int64_t(pos_ok ? qpos : 0) * (D / 2);
+    if (STYLE == PRKV_ROPE_HALF_SPLIT) {
 #pragma unroll
-    for (int kb = 0; kb < KB / 2; ++kb) {
+      for (int kb = 0; kb < KB / 2; ++kb) {
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int j = 32 * kb + 8 * a + e;  // pairs with j + D/2 (k-block kb + KB/2)
-        const f32x4 cs = pos_ok ? p.rope[int64_t(qpos) * (D / 2) + j] : f32x4{1.f, 0.f, 0.f, 0.f};
-        const float x1 = x[kb][e], x2 = x[kb + KB / 2][e];
-        x[kb][e] = rot_first(x1, x2, cs);
-        x[kb + KB / 2][e] = rot_second(x1, x2, cs);
+        for (int e = 0; e < 8; ++e) {
+          const int j = 32 * kb + 8 * a + e;  // pairs with j + D/2 (k-block kb + KB/2)
+          const f32x4 cs = pos_ok ? rrow[j] : f32x4{1.f, 0.f, 0.f, 0.f};
+          const float x1 = x[kb][e], x2 = x[kb + KB / 2][e];
+          x[kb][e] = rot_first(x1, x2, cs);
+          x[kb + KB / 2][e] = rot_second(x1, x2, cs);
+        }
+      }
+    } else {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+#pragma unroll
+        for (int m = 0; m < 4; ++m) {
+          const int j = 16 * kb + 4 * a + m;  // dims 2j, 2j + 1 = e 2m, 2m + 1
+          const f32x4 cs = pos_ok ? rrow[j] : f32x4{1.f, 0.f, 0.f, 0.f};
+          const float x1 = x[kb][2 * m], x2 = x[kb][2 * m + 1];
+          x[kb][2 * m] = rot_first(x1, x2, cs);
+          x[kb][2 * m + 1] = rot_second(x1, x2, cs);
+        }
       }
     }
 #pragma unroll
@@ -168,6 +187,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     const int slot = int(blk * p.block_size + pos % p.block_size);
     return pos >= ctx ? -1 : (inb ? slot : -2);
   };
+  // V item -> (key quad, dims chunk): runs of kVLanes consecutive lanes share
+  // a dims chunk and take consecutive key quads.  A run writes 64 contiguous
+  // bytes of each V^T row it touches, and the next run (next chunk, 8 rows
+  // down, 8 * VROW bytes = 16 banks over) lands beside it, so the transposed
+  // writes of a half-wave hit distinct banks; in global memory a wave reads
+  // 128 contiguous bytes of each of 32 rows.
+  static_assert((kTile / 4) % kVLanes == 0, "key quads must tile the lane runs");
+  auto v_kq = [](int item) { return item % kVLanes + kVLanes * (item / kVLanes / DC); };
+  auto v_dc = [](int item) { return (item / kVLanes) % DC; };
   // Masked keys load slot 0 (always a valid address, a cache hit) and are
   // zeroed at commit; `valid` holds one bit per load.
   u32x4 pk[KI], pv[VI][4];
@@ -187,7 +215,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int h = 0; h < VI; ++h) {
       const int item = threadIdx.x + kThreads * h;
       const int it = item < VITEMS ? item : 0;
-      const int kq = it / DC, dc = it % DC;
+      const int kq = v_kq(it), dc = v_dc(it);
 #pragma unroll
       for (int k4 = 0; k4 < 4; ++k4) {
         const int sv = slot_of(base + 4 * kq + k4);
@@ -215,7 +243,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int h = 0; h < VI; ++h) {
       const int item = threadIdx.x + kThreads * h;
       if (item < VITEMS) {
-        const int kq = item / DC, dc = item % DC;
+        const int kq = v_kq(item), dc = v_dc(item);
         u32x4 w[4];
 #pragma unroll
         for (int k4 = 0; k4 < 4; ++k4) w[k4] = (valid >> (KI + 4 * h + k4)) & 1u ? pv[h][k4] : zero;
@@ -329,8 +357,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
 
 template <int D>
 hipError_t launch_attend(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
-                         int64_t grid, hipStream_t s) {
-  hipLaunchKernelGGL(attend_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), 0, s, p, kc, vc);
+                         int64_t grid, int style, hipStream_t s) {
+  if (style == PRKV_ROPE_INTERLEAVED)
+    hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_INTERLEAVED>), dim3(unsigned(grid)),
+                       dim3(kThreads), 0, s, p, kc, vc);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_HALF_SPLIT>), dim3(unsigned(grid)),
+                       dim3(kThreads), 0, s, p, kc, vc);
   return hipGetLastError();
 }
 
@@ -404,8 +437,8 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
   p.block_size = block_size;
   p.max_position = d.max_position;
   hipStream_t s = static_cast<hipStream_t>(stream);
-  const hipError_t e = d.head_dim == 64 ? launch_attend<64>(p, kc, vc, grid, s)
-                                        : launch_attend<128>(p, kc, vc, grid, s);
+  const hipError_t e = d.head_dim == 64 ? launch_attend<64>(p, kc, vc, grid, d.rope_style, s)
+                                        : launch_attend<128>(p, kc, vc, grid, d.rope_style, s);
   if (e != hipSuccess) return prkv::fail(PRKV_ERR_HIP, "attend launch: %s", hipGetErrorString(e));
   return PRKV_OK;
 }

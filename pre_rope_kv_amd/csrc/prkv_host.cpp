@@ -55,10 +55,25 @@ int validate_desc(const prkv_store_desc* d) {
     return fail(PRKV_ERR_INVALID_ARG, "capacity_rows %lld not in [1, 2^31-1]",
                 (long long)d->capacity_rows);
   if (d->max_position < 1) return fail(PRKV_ERR_INVALID_ARG, "max_position %d < 1", d->max_position);
-  if (d->rope_style != PRKV_ROPE_HALF_SPLIT)
+  if (d->rope_style != PRKV_ROPE_HALF_SPLIT && d->rope_style != PRKV_ROPE_INTERLEAVED)
     return fail(PRKV_ERR_INVALID_ARG, "rope_style %d unsupported", d->rope_style);
   if (!(d->rope_theta > 1.0) || !std::isfinite(d->rope_theta))
     return fail(PRKV_ERR_INVALID_ARG, "rope_theta must be finite and > 1");
+  if (d->key_layout != PRKV_KEYS_PRE_ROPE && d->key_layout != PRKV_KEYS_CHUNK_LOCAL)
+    return fail(PRKV_ERR_INVALID_ARG, "key_layout %d unsupported", d->key_layout);
+  if (d->rope_scaling == PRKV_SCALING_LLAMA3) {
+    const double f = d->scaling_factor, lo = d->low_freq_factor, hi = d->high_freq_factor;
+    if (!(f >= 1.0) || !std::isfinite(f))
+      return fail(PRKV_ERR_INVALID_ARG, "scaling_factor must be finite and >= 1");
+    if (!(lo > 0.0) || !(hi > lo) || !std::isfinite(hi))
+      return fail(PRKV_ERR_INVALID_ARG, "need 0 < low_freq_factor < high_freq_factor < inf");
+    if (d->original_max_position < 1)
+      return fail(PRKV_ERR_INVALID_ARG, "original_max_position %d < 1",
+                  d->original_max_position);
+  } else if (d->rope_scaling != PRKV_SCALING_NONE) {
+    return fail(PRKV_ERR_INVALID_ARG, "rope_scaling %d unsupported", d->rope_scaling);
+  }
+  if (d->reserved_ != 0) return fail(PRKV_ERR_INVALID_ARG, "reserved_ must be 0");
   const double heads_dim = double(d->num_kv_heads) * d->head_dim;
   if (heads_dim * d->capacity_rows * d->num_layers * 2.0 > 9.0e18)
     return fail(PRKV_ERR_INVALID_ARG, "arena size overflows");
@@ -146,11 +161,27 @@ int rope_table_fill(const prkv_store_desc* desc, float* out, size_t out_bytes) {
   if (out_bytes < need)
     return fail(PRKV_ERR_BUFFER_TOO_SMALL, "rope table needs %zu bytes, got %zu", need, out_bytes);
   const int half = desc->head_dim / 2;
-  // theta_j in extended precision, then one rounding to double
+  // f_j in extended precision (with the frequency rule), then one rounding
+  // to double
   std::vector<double> inv(half);
-  for (int j = 0; j < half; ++j)
-    inv[j] = double(std::pow((long double)desc->rope_theta,
-                             -(2.0L * j) / (long double)desc->head_dim));
+  for (int j = 0; j < half; ++j) {
+    long double f = std::pow((long double)desc->rope_theta,
+                             -(2.0L * j) / (long double)desc->head_dim);
+    if (desc->rope_scaling == PRKV_SCALING_LLAMA3) {
+      const long double pi = 3.14159265358979323846264338327950288L;
+      const long double W = desc->original_max_position;
+      const long double lo = desc->low_freq_factor, hi = desc->high_freq_factor;
+      const long double factor = desc->scaling_factor;
+      const long double wavelen = 2.0L * pi / f;
+      if (wavelen > W / lo) {
+        f = f / factor;
+      } else if (wavelen >= W / hi) {
+        const long double m = (W / wavelen - lo) / (hi - lo);
+        f = (1.0L - m) * f / factor + m * f;
+      }
+    }
+    inv[j] = double(f);
+  }
   for (int64_t p = 0; p < desc->max_position; ++p) {
     float* row = out + p * int64_t(half) * 4;
     for (int j = 0; j < half; ++j) {
@@ -210,6 +241,7 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
   const size_t words = size_t((num_slots + 63) / 64);
   if (seen.size() < words) seen.resize(words, 0);
   const prkv_store_desc& d = st->desc;
+  const bool chunk_local = d.key_layout == PRKV_KEYS_CHUNK_LOCAL;
   int rc = PRKV_OK;
   for (int32_t r = 0; r < n_req && rc == PRKV_OK; ++r) {
     const int32_t* bt = block_tables + int64_t(r) * bt_stride;
@@ -223,6 +255,7 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
       }
       const int64_t row0 = st->first_row[f];
       const int32_t len = st->length[f];
+      const int64_t fact_start = p;
       if (p + len > d.max_position) {
         rc = fail(PRKV_ERR_OUT_OF_RANGE, "request %d: position %lld >= max_position %d", r,
                   (long long)(p + len - 1), d.max_position);
@@ -252,7 +285,7 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
         }
         w |= bit;
         s_row.push_back(int32_t(row0 + t));
-        s_pos.push_back(int32_t(p));
+        s_pos.push_back(int32_t(chunk_local ? fact_start : p));
         s_slot.push_back(int32_t(s));
       }
     }

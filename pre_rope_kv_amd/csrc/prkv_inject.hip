@@ -22,8 +22,10 @@
 //    large batches.)
 //  - A token's work is L*H*D/16 "chunks"; chunk (l, h, c) covers 8 RoPE
 //    pairs: 16 bytes at element h*D + 8c (first half of the head) and 16
-//    bytes at h*D + D/2 + 8c (second half).  A lane owns whole pairs, so no
-//    cross-lane exchange is needed.  Lanes take chunks lane, lane+64, ...;
+//    bytes at h*D + D/2 + 8c (second half).  With half-split pairing these
+//    hold x1 and x2 of pairs 8c .. 8c+7; with interleaved pairing each holds
+//    4 whole pairs.  Either way a lane owns whole pairs, so no cross-lane
+//    exchange is needed.  Lanes take chunks lane, lane+64, ...;
 //    since 64 is a multiple of D/16, a lane's c is fixed (lane % (D/16)) and
 //    its 8 (cos, sin) pairs are loaded once per token and kept in VGPRs for
 //    every layer.
@@ -81,7 +83,7 @@ struct InjectParams {
   int32_t iters_per_split;   // 64-chunk iterations per split
 };
 
-// Rotates 8 pairs: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
+// Half-split pairing: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
 __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const f32x4 (&cs)[8]) {
   u32x4 olo, ohi;
 #pragma unroll
@@ -95,7 +97,32 @@ __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const f32x4 (&cs)[
   hi = ohi;
 }
 
-template <int D>
+// Interleaved pairing: word d of `a` is pair 0..3 as (x1, x2), word d of `b`
+// is pair 4..7.
+__device__ __forceinline__ void rotate8_interleaved(u32x4& a, u32x4& b, const f32x4 (&cs)[8]) {
+#pragma unroll
+  for (int d = 0; d < 4; ++d) {
+    const float a1 = lo_bf16(a[d]), a2 = hi_bf16(a[d]);
+    const float b1 = lo_bf16(b[d]), b2 = hi_bf16(b[d]);
+    a[d] = pack_bf16(rot_first(a1, a2, cs[d]), rot_second(a1, a2, cs[d]));
+    b[d] = pack_bf16(rot_first(b1, b2, cs[4 + d]), rot_second(b1, b2, cs[4 + d]));
+  }
+}
+
+// LDS index of pair j's (cos, sin) within a token's row: the pairs lane c
+// needs are k*CPH + c, k = 0..7.  Half-split: the two 16-byte chunks at 8c
+// and D/2 + 8c hold pairs 8c .. 8c+7.  Interleaved: the chunk at 8c holds
+// pairs 4c .. 4c+3 and the chunk at D/2 + 8c pairs D/4 + 4c .. D/4 + 4c + 3.
+template <int D, int STYLE>
+__device__ __forceinline__ int pair_slot(int j) {
+  constexpr int CPH = D / 16;
+  if (STYLE == PRKV_ROPE_HALF_SPLIT) return (j & 7) * CPH + (j >> 3);
+  const int hi = j >= D / 4;
+  const int jj = j - hi * (D / 4);
+  return (4 * hi + (jj & 3)) * CPH + (jj >> 2);
+}
+
+template <int D, int STYLE>
 __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerPtrs kc,
                                                           LayerPtrs vc) {
   constexpr int CPH = D / 16;   // 16-byte chunks per half head
@@ -154,12 +181,13 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     }
     __syncthreads();
 
-    // 2. Stage each token's cos/sin row in LDS: pair j = 8c + k goes to k*CPH + c.
+    // 2. Stage each token's cos/sin row in LDS, ordered so that lane c reads
+    //    its 8 pairs at k*CPH + c (pair_slot).
     for (int e = threadIdx.x; e < tile_tokens * HALF; e += kThreads) {
       const int i = e / HALF, j = e - (e / HALF) * HALF;
       if (meta[3 * i] < 0) continue;
       const f32x4 v = p.rope[int64_t(meta[3 * i + 1]) * HALF + j];
-      smem[i * HALF + (j & 7) * CPH + (j >> 3)] = v;
+      smem[i * HALF + pair_slot<D, STYLE>(j)] = v;
     }
     __syncthreads();
 
@@ -200,7 +228,8 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           if (!live[u]) continue;
-          rotate8(ka[u], kb[u], cs);
+          if (STYLE == PRKV_ROPE_HALF_SPLIT) rotate8(ka[u], kb[u], cs);
+          else rotate8_interleaved(ka[u], kb[u], cs);
           uint16_t* kd = kc.p[lay[u]] + soff[u];
           uint16_t* vd = vc.p[lay[u]] + soff[u];
           __builtin_nontemporal_store(ka[u], reinterpret_cast<u32x4*>(kd));
@@ -252,6 +281,7 @@ struct DeviceBatch {
   int32_t store_max_facts;
   int32_t block_size;
   int32_t max_position;
+  int32_t chunk_local;         // rotation position = the fact's first position
 };
 
 constexpr int kPlanThreads = 1024;
@@ -356,7 +386,7 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(DeviceBatch b) {
       row = -1;
     }
     b.src_row[tok] = row;
-    b.pos[tok] = bad ? 0 : int32_t(ps);
+    b.pos[tok] = bad ? 0 : int32_t(b.chunk_local ? pos0 : ps);
     b.slot[tok] = slot;
   }
 }
@@ -385,8 +415,13 @@ int compute_units() {
 
 template <int D>
 hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
-                  int64_t grid, size_t lds, hipStream_t s) {
-  hipLaunchKernelGGL(inject_kernel<D>, dim3(unsigned(grid)), dim3(kThreads), lds, s, p, kc, vc);
+                  int64_t grid, size_t lds, int style, hipStream_t s) {
+  if (style == PRKV_ROPE_INTERLEAVED)
+    hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED>), dim3(unsigned(grid)),
+                       dim3(kThreads), lds, s, p, kc, vc);
+  else
+    hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT>), dim3(unsigned(grid)),
+                       dim3(kThreads), lds, s, p, kc, vc);
   return hipGetLastError();
 }
 
@@ -477,13 +512,13 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
 
   hipError_t e;
   switch (D) {
-    case 16: e = launch<16>(p, kc, vc, grid, lds, s); break;
-    case 32: e = launch<32>(p, kc, vc, grid, lds, s); break;
-    case 64: e = launch<64>(p, kc, vc, grid, lds, s); break;
-    case 128: e = launch<128>(p, kc, vc, grid, lds, s); break;
-    case 256: e = launch<256>(p, kc, vc, grid, lds, s); break;
-    case 512: e = launch<512>(p, kc, vc, grid, lds, s); break;
-    case 1024: e = launch<1024>(p, kc, vc, grid, lds, s); break;
+    case 16: e = launch<16>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 32: e = launch<32>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 64: e = launch<64>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 128: e = launch<128>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 256: e = launch<256>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 512: e = launch<512>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 1024: e = launch<1024>(p, kc, vc, grid, lds, d.rope_style, s); break;
     default: return prkv::fail(PRKV_ERR_INVALID_ARG, "head_dim %d unsupported", D);
   }
   if (e != hipSuccess) return hip_fail(e, "inject launch");
@@ -678,6 +713,7 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
   db.store_max_facts = st->desc.max_facts;
   db.block_size = block_size;
   db.max_position = st->desc.max_position;
+  db.chunk_local = st->desc.key_layout == PRKV_KEYS_CHUNK_LOCAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);

@@ -45,7 +45,9 @@ class DeviceWorkload:
         self.gen_device = gen_device or self.device
         self.stream = stream or torch.cuda.current_stream(self.device)
         self.desc = prkv.desc(sp.num_layers, sp.num_kv_heads, sp.head_dim, w.max_facts,
-                              w.capacity_rows, sp.max_position, sp.rope_theta)
+                              w.capacity_rows, sp.max_position, sp.rope_theta,
+                              rope_style=sp.rope_style, key_layout=sp.key_layout,
+                              llama3_scaling=sp.llama3_scaling)
         arena_bytes, rope_bytes = prkv.store_required_bytes(self.desc)
         shape = (sp.num_layers, w.capacity_rows, sp.num_kv_heads, sp.head_dim)
         self.store_location = store_location

@@ -49,6 +49,13 @@ class StoreDesc(ctypes.Structure):
         ("max_position", ctypes.c_int32),
         ("rope_style", ctypes.c_int32),
         ("rope_theta", ctypes.c_double),
+        ("key_layout", ctypes.c_int32),
+        ("rope_scaling", ctypes.c_int32),
+        ("scaling_factor", ctypes.c_double),
+        ("low_freq_factor", ctypes.c_double),
+        ("high_freq_factor", ctypes.c_double),
+        ("original_max_position", ctypes.c_int32),
+        ("reserved_", ctypes.c_int32),
     ]
 
 
@@ -174,10 +181,24 @@ def _i32(a):
     return a
 
 
+ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
+SCALING_NONE, SCALING_LLAMA3 = 0, 1
+KEYS_PRE_ROPE, KEYS_CHUNK_LOCAL = 0, 1
+
+
 def desc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows, max_position,
-         rope_theta, rope_style=0):
-    return StoreDesc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows,
-                     max_position, rope_style, float(rope_theta))
+         rope_theta, rope_style=ROPE_HALF_SPLIT, key_layout=KEYS_PRE_ROPE, llama3_scaling=None):
+    """prkv_store_desc.  llama3_scaling: None or (factor, low_freq_factor,
+    high_freq_factor, original_max_position)."""
+    d = StoreDesc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows,
+                  max_position, rope_style, float(rope_theta))
+    d.key_layout = key_layout
+    if llama3_scaling is not None:
+        factor, lo, hi, w = llama3_scaling
+        d.rope_scaling = SCALING_LLAMA3
+        d.scaling_factor, d.low_freq_factor, d.high_freq_factor = float(factor), float(lo), float(hi)
+        d.original_max_position = int(w)
+    return d
 
 
 def store_required_bytes(d):

@@ -54,6 +54,9 @@ class Spec:
     num_q_heads: int = 0      # only for the attention-equivalence check
     max_position: int = 16384
     emb_dim: int = 1536       # retrieval embedding width
+    rope_style: int = 0       # 0 half-split pairs, 1 interleaved pairs
+    llama3_scaling: tuple = None  # (factor, low, high, original max position) or None
+    key_layout: int = 0       # 0 pre-RoPE keys, 1 keys rotated at chunk-local positions
 
     @property
     def row_bytes(self):

@@ -25,7 +25,8 @@ import torch
 from oracle import attention, bf16, inject, rope
 from pre_rope_kv_amd import harness, prkv, workloads
 
-from test_gpu_parity import _release_device_memory, _say, custom_workload  # noqa: F401
+from test_gpu_parity import (_release_device_memory, _say, custom_workload,  # noqa: F401
+                             rope_kwargs)
 
 pytestmark = pytest.mark.gpu
 
@@ -67,9 +68,11 @@ def expected(w, q_bits, q_len, hq, layers, gen):
         ctx = k_all.shape[1]
         pos = np.arange(ctx)
         q_pos = np.arange(ctx - q_len, ctx)
-        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta,
+                            **rope_kwargs(sp))
         for li, l in enumerate(layers):
-            kk = bf16.bf16_bits_to_f64(inject.rotate_k_bits(k_all[l], pos[:, None], sp.rope_theta))
+            kk = bf16.bf16_bits_to_f64(inject.rotate_k_bits(k_all[l], pos[:, None], sp.rope_theta,
+                                                            **rope_kwargs(sp)))
             vv = bf16.bf16_bits_to_f64(v_all[l])
             out[li, r] = attention.causal_gqa(q_rot, q_pos, kk, vv, pos,
                                                1.0 / math.sqrt(sp.head_dim))
@@ -89,7 +92,8 @@ def from_cache(dw, q_bits, q_len, layers):
                                  for p in range(ctx)], device=kf.device)
         pos = np.arange(ctx)
         q_pos = np.arange(ctx - q_len, ctx)
-        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta,
+                            **rope_kwargs(sp))
         for li, l in enumerate(layers):
             kk = bf16.bf16_bits_to_f64(kf[l, slots].cpu().numpy().view(np.uint16))
             vv = bf16.bf16_bits_to_f64(vf[l, slots].cpu().numpy().view(np.uint16))

@@ -18,7 +18,7 @@ import numpy as np
 import pytest
 import torch
 
-from oracle import attention, bf16, inject, paged
+from oracle import attention, bf16, inject, paged, rope
 from pre_rope_kv_amd import harness, prkv, workloads
 
 pytestmark = pytest.mark.gpu
@@ -34,6 +34,17 @@ def _say(*a):
 # ---------------------------------------------------------------------------
 # helpers
 # ---------------------------------------------------------------------------
+
+def rope_kwargs(sp):
+    """The oracle's RoPE options (pairing, frequency rule) for a workload spec."""
+    return dict(style=rope.INTERLEAVED if sp.rope_style == prkv.ROPE_INTERLEAVED
+                else rope.HALF_SPLIT,
+                scaling=rope.Llama3Scaling(*sp.llama3_scaling) if sp.llama3_scaling else None)
+
+
+def is_chunk_local(sp):
+    return sp.key_layout == prkv.KEYS_CHUNK_LOCAL
+
 
 def oracle_images(w, gen_device, facts=None, prior=None):
     """Expected K/V images of every listed block, computed by the oracle from
@@ -56,7 +67,8 @@ def oracle_images(w, gen_device, facts=None, prior=None):
                               sp.head_dim, workloads.SENTINEL_BF16)
     if prior is not None:
         prior(img_k, img_v)
-    n = inject.inject(k_ar, v_ar, rows, w.requests(), sp.block_size, sp.rope_theta, img_k, img_v)
+    n = inject.inject(k_ar, v_ar, rows, w.requests(), sp.block_size, sp.rope_theta, img_k, img_v,
+                      chunk_local=is_chunk_local(sp), **rope_kwargs(sp))
     return img_k, img_v, n
 
 
@@ -100,8 +112,10 @@ def inject_via(dw, path):
     dw.inject_device()
     torch.cuda.synchronize()
     n, src, pos, slot = dw.device_mapping()
-    o_src, o_pos, o_slot = paged.token_mapping(dw.w.requests(), dw.w.fact_rows,
-                                               dw.w.spec.block_size)
+    o_src, _, o_slot = paged.token_mapping(dw.w.requests(), dw.w.fact_rows,
+                                           dw.w.spec.block_size)
+    o_pos = paged.rotation_positions(dw.w.requests(), dw.w.fact_rows,
+                                     is_chunk_local(dw.w.spec))
     assert n == len(o_src)
     assert np.array_equal(src, np.array(o_src, np.int32))
     assert np.array_equal(pos, np.array(o_pos, np.int32))
@@ -277,19 +291,20 @@ def test_llama8b_single_request_full(name, path):
     assert dw.count_non_sentinel() == expect
 
 
-def _full_size(name, n_sample_tokens, seed, path="host"):
-    spec = workloads.SPECS[name]
+def _full_size(name, n_sample_tokens, seed, path="host", **variant):
+    spec = workloads.dataclasses.replace(workloads.SPECS[name], **variant)
     # reserve: arenas + table + slack; the cache takes the rest (up to the spec)
-    w0 = workloads.make(name)
+    w0 = workloads.make(spec)
     reserve = 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes + (1 << 30)
     nb = harness.fit_num_blocks(spec, reserve)
-    w = w0 if nb == spec.num_blocks else workloads.make(name, num_blocks=nb)
+    w = w0 if nb == spec.num_blocks else workloads.make(spec, num_blocks=nb)
     _say(f"{name}: num_blocks {nb} (spec {spec.num_blocks}), tokens {w.n_tokens}")
     dw = harness.DeviceWorkload(w)
     inject_via(dw, path)
     assert int(dw.status.item()) == 0
-    src, pos, slot = (np.asarray(a) for a in
-                      paged.token_mapping(w.requests(), w.fact_rows, spec.block_size))
+    src, _, slot = (np.asarray(a) for a in
+                    paged.token_mapping(w.requests(), w.fact_rows, spec.block_size))
+    pos = np.asarray(paged.rotation_positions(w.requests(), w.fact_rows, is_chunk_local(spec)))
     assert np.array_equal(dw.d_map[2].cpu().numpy(), slot)
     L, H, D = spec.num_layers, spec.num_kv_heads, spec.head_dim
     kflat = dw.k_cache.view(L, -1, H, D)
@@ -308,7 +323,8 @@ def _full_size(name, n_sample_tokens, seed, path="host"):
             if picks:
                 kk = k[:, picks].cpu().numpy().view(np.uint16)          # [L][n][H][D]
                 pp = pos[t0 + np.array(picks)]
-                k_want.append(inject.rotate_k_bits(kk, pp[None, :, None], spec.rope_theta))
+                k_want.append(inject.rotate_k_bits(kk, pp[None, :, None], spec.rope_theta,
+                                                   **rope_kwargs(spec)))
                 k_got.append(kflat[:, s[picks]].cpu().numpy().view(np.uint16))
             t0 += ln
     assert t0 == len(src)

@@ -55,16 +55,33 @@ def test_required_bytes():
     assert table == 256 * 32 * 16
 
 
+LLAMA31 = (8.0, 1.0, 4.0, 8192)
+
+
 @pytest.mark.parametrize("bad", [
     dict(num_layers=0), dict(num_layers=129), dict(num_kv_heads=0), dict(head_dim=96),
     dict(head_dim=8), dict(head_dim=2048), dict(max_facts=0), dict(capacity_rows=0),
     dict(capacity_rows=2**31), dict(max_position=0), dict(rope_theta=1.0),
-    dict(rope_theta=float("nan")), dict(rope_style=1),
+    dict(rope_theta=float("nan")), dict(rope_style=2), dict(rope_style=-1),
+    dict(key_layout=2), dict(llama3_scaling=(0.5, 1.0, 4.0, 8192)),
+    dict(llama3_scaling=(8.0, 4.0, 1.0, 8192)), dict(llama3_scaling=(8.0, 0.0, 4.0, 8192)),
+    dict(llama3_scaling=(8.0, 1.0, 4.0, 0)), dict(llama3_scaling=(float("inf"), 1.0, 4.0, 8192)),
+    dict(raw=("rope_scaling", 2)), dict(raw=("reserved_", 1)),
 ])
 def test_bad_descriptor(bad):
+    raw = bad.pop("raw", None)
+    d = _desc(**bad)
+    if raw:
+        setattr(d, *raw)
     with pytest.raises(prkv.PrkvError) as ei:
-        prkv.store_create(_desc(**bad))
+        prkv.store_create(d)
     assert ei.value.name == "INVALID_ARG"
+
+
+def test_variant_descriptors_accepted():
+    for kw in (dict(rope_style=1), dict(key_layout=1), dict(llama3_scaling=LLAMA31),
+               dict(rope_style=1, key_layout=1, llama3_scaling=LLAMA31)):
+        prkv.store_destroy(prkv.store_create(_desc(**kw)))
 
 
 def test_store_create_pointer_rules():
@@ -149,6 +166,25 @@ def test_slot_mapping_matches_oracle(name):
     assert np.array_equal(slot, np.array(o_slot, np.int32))
 
 
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k50", "llama3_70b_batch16_k50"])
+def test_slot_mapping_chunk_local_rotation_positions(name):
+    w = workloads.make(name)
+    d = prkv.desc(w.spec.num_layers, w.spec.num_kv_heads, w.spec.head_dim, w.max_facts,
+                  w.capacity_rows, w.spec.max_position, w.spec.rope_theta,
+                  key_layout=prkv.KEYS_CHUNK_LOCAL)
+    st = prkv.store_create(d)
+    for f in w.put_order:
+        prkv.store_put_fact(st, f, w.length_of(f))
+    req_ptr, ids, start, bt, bt_len = w.csr()
+    src, pos, slot = prkv.build_slot_mapping(st, req_ptr, ids, start, bt, bt_len,
+                                             w.spec.block_size, w.num_blocks)
+    o_src, _, o_slot = paged.token_mapping(w.requests(), w.fact_rows, w.spec.block_size)
+    o_rot = paged.rotation_positions(w.requests(), w.fact_rows, chunk_local=True)
+    assert np.array_equal(src, np.array(o_src, np.int32))
+    assert np.array_equal(pos, np.array(o_rot, np.int32))
+    assert np.array_equal(slot, np.array(o_slot, np.int32))
+
+
 def _small_mapping_case():
     d = _desc(max_facts=8, capacity_rows=64, max_position=64)
     st = prkv.store_create(d)
@@ -226,12 +262,16 @@ def test_slot_mapping_empty_and_reuse():
     assert slot.tolist() == [4, 5]
 
 
-@pytest.mark.parametrize("d_model,theta", [(64, 1e4), (128, 5e5), (16, 10.0)])
-def test_rope_table_hi_lo(d_model, theta):
-    d = prkv.desc(1, 1, d_model, 1, 1, 16384, theta)
+@pytest.mark.parametrize("d_model,theta,scaled", [(64, 1e4, False), (128, 5e5, False),
+                                                  (16, 10.0, False), (128, 5e5, True),
+                                                  (64, 5e5, True)])
+def test_rope_table_hi_lo(d_model, theta, scaled):
+    d = prkv.desc(1, 1, d_model, 1, 1, 16384, theta,
+                  llama3_scaling=LLAMA31 if scaled else None)
     t = prkv.rope_table_fill(d).astype(np.float64)
     pos = np.arange(16384)
-    w = rope.rotation_factors(pos, d_model, theta)   # float64 cos + i sin
+    w = rope.rotation_factors(pos, d_model, theta,     # float64 cos + i sin
+                              rope.Llama3Scaling(*LLAMA31) if scaled else None)
     ch, cl, sh, sl = t[..., 0], t[..., 1], t[..., 2], t[..., 3]
     # hi parts are the float32 roundings; hi + lo carries ~48 bits
     assert np.array_equal(ch, w.real.astype(np.float32).astype(np.float64))

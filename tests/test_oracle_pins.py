@@ -122,9 +122,9 @@ def test_ulp_distance_definition():
 # RoPE rotation
 # --------------------------------------------------------------------------
 
-def load_rope_golden():
+def load_rope_golden(name="rope_half_split.txt"):
     cases = []
-    with open(os.path.join(GOLDEN, "rope_half_split.txt")) as fh:
+    with open(os.path.join(GOLDEN, name)) as fh:
         for line in fh:
             line = line.split("#")[0].strip()
             if not line:
@@ -138,6 +138,49 @@ def check_rope_golden():
     for p, x, want in load_rope_golden():
         got = rope.rotate(x, p, 100.0)
         assert np.allclose(got, want, rtol=0, atol=1e-15), (p, x, got, want)
+
+
+def check_rope_golden_interleaved():
+    for p, x, want in load_rope_golden("rope_interleaved.txt"):
+        got = rope.rotate(x, p, 100.0, style=rope.INTERLEAVED)
+        assert np.allclose(got, want, rtol=0, atol=1e-15), (p, x, got, want)
+
+
+def _roformer_matrix_rotation(x, p, base):
+    """RoFormer's block-diagonal R_p: 2x2 rotation blocks on dims (2j, 2j+1)."""
+    d = x.shape[-1]
+    r = np.zeros((d, d))
+    for j in range(d // 2):
+        ang = p * math.pow(base, -2.0 * j / d)
+        c, s = math.cos(ang), math.sin(ang)
+        r[2 * j, 2 * j], r[2 * j, 2 * j + 1] = c, -s
+        r[2 * j + 1, 2 * j], r[2 * j + 1, 2 * j + 1] = s, c
+    return r @ x
+
+
+def check_rope_interleaved_matrix_form():
+    rng = np.random.default_rng(17)
+    for d, base in ((64, 1e4), (128, 5e5), (8, 10.0)):
+        for p in (0, 1, 3, 37, 1000, 13311):
+            x = rng.standard_normal(d)
+            got = rope.rotate(x, p, base, style=rope.INTERLEAVED)
+            want = _roformer_matrix_rotation(x, p, base)
+            assert np.allclose(got, want, rtol=0, atol=1e-12 * max(1, p) ** 0.5), (d, p)
+
+
+def check_rope_styles_are_a_permutation():
+    # interleaved = half split conjugated by the permutation that moves the
+    # even dims to the first half and the odd dims to the second half
+    rng = np.random.default_rng(18)
+    for d in (4, 64, 128):
+        perm = np.concatenate([np.arange(0, d, 2), np.arange(1, d, 2)])
+        x = rng.standard_normal((20, d))
+        pos = rng.integers(0, 16384, size=20)
+        for scaling in (None, rope.LLAMA31):
+            a = rope.rotate(x, pos, 5e5, style=rope.INTERLEAVED, scaling=scaling)
+            b = np.empty_like(x)
+            b[:, perm] = rope.rotate(x[:, perm], pos, 5e5, scaling=scaling)
+            assert np.array_equal(a, b), d
 
 
 def _matrix_rotation(x, p, base):
@@ -217,6 +260,26 @@ def test_rope_golden_half_split():
     check_rope_golden()
 
 
+def test_rope_golden_interleaved():
+    check_rope_golden_interleaved()
+
+
+def test_rope_interleaved_matches_roformer_matrix():
+    check_rope_interleaved_matrix_form()
+
+
+def test_rope_styles_are_a_permutation():
+    check_rope_styles_are_a_permutation()
+
+
+def test_llama3_regions():
+    check_llama3_regions()
+
+
+def test_llama3_continuous_and_monotone():
+    check_llama3_continuous_and_monotone()
+
+
 def test_rope_matches_matrix_form():
     check_rope_matrix_form()
 
@@ -248,6 +311,57 @@ def test_rope_frequencies_geometric():
         assert f[0] == 1.0
         assert np.allclose(f[1:] / f[:-1], math.exp(-2.0 / d * math.log(base)), rtol=1e-14)
         assert math.isclose(f[-1], math.exp(-(d - 2) / d * math.log(base)), rel_tol=1e-14)
+
+
+# --------------------------------------------------------------------------
+# Llama 3.1 frequency rule
+# --------------------------------------------------------------------------
+
+def check_llama3_regions():
+    # Closed form of the three regions for D = 128, base 5e5, W = 8192, low 1,
+    # high 4: f_j is kept while 2 pi base^(2j/D) < W/4, divided by 8 once
+    # 2 pi base^(2j/D) > W/1, blended in between.  The boundaries in j come
+    # from logarithms, not from the oracle.
+    d, base, sc = 128, 5e5, rope.LLAMA31
+    j_keep = (d / 2) * math.log(sc.original_max_position / sc.high_freq_factor / (2 * math.pi)) \
+        / math.log(base)
+    j_div = (d / 2) * math.log(sc.original_max_position / sc.low_freq_factor / (2 * math.pi)) \
+        / math.log(base)
+    plain = rope.inv_freq(d, base)
+    scaled = rope.inv_freq(d, base, sc)
+    n_keep = n_div = n_mid = 0
+    for j in range(d // 2):
+        if j < j_keep:
+            assert scaled[j] == plain[j], j
+            n_keep += 1
+        elif j > j_div:
+            assert scaled[j] == plain[j] / sc.factor, j   # exact: a power-of-two divide
+            n_div += 1
+        else:
+            assert plain[j] / sc.factor < scaled[j] < plain[j], j
+            n_mid += 1
+    assert (n_keep, n_mid, n_div) == (29, 6, 29)
+    # no rule: the plain frequencies; factor 1: nothing changes anywhere
+    same = rope.Llama3Scaling(1.0, 1.0, 4.0, 8192)
+    assert np.array_equal(rope.inv_freq(d, base, same), plain)
+
+
+def check_llama3_continuous_and_monotone():
+    from decimal import Decimal
+    sc = rope.LLAMA31
+    # the blend meets the kept value at wavelength W/high and the divided
+    # value at W/low (continuity at both ends of the middle region)
+    for w_edge, outer in ((sc.original_max_position / sc.high_freq_factor, 1.0),
+                          (sc.original_max_position / sc.low_freq_factor, 1.0 / sc.factor)):
+        f_edge = 2 * math.pi / w_edge
+        for rel in (1 + 1e-9, 1 - 1e-9):
+            f = Decimal(repr(f_edge * rel))
+            got = float(rope.scaled_frequency(f, sc)) / float(f)
+            assert abs(got - outer) < 1e-7, (w_edge, rel, got)
+    # f' is increasing in f over a fine grid spanning all three regions
+    fs = np.geomspace(2 * math.pi / 20000, 2 * math.pi / 1000, 4000)
+    vals = [float(rope.scaled_frequency(Decimal(repr(float(f))), sc)) for f in fs]
+    assert all(b > a for a, b in zip(vals, vals[1:]))
 
 
 # --------------------------------------------------------------------------
@@ -396,6 +510,79 @@ def test_inject_equals_encode_in_place():
     check_inject_equals_encode_in_place()
 
 
+def check_chunk_local_relocation():
+    """A store of keys already rotated at chunk-local positions 0 .. len-1:
+    injection applies R(s), s = the fact's first serving position.
+    (1) a fact injected at position 0 comes out bit for bit as stored;
+    (2) every key is the correctly rounded R(s) of its stored value (textbook
+        matrix);
+    (3) against the pre-RoPE store (Theorem 6: R(s) R(t) = R(s + t)) the
+        result differs only by the one extra rounding of the stored key."""
+    c = _tiny_case(seed=3)
+    L, H, D, bs, base = c["L"], c["H"], c["D"], c["bs"], c["base"]
+    for style in (rope.HALF_SPLIT, rope.INTERLEAVED):
+        mat = _matrix_rotation if style == rope.HALF_SPLIT else _roformer_matrix_rotation
+        # the chunk-local store: each fact's keys rotated to t = 0 .. len-1, rounded once
+        k_local = np.empty_like(c["k"])
+        for f, (r0, ln) in c["rows"].items():
+            t = np.arange(ln)[None, :, None, None]
+            k_local[:, r0:r0 + ln] = inject.rotate_k_bits(c["k"][:, r0:r0 + ln], t[..., 0], base,
+                                                          style=style)
+        for prefix in (0, c["prefix"]):
+            req = [(c["ids"], prefix, c["bt"])]
+            imgs = {}
+            for name, arena, local in (("pre", c["k"], False), ("local", k_local, True)):
+                ik = inject.PagedImage(L, c["bt"], bs, H, D, 0x7F7F)
+                iv = inject.PagedImage(L, c["bt"], bs, H, D, 0x7F7F)
+                inject.inject(arena, c["v"], c["rows"], req, bs, base, ik, iv, style=style,
+                              chunk_local=local)
+                imgs[name] = ik
+            p = prefix
+            for i, f in enumerate(c["ids"]):
+                r0, ln = c["rows"][f]
+                for t in range(ln):
+                    s = paged.slot_of(p + t, c["bt"], bs)
+                    for layer in range(L):
+                        got_bits = imgs["local"].row(layer, s)
+                        if p == 0:
+                            assert np.array_equal(got_bits, k_local[layer, r0 + t])
+                        got = bf16.bf16_bits_to_f64(got_bits)
+                        stored = bf16.bf16_bits_to_f64(k_local[layer, r0 + t])
+                        exact = np.stack([mat(stored[h], p, base) for h in range(H)])
+                        ulp = np.exp2(np.floor(np.log2(np.abs(got))) - 7)
+                        assert np.all(np.abs(got - exact) <= 0.5 * ulp * (1 + 1e-9))
+                        pre = bf16.bf16_bits_to_f64(imgs["pre"].row(layer, s))
+                        x = bf16.bf16_bits_to_f64(c["k"][layer, r0 + t])
+                        first, second = rope.pair_indices(D, style)
+                        norm = np.hypot(x[:, first], x[:, second])
+                        bound = 3 * 2.0 ** -8 * np.concatenate([norm, norm], axis=-1)
+                        diff = np.abs(got - pre)
+                        order = np.concatenate([first, second])
+                        assert np.all(diff[:, order] <= bound), (style, prefix, f, t)
+                p += ln
+            assert prefix == 0 or p > c["prefix"]
+
+
+def test_chunk_local_relocation():
+    check_chunk_local_relocation()
+
+
+def check_rotation_positions():
+    # pre-RoPE: the serving position; chunk-local: serving position minus the
+    # token's index in its fact (so that R(rotation) R(index) = R(position))
+    c = _tiny_case(seed=4)
+    req = [(c["ids"], c["prefix"], c["bt"]), (c["ids"][::-1], 7, c["bt"])]
+    _, pos, _ = paged.token_mapping(req, c["rows"], c["bs"])
+    assert paged.rotation_positions(req, c["rows"], False) == pos
+    local = paged.rotation_positions(req, c["rows"], True)
+    idx = [t for ids, _, _ in req for f in ids for t in range(c["rows"][f][1])]
+    assert [a + t for a, t in zip(local, idx)] == pos
+
+
+def test_rotation_positions():
+    check_rotation_positions()
+
+
 def check_attention_matches_torch():
     import torch
     rng = np.random.default_rng(14)
@@ -540,6 +727,10 @@ def test_retrieve_topk_brute_force():
 
 
 ALL_CHECKS = [
+    check_rope_golden_interleaved, check_rope_interleaved_matrix_form,
+    check_rope_styles_are_a_permutation, check_llama3_regions,
+    check_llama3_continuous_and_monotone, check_chunk_local_relocation,
+    check_rotation_positions,
     check_retrieve_scores_exact, check_retrieve_topk_golden, check_retrieve_topk_brute_force,
     check_bf16_golden, check_bf16_exhaustive_roundtrip, check_bf16_midpoints,
     check_bf16_matches_torch, check_rope_golden, check_rope_matrix_form,
