@@ -55,24 +55,27 @@ def parse():
     return ap.parse_args()
 
 
-KERNEL_SOURCE = os.path.join(ROOT, "pre_rope_kv_amd", "csrc", "prkv_inject.hip")
-KERNEL_NAME = "inject_kernel"
+# kernels with committed rocprofv3 summaries: name prefix -> source file
+PROFILED = {"inject_kernel": "prkv_inject.hip", "attend_kernel": "prkv_attend.hip"}
+ATTN_Q_LEN = 16        # query tokens per request in the attention section
+ATTN_GROUP = 4         # query heads per KV head
 
 
-def kernel_source_sha():
+def kernel_source_sha(kernel="inject_kernel"):
     import hashlib
-    with open(KERNEL_SOURCE, "rb") as fh:
+    path = os.path.join(ROOT, "pre_rope_kv_amd", "csrc", PROFILED[kernel])
+    with open(path, "rb") as fh:
         return hashlib.sha256(fh.read()).hexdigest()[:16]
 
 
-def profile_path(workload):
-    return os.path.join(ROOT, "profiles", f"{KERNEL_NAME}_{workload}.md")
+def profile_path(workload, kernel="inject_kernel"):
+    return os.path.join(ROOT, "profiles", f"{kernel}_{workload}.md")
 
 
-def read_profile_traffic(workload):
+def read_profile_traffic(workload, kernel="inject_kernel"):
     """HBM bytes per launch from the committed counter summary, or None when
     there is none or the kernel source changed since it was taken."""
-    path = profile_path(workload)
+    path = profile_path(workload, kernel)
     if not os.path.exists(path):
         return None
     fields = {}
@@ -81,7 +84,7 @@ def read_profile_traffic(workload):
             if line.startswith("- ") and ": " in line:
                 k, v = line[2:].split(": ", 1)
                 fields[k.strip()] = v.strip().strip("`")
-    if fields.get("kernel_source_sha256") != kernel_source_sha():
+    if fields.get("kernel_source_sha256") != kernel_source_sha(kernel):
         return None
     try:
         return int(fields["traffic_bytes_per_launch"])
@@ -89,13 +92,37 @@ def read_profile_traffic(workload):
         return None
 
 
+def attention_bytes(w):
+    """(cache bytes read, minimal total bytes) of one attend_paged launch over
+    every request's whole context: K and V rows once, the queries once, the
+    float32 outputs once."""
+    sp = w.spec
+    ctx = sum(int(w.prefix[r]) + sum(w.length_of(f) for f in ids)
+              for r, ids in enumerate(w.retrieved))
+    hq = ATTN_GROUP * sp.num_kv_heads
+    kv = ctx * sp.num_layers * sp.num_kv_heads * sp.head_dim * 2 * 2
+    q = sp.n_requests * ATTN_Q_LEN * hq * sp.head_dim * 2
+    out = sp.num_layers * sp.n_requests * ATTN_Q_LEN * hq * sp.head_dim * 4
+    return kv, kv + q + out
+
+
+def algorithmic_bytes(kernel, w):
+    if kernel == "inject_kernel":
+        return w.n_tokens * w.spec.bytes_per_token, (
+            "read K and V rows, write K and V rows: tokens x layers x 4 x H x D x 2 B")
+    return attention_bytes(w)[1], (
+        f"K and V rows of every context position once, {ATTN_Q_LEN} bf16 query rows x "
+        f"{ATTN_GROUP} heads per KV head, float32 outputs (all layers)")
+
+
 def summarize_profile(workload, trace_dir, fetch_dir, write_dir, commands):
-    """Write the rocprofv3 summary for the inject kernel.
+    """Write the rocprofv3 summaries: one file per profiled kernel plus a
+    table of every kernel in the traced run.
 
     Counter calibration: the 4 GiB device-to-device memcpy of copy_ceiling_gbps
     (__amd_rocclr_copyBuffer, known to read 4 GiB and write 4 GiB) is looked up
-    in the same counter runs; FETCH_SIZE and WRITE_SIZE of the inject kernel
-    are scaled by (4 GiB / what the counter reads for that copy).
+    in the same counter runs; FETCH_SIZE and WRITE_SIZE of a kernel are scaled
+    by (4 GiB / what the counter reads for that copy).
     """
     import csv
     import glob
@@ -108,68 +135,82 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, commands):
         with open(files[0]) as fh:
             return list(csv.DictReader(fh))
 
-    stats = [r for r in rows(trace_dir, "kernel_stats.csv") if r["Name"].startswith(KERNEL_NAME)]
-    trace = [r for r in rows(trace_dir, "kernel_trace.csv")
-             if r["Kernel_Name"].startswith(KERNEL_NAME)]
-    durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in trace]
     copy_kib = 4 * 1024 * 1024
 
-    def counter(d, name):
+    def counter(d, name, kernel):
         rs = rows(d, "counter_collection.csv")
-        inj = [float(r["Counter_Value"]) for r in rs if r["Kernel_Name"].startswith(KERNEL_NAME)
-               and r["Counter_Name"] == name]
+        vals = [float(r["Counter_Value"]) for r in rs if r["Kernel_Name"].startswith(kernel)
+                and r["Counter_Name"] == name]
         cal = [float(r["Counter_Value"]) for r in rs
-               if r["Kernel_Name"].startswith("__amd_rocclr_copyBuffer")
-               and r["Kernel_Name"].strip() == "__amd_rocclr_copyBuffer"
+               if r["Kernel_Name"].strip() == "__amd_rocclr_copyBuffer"
                and r["Counter_Name"] == name and float(r["Counter_Value"]) > copy_kib / 4]
-        return statistics.mean(inj), statistics.mean(cal), len(inj), len(cal)
+        return statistics.mean(vals), statistics.mean(cal), len(vals), len(cal)
 
-    f_inj, f_cal, nf, ncf = counter(fetch_dir, "FETCH_SIZE")
-    w_inj, w_cal, nw, ncw = counter(write_dir, "WRITE_SIZE")
-    f_scale, w_scale = copy_kib / f_cal, copy_kib / w_cal
-    fetch_b = f_inj * f_scale * 1024
-    write_b = w_inj * w_scale * 1024
     from pre_rope_kv_amd import workloads
     w = workloads.make(workload)
-    alg = w.n_tokens * w.spec.bytes_per_token
-    st = stats[0]
-    lines = [
-        f"# {KERNEL_NAME} on {workload} (MI355X, gfx950)",
-        "",
-        "rocprofv3 summaries of `bench.py` on one MI355X; raw CSVs stay in the run's",
-        "output directory.  Commands (from the repository root):",
-        "",
-    ] + [f"    {c}" for c in commands] + [
-        "",
-        "## Kernel trace (--kernel-trace --stats)",
-        "",
-        f"- calls: {st['Calls']}",
-        f"- average_ms: {float(st['AverageNs']) / 1e6:.4f}",
-        f"- min_ms: {float(st['MinNs']) / 1e6:.4f}",
-        f"- max_ms: {float(st['MaxNs']) / 1e6:.4f}",
-        f"- median_ms_from_trace: {statistics.median(durs):.4f}",
-        f"- share_of_gpu_time_in_run_pct: {float(st['Percentage']):.2f}",
-        "",
-        "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs)",
-        "",
-        "Calibration: the 4 GiB device-to-device memcpy (`__amd_rocclr_copyBuffer`)",
-        "in the same runs reads 4 GiB and writes 4 GiB by construction.",
-        "",
-        f"- fetch_size_kib_per_launch_raw: {f_inj:.0f} (mean of {nf} launches)",
-        f"- fetch_size_kib_for_4GiB_copy: {f_cal:.0f} (mean of {ncf}); scale {f_scale:.4f}",
-        f"- write_size_kib_per_launch_raw: {w_inj:.0f} (mean of {nw} launches)",
-        f"- write_size_kib_for_4GiB_copy: {w_cal:.0f} (mean of {ncw}); scale {w_scale:.4f}",
-        f"- fetch_bytes_per_launch: {fetch_b:.0f}",
-        f"- write_bytes_per_launch: {write_b:.0f}",
-        f"- traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
-        f"- algorithmic_bytes_per_launch: {alg}",
-        f"- traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
-        f"- kernel_source_sha256: `{kernel_source_sha()}`",
-        "",
-    ]
-    with open(profile_path(workload), "w") as fh:
-        fh.write("\n".join(lines))
-    print(profile_path(workload))
+    all_stats = rows(trace_dir, "kernel_stats.csv")
+    all_trace = rows(trace_dir, "kernel_trace.csv")
+    header = ["rocprofv3 summaries of `bench.py` on one MI355X; raw CSVs stay in the run's",
+              "output directory.  Commands (from the repository root):", ""] + \
+        [f"    {c}" for c in commands]
+    for kernel in PROFILED:
+        stats = [r for r in all_stats if r["Name"].startswith(kernel)]
+        durs = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in all_trace
+                if r["Kernel_Name"].startswith(kernel)]
+        if not stats:
+            continue
+        f_k, f_cal, nf, ncf = counter(fetch_dir, "FETCH_SIZE", kernel)
+        w_k, w_cal, nw, ncw = counter(write_dir, "WRITE_SIZE", kernel)
+        f_scale, w_scale = copy_kib / f_cal, copy_kib / w_cal
+        fetch_b = f_k * f_scale * 1024
+        write_b = w_k * w_scale * 1024
+        alg, alg_what = algorithmic_bytes(kernel, w)
+        st = stats[0]
+        lines = [f"# {kernel} on {workload} (MI355X, gfx950)", ""] + header + [
+            "",
+            "## Kernel trace (--kernel-trace --stats)",
+            "",
+            f"- kernel: {st['Name'][:80]}",
+            f"- calls: {st['Calls']}",
+            f"- average_ms: {float(st['AverageNs']) / 1e6:.4f}",
+            f"- min_ms: {float(st['MinNs']) / 1e6:.4f}",
+            f"- max_ms: {float(st['MaxNs']) / 1e6:.4f}",
+            f"- median_ms_from_trace: {statistics.median(durs):.4f}",
+            f"- share_of_gpu_time_in_run_pct: {float(st['Percentage']):.2f}",
+            "",
+            "## HBM traffic (--pmc FETCH_SIZE, then --pmc WRITE_SIZE, separate runs)",
+            "",
+            "Calibration: the 4 GiB device-to-device memcpy (`__amd_rocclr_copyBuffer`)",
+            "in the same runs reads 4 GiB and writes 4 GiB by construction.",
+            f"Algorithmic bytes: {alg_what}.",
+            "",
+            f"- fetch_size_kib_per_launch_raw: {f_k:.0f} (mean of {nf} launches)",
+            f"- fetch_size_kib_for_4GiB_copy: {f_cal:.0f} (mean of {ncf}); scale {f_scale:.4f}",
+            f"- write_size_kib_per_launch_raw: {w_k:.0f} (mean of {nw} launches)",
+            f"- write_size_kib_for_4GiB_copy: {w_cal:.0f} (mean of {ncw}); scale {w_scale:.4f}",
+            f"- fetch_bytes_per_launch: {fetch_b:.0f}",
+            f"- write_bytes_per_launch: {write_b:.0f}",
+            f"- traffic_bytes_per_launch: {int(round(fetch_b + write_b))}",
+            f"- algorithmic_bytes_per_launch: {alg}",
+            f"- traffic_over_algorithmic: {(fetch_b + write_b) / alg:.4f}",
+            f"- kernel_source_sha256: `{kernel_source_sha(kernel)}`",
+            "",
+        ]
+        with open(profile_path(workload, kernel), "w") as fh:
+            fh.write("\n".join(lines))
+        print(profile_path(workload, kernel))
+    table = [f"# Every kernel in the traced bench run on {workload} (MI355X, gfx950)", ""] + \
+        header[:2] + ["", f"    {commands[0]}", "",
+                      "| kernel | calls | average ms | min ms | max ms | share of GPU time % |",
+                      "|---|---|---|---|---|---|"]
+    for r in sorted(all_stats, key=lambda r: -float(r["Percentage"])):
+        table.append(f"| {r['Name'][:70]} | {r['Calls']} | {float(r['AverageNs']) / 1e6:.4f} | "
+                     f"{float(r['MinNs']) / 1e6:.4f} | {float(r['MaxNs']) / 1e6:.4f} | "
+                     f"{float(r['Percentage']):.2f} |")
+    path = os.path.join(ROOT, "profiles", f"all_kernels_{workload}.md")
+    with open(path, "w") as fh:
+        fh.write("\n".join(table) + "\n")
+    print(path)
 
 
 def copy_ceiling_gbps(torch, nbytes=4 << 30, reps=10):
@@ -259,13 +300,14 @@ def main():
     args = parse()
     if args.summarize_profile:
         trace_dir, fetch_dir, write_dir = args.summarize_profile
+        regex = "|".join(list(PROFILED) + ["copyBuffer"])
         cmds = [
             f"rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o inject -f csv -- "
             "python -u bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-e2e",
-            f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"inject_kernel|copyBuffer\" "
+            f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py --steps 3 --warmup 1 "
             "--no-cpu-baseline --no-e2e",
-            f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"inject_kernel|copyBuffer\" "
+            f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {write_dir} -o write -f csv -- python -u bench.py --steps 3 --warmup 1 "
             "--no-cpu-baseline --no-e2e",
             f"python bench.py --workload {args.workload} --summarize-profile {trace_dir} "
@@ -414,7 +456,7 @@ def main():
         # query prefill over the injected cache: the last q_len positions of each
         # request's context act as its query (16 tokens, 4 query heads per KV head)
         import math
-        q_len, hq = 16, 4 * spec.num_kv_heads
+        q_len, hq = ATTN_Q_LEN, ATTN_GROUP * spec.num_kv_heads
         with torch.cuda.stream(stream):
             dw.k_cache.zero_()
             dw.v_cache.zero_()
@@ -441,8 +483,11 @@ def main():
         _, a_per, a_ms = timed(step_attend)
         assert int(dw.status.item()) == 0
         assert bool(torch.isfinite(out).all()), "attention produced non-finite values"
-        kv_bytes = sum(ctxs) * spec.num_layers * spec.num_kv_heads * spec.head_dim * 2 * 2
+        kv_bytes, a_alg = attention_bytes(w)
+        assert kv_bytes == sum(ctxs) * spec.num_layers * spec.num_kv_heads * spec.head_dim * 4
         flops = sum(ctxs) * spec.num_layers * hq * q_len * spec.head_dim * 4
+        a_traffic = (read_profile_traffic(spec.name, "attend_kernel")
+                     if (w is w0 and args.store == "device") else None)
         attn = {
             "what": f"attend_paged: {q_len} query tokens x {hq} query heads per request over "
                     "its whole context in the paged cache, all layers, one launch",
@@ -452,6 +497,11 @@ def main():
             "pct_of_hbm_peak": 100.0 * kv_bytes / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
             "tflops": flops / (a_ms * 1e-3) / 1e12,
             "pct_of_bf16_mfma_peak": 100.0 * flops / (a_ms * 1e-3) / 1e12 / 2500.0,
+            "roofline": {"bound": "hbm", "achieved": a_alg / (a_ms * 1e-3) / 1e9,
+                         "peak": PEAK_HBM_GBPS, "unit": "GB/s",
+                         "frac": a_alg / (a_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+                         "traffic": a_traffic, "kernel": f"attend_kernel<{spec.head_dim}>",
+                         "bytes_per_launch": a_alg},
             "bound": "hbm (about 64 flop per byte of cache read, below the MFMA ridge)",
         }
         del out, qt
