@@ -45,13 +45,14 @@ namespace {
 using namespace prkv_dev;
 
 constexpr int kWave = 64;
-constexpr int kKeys = 64;       // keys per compute step
-constexpr int kTile = 128;      // keys staged per tile (two compute steps)
+constexpr int kTile = 64;       // keys per tile (one compute step)
 constexpr int kMaxRows = 64;    // query rows per workgroup
 constexpr int kThreads = kMaxRows / 16 * kWave;
 constexpr int kBtLds = 2048;    // block-table entries kept in LDS
-constexpr int kVLanes = 8;      // lanes per run in the V staging
-constexpr int kVPad = 8;        // pad bytes per V^T row in LDS
+
+typedef short i16x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
+typedef __attribute__((address_space(3))) void lds_void;
 
 struct LayerCPtrs {
   const uint16_t* p[prkv::kMaxLayers];
@@ -75,17 +76,40 @@ __device__ __forceinline__ bf16x8 load8(const unsigned char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
+// i receives element i % 4 of the 8-byte words addressed by lanes i / 4,
+// i / 4 + 4, i / 4 + 8, i / 4 + 12 of its group.
+__device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
+  const i16x4 v = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_i16x4*)(p));
+  return __builtin_bit_cast(uint2, v);
+}
+
+// 16 bytes per lane from global memory straight into LDS: lane l's bytes land
+// at lds + 16 l (lds is wave-uniform; it goes to M0).  Written as inline
+// assembly on purpose: the compiler then does not track these loads, so it
+// does not make every later LDS read wait for them (it cannot tell that they
+// fill the other buffer).  The caller waits for them explicitly
+// (s_waitcnt vmcnt(0) before the barrier that publishes the tile).
+__device__ __forceinline__ void load_lds16(const void* src, unsigned char* lds) {
+  const uint32_t m0 =
+      __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(src), "s"(m0)
+               : "memory", "m0");
+}
+
 template <int D, int STYLE>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(AttnParams p, LayerCPtrs kc,
                                                           LayerCPtrs vc) {
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
-  constexpr int KROW = D * 2 + 16;      // bytes per K row in LDS (padded)
-  constexpr int VROW = kTile * 2 + kVPad;  // bytes per V^T row in LDS (padded)
-  constexpr int DC = D / 8;             // 16-byte chunks per head row
-  __shared__ __align__(16) unsigned char s_k[kTile * KROW];
-  __shared__ __align__(16) unsigned char s_vt[D * VROW];
-  __shared__ int s_slot[kTile];         // slot of each key of the tile, -1 if masked
+  constexpr int ROWB = D * 2;           // bytes per K or V row
+  constexpr int DC = D / 8;             // 16-byte chunks per row
+  constexpr int TILEB = kTile * ROWB;   // bytes per K or V tile
+  // two tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
+  __shared__ __align__(1024) unsigned char s_kv[2][2][TILEB];
+  __shared__ __align__(16) int s_slots[3][kTile];  // per key: slot, -1 beyond ctx, -2 missing
   __shared__ int s_bt[kBtLds];          // the request's block table (first kBtLds entries)
 
   const int g = blockIdx.x % p.num_kv_heads;
@@ -146,7 +170,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
-        const float v = row_ok ? x[kb][e] : 0.f;
+        const float v = row_ok ? x[kb][e] * p.scale_log2 : 0.f;  // scores come out in log2 units
         const __bf16 h = (__bf16)v;
         qh[kb][e] = h;
         ql[kb][e] = (__bf16)(v - (float)h);
@@ -166,127 +190,113 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   const int64_t row_elems = int64_t(p.num_kv_heads) * D;
   const int ntiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
 
-  // Staging of a 128-key tile by the workgroup's lanes: K as kTile x DC
-  // 16-byte chunks (KI per lane), V as kTile/4 x DC items of 4 keys x 8 dims
-  // (VI per lane).  The loads of tile t+1 are issued into registers before
-  // tile t is computed and written to LDS after the next barrier.
-  constexpr int KI = kTile * DC / kThreads;
-  constexpr int VITEMS = (kTile / 4) * DC;
-  constexpr int VI = (VITEMS + kThreads - 1) / kThreads;
-  static_assert(KI >= 1 && kTile * DC % kThreads == 0, "K staging must tile the workgroup");
-  static_assert(KI + 4 * VI <= 32, "validity bits");
   // (the host checks bt_stride <= kBtLds, so nb <= kBtLds)
   for (int i = threadIdx.x; i < nb; i += kThreads) s_bt[i] = btr[i];
   __syncthreads();
-  // Slot of position pos: -1 beyond the context, -2 block missing from the
-  // table.  Branch-free, so the prefetch below is straight-line code.
+  // Slot of position pos < ctx, or -2 when its block is missing from the table.
   auto slot_of = [&](int pos) -> int {
     const int bi = pos / p.block_size;
     const int64_t blk = s_bt[bi < nb ? bi : 0];
     const bool inb = bi < nb && blk >= 0 && blk < p.num_blocks;
-    const int slot = int(blk * p.block_size + pos % p.block_size);
-    return pos >= ctx ? -1 : (inb ? slot : -2);
+    return inb ? int(blk * p.block_size + pos % p.block_size) : -2;
   };
-  // V item -> (key quad, dims chunk): runs of kVLanes consecutive lanes share
-  // a dims chunk and take consecutive key quads.  A run writes 64 contiguous
-  // bytes of each V^T row it touches, and the next run (next chunk, 8 rows
-  // down, 8 * VROW bytes = 16 banks over) lands beside it, so the transposed
-  // writes of a half-wave hit distinct banks; in global memory a wave reads
-  // 128 contiguous bytes of each of 32 rows.
-  static_assert((kTile / 4) % kVLanes == 0, "key quads must tile the lane runs");
-  auto v_kq = [](int item) { return item % kVLanes + kVLanes * (item / kVLanes / DC); };
-  auto v_dc = [](int item) { return (item / kVLanes) % DC; };
-  // Masked keys load slot 0 (always a valid address, a cache hit) and are
-  // zeroed at commit; `valid` holds one bit per load.
-  u32x4 pk[KI], pv[VI][4];
-  uint32_t valid = 0;
-  bool missing = false;  // some key's block is missing from the table
-  auto prefetch = [&](int base) {
-    valid = 0;
-#pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      const int sk = slot_of(base + c / DC);
-      valid |= uint32_t(sk >= 0) << i;
-      pk[i] = *reinterpret_cast<const u32x4*>(kl + int64_t(sk >= 0 ? sk : 0) * row_elems +
-                                              g * D + 8 * (c % DC));
-    }
-#pragma unroll
-    for (int h = 0; h < VI; ++h) {
-      const int item = threadIdx.x + kThreads * h;
-      const int it = item < VITEMS ? item : 0;
-      const int kq = v_kq(it), dc = v_dc(it);
-#pragma unroll
-      for (int k4 = 0; k4 < 4; ++k4) {
-        const int sv = slot_of(base + 4 * kq + k4);
-        valid |= uint32_t(sv >= 0 && item < VITEMS) << (KI + 4 * h + k4);
-        pv[h][k4] = *reinterpret_cast<const u32x4*>(vl + int64_t(sv >= 0 ? sv : 0) * row_elems +
-                                                    g * D + 8 * dc);
-      }
-    }
-  };
-  // registers -> LDS for the tile starting at `base` (call between barriers)
-  auto commit = [&](int base) {
-    const u32x4 zero = {0u, 0u, 0u, 0u};
+  // Is any block of the context missing?  Its keys are masked and reported;
+  // with none, a tile that ends at or before the first query position needs
+  // no mask at all (every key is visible to every row).
+  int bad = 0;
+  const int nblk = ctx > 0 ? (ctx - 1) / p.block_size + 1 : 0;
+  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+    const int64_t blk = i < nb ? s_bt[i] : -1;
+    bad |= blk < 0 || blk >= p.num_blocks;
+  }
+  const bool any_missing = __syncthreads_or(bad) != 0;
+  if (any_missing && threadIdx.x == 0 && p.status) atomicOr(p.status, 4);
+
+  // LDS layout of a tile: row k (key) of K or V is ROWB contiguous bytes;
+  // its logical 16-byte chunk c sits at chunk position c ^ swz(k).  The
+  // swizzles make the MFMA operand reads conflict-free without padding
+  // (padding is impossible: a direct load fills 1 KB contiguously):
+  //   K, read 16 rows x one chunk per 16 lanes: swk spreads the 16 rows over
+  //     all 64 banks;
+  //   V, read transposed (4 rows x 32 bytes per 16 lanes, 8 rows per 32):
+  //     swv moves each row's 32-byte piece to its own bank group.
+  auto swk = [](int k) { return D == 128 ? k % 16 : (k / 2) % 8; };
+  auto swv = [](int k) { return D == 128 ? 2 * (k % 8) : 2 * ((k / 2) % 4); };
+
+  // The slots of a tile, one per key, by the first kTile lanes two tiles
+  // ahead, in a ring of three buffers.
+  auto fill_slots = [&](int t) {
     if (threadIdx.x < kTile) {
-      const int sl = slot_of(base + threadIdx.x);
-      missing |= sl == -2;
-      s_slot[threadIdx.x] = sl;
+      const int pos = t * kTile + threadIdx.x;
+      s_slots[t % 3][threadIdx.x] = pos < ctx ? slot_of(pos) : -1;
     }
+  };
+  // Issue the direct loads of tile t into buffer t % 2.  Instruction n of
+  // the tile (DC per tile for K, the same for V) fills rows n * (64 / DC) ..
+  // of 1 KB; lane l takes row n * (64 / DC) + l / DC, chunk position l % DC,
+  // i.e. logical chunk (l % DC) ^ swizzle.  Masked keys load slot 0 (a valid
+  // address) and are zeroed before use.
+  constexpr int RPI = 64 / DC;          // rows per load instruction
+  constexpr int NI = DC / 4;            // instructions per wave per tile, for K and for V
+  auto issue = [&](int t) {
+    const int* sl = s_slots[t % 3];
+    unsigned char* kd = s_kv[t & 1][0];
+    unsigned char* vd = s_kv[t & 1][1];
 #pragma unroll
-    for (int i = 0; i < KI; ++i) {
-      const int c = threadIdx.x + kThreads * i;
-      *reinterpret_cast<u32x4*>(s_k + (c / DC) * KROW + (c % DC) * 16) =
-          (valid >> i) & 1u ? pk[i] : zero;
+    for (int i = 0; i < NI; ++i) {
+      const int n = i * 4 + wave;
+      const int k = n * RPI + lane / DC;
+      const int pk = lane % DC;
+      const int sk = sl[k];
+      const int64_t off = int64_t(sk >= 0 ? sk : 0) * row_elems + g * D;
+      load_lds16(kl + off + 8 * (pk ^ swk(k)), kd + n * 1024);
+      load_lds16(vl + off + 8 * (pk ^ swv(k)), vd + n * 1024);
     }
-#pragma unroll
-    for (int h = 0; h < VI; ++h) {
-      const int item = threadIdx.x + kThreads * h;
-      if (item < VITEMS) {
-        const int kq = v_kq(item), dc = v_dc(item);
-        u32x4 w[4];
-#pragma unroll
-        for (int k4 = 0; k4 < 4; ++k4) w[k4] = (valid >> (KI + 4 * h + k4)) & 1u ? pv[h][k4] : zero;
-#pragma unroll
-        for (int d = 0; d < 4; ++d) {
-          uint2 even, odd;  // dims 8dc + 2d and 8dc + 2d + 1, keys 4kq .. 4kq + 3
-          even.x = (w[0][d] & 0xffffu) | (w[1][d] << 16);
-          even.y = (w[2][d] & 0xffffu) | (w[3][d] << 16);
-          odd.x = (w[0][d] >> 16) | (w[1][d] & 0xffff0000u);
-          odd.y = (w[2][d] >> 16) | (w[3][d] & 0xffff0000u);
-          *reinterpret_cast<uint2*>(s_vt + (8 * dc + 2 * d) * VROW + 8 * kq) = even;
-          *reinterpret_cast<uint2*>(s_vt + (8 * dc + 2 * d + 1) * VROW + 8 * kq) = odd;
-        }
+  };
+  // Zero the K and V rows of masked keys of the tile in buffer `buf`.
+  auto zero_masked = [&](const int* sl, int buf) {
+    const u32x4 zero = {0u, 0u, 0u, 0u};
+    for (int e = threadIdx.x; e < kTile * DC; e += kThreads) {
+      const int k = e / DC;
+      if (sl[k] < 0) {
+        *reinterpret_cast<u32x4*>(s_kv[buf][0] + k * ROWB + 16 * (e % DC)) = zero;
+        *reinterpret_cast<u32x4*>(s_kv[buf][1] + k * ROWB + 16 * (e % DC)) = zero;
       }
     }
   };
-  // one 64-key step at key offset `ko` of the staged tile starting at `base`
-  auto compute = [&](int base, int ko) {
+  // One 64-key tile; `masked` (uniform) applies the causal, context and
+  // missing-block mask from the tile's slots.
+  auto compute = [&](const unsigned char* kt_lds, const unsigned char* vt_lds, int base,
+                     const int* sl, bool masked) {
     // S^T = K Q^T: lane holds keys 16kt + 4a + i of its row
     f32x4 s[4];
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int k = 16 * kt + c16;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
-        const bf16x8 ka = load8(s_k + (ko + 16 * kt + c16) * KROW + (32 * kb + 8 * a) * 2);
+        const bf16x8 ka = load8(kt_lds + k * ROWB + 16 * ((4 * kb + a) ^ swk(k)));
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, qh[kb], s[kt], 0, 0, 0);
         s[kt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(ka, ql[kb], s[kt], 0, 0, 0);
       }
     }
-    // mask, scale, online softmax
+    // mask, online softmax (scores are already scaled to log2 units)
     float mt_max = -INFINITY;
 #pragma unroll
     for (int kt = 0; kt < 4; ++kt) {
+      if (masked) {
+        const int k0 = 16 * kt + 4 * a;
+        const int4 s4 = *reinterpret_cast<const int4*>(sl + k0);
+        const int sk[4] = {s4.x, s4.y, s4.z, s4.w};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int key = ko + 16 * kt + 4 * a + i;
-        const int sk = s_slot[key];
-        const bool ok = row_ok & (base + key <= qpos) & (sk >= 0);
-        const float v = ok ? s[kt][i] * p.scale_log2 : -INFINITY;
-        s[kt][i] = v;
-        mt_max = fmaxf(mt_max, v);
+        for (int i = 0; i < 4; ++i) {
+          const bool ok = row_ok & (base + k0 + i <= qpos) & (sk[i] >= 0);
+          s[kt][i] = ok ? s[kt][i] : -INFINITY;
+        }
       }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) mt_max = fmaxf(mt_max, s[kt][i]);
     }
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
@@ -306,7 +316,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
     m_run = m_new;
-    // O^T += V^T P^T over two 32-key steps
+    // O^T += V^T P^T over two 32-key halves.  The B operand P^T of lane
+    // (a, c16) holds keys 32kk + 4a + i and 32kk + 16 + 4a + i (i = 0..3,
+    // straight from the S^T accumulators); the A operand V^T needs the same
+    // keys for dim c16 of the 16-dim tile, which two transposing reads
+    // deliver: source lane c16 addresses key 32kk + 4a + c16 / 4 (+16), dims
+    // 16mt + 4 (c16 % 4) .. + 3.
 #pragma unroll
     for (int kk = 0; kk < 2; ++kk) {
       bf16x8 ph, pl;
@@ -317,11 +332,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         ph[j] = h;
         pl[j] = (__bf16)(v - (float)h);
       }
+      const int k = 32 * kk + 4 * a + c16 / 4;   // swv(k + 16) == swv(k)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
-        const unsigned char* vr = s_vt + (16 * mt + c16) * VROW;
-        const uint2 lo4 = *reinterpret_cast<const uint2*>(vr + (ko + 32 * kk + 4 * a) * 2);
-        const uint2 hi4 = *reinterpret_cast<const uint2*>(vr + (ko + 32 * kk + 16 + 4 * a) * 2);
+        const unsigned char* vp =
+            vt_lds + k * ROWB + 16 * ((2 * mt + (c16 % 4) / 2) ^ swv(k)) + 8 * (c16 % 2);
+        const uint2 lo4 = read_tr(vp);
+        const uint2 hi4 = read_tr(vp + 16 * ROWB);
         const u32x4 packed = {lo4.x, lo4.y, hi4.x, hi4.y};
         const bf16x8 va = __builtin_bit_cast(bf16x8, packed);
         o[mt] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(va, ph, o[mt], 0, 0, 0);
@@ -330,18 +347,29 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  if (ntiles > 0) prefetch(0);
+  // Pipeline: tile t+1 streams into the other buffer while tile t is
+  // computed; slots run two tiles ahead.
+  if (ntiles > 0) {
+    fill_slots(0);
+    if (ntiles > 1) fill_slots(1);
+    __syncthreads();
+    issue(0);
+  }
   for (int t = 0; t < ntiles; ++t) {
     const int base = t * kTile;
-    __syncthreads();  // the previous tile is consumed
-    commit(base);
-    __syncthreads();
-    if (t + 1 < ntiles) prefetch(base + kTile);
-    compute(base, 0);
-    if (base + kKeys < ctx) compute(base, kKeys);
+    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t have landed
+    __syncthreads();                 // ... and every wave's; tile t-1 is consumed
+    __asm__ volatile("" ::: "memory");
+    if (t + 2 < ntiles) fill_slots(t + 2);
+    if (t + 1 < ntiles) issue(t + 1);
+    const int* sl = s_slots[t % 3];
+    const bool masked = any_missing || base + kTile - 1 > q0;
+    if (masked) {
+      zero_masked(sl, t & 1);
+      __syncthreads();
+    }
+    compute(s_kv[t & 1][0], s_kv[t & 1][1], base, sl, masked);
   }
-
-  if (missing && p.status) atomicOr(p.status, 4);
 
   // normalise and write O[layer][r][qi][hq][d], d = 16mt + 4a + i
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
