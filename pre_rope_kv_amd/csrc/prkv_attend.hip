@@ -10,28 +10,32 @@
 //
 // Work unit: one workgroup per (layer, request, KV head).  Its rows are the
 // q_len query tokens x the `group` query heads sharing that KV head (at most
-// 64 rows, 16 per wave).  Keys stream in tiles of 128 positions: the K rows
-// of the tile are gathered through the block table (kept in LDS) into
-// registers while the previous tile is computed, then written to LDS
-// (row-major, padded), V transposed on the way in.  Per 64-key step of a tile
-// each wave computes
+// 64 rows, 16 per wave).  Keys stream in tiles of 32 positions through a
+// double-buffered LDS ring: while tile t is computed, tile t+1's K and V rows
+// travel from the paged cache straight into LDS (global_load_lds_dwordx4,
+// no register staging), gathered through the block table (kept in LDS; the
+// slot of every key is computed once, two tiles ahead).  Per tile each wave
+// computes
 //   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; the accumulator then holds, per
-//                  lane, 16 scores of the lane's own query row)
-//   online softmax in fp32 (exp2, running max and sum per row)
+//                  lane, scores of the lane's own query row)
+//   online softmax in fp32 (exp2, lazily rescaled running max, running sum)
 //   O^T += V^T P^T (same MFMA; S^T's accumulator layout is exactly the B
-//                  operand layout P^T needs, with the key order permuted the
-//                  same way in V^T's A operand)
-// The rotated query and the probabilities are split into bf16 hi + lo parts
-// and multiplied twice, so the products carry ~16 significant bits and the
-// result is accurate to fp32 rounding; K and V are the cache's bf16 values.
-// At 16 query tokens the kernel reads each cache row once per 64 rows of
-// work (about 64 flop/B), below the MFMA ridge: it is bound by reading the
-// cache, and the doubled MFMAs cost nothing.
+//                  operand layout P^T needs; the V^T A operand comes from
+//                  row-major V through transposing LDS reads,
+//                  ds_read_b64_tr_b16)
+// Rows are stored unpadded with XOR-swizzled 16-byte chunks so both operand
+// reads are free of bank conflicts.  The rotated query and the
+// probabilities are split into bf16 hi + lo parts and multiplied twice, so
+// the products carry ~16 significant bits and the result is accurate to
+// fp32 rounding; K and V are the cache's bf16 values.  At 16 query tokens
+// the kernel does about 64 flop per byte of cache (128 with the doubled
+// products), below the MFMA ridge: it is bound by reading the cache.
+// ~145 VGPRs and 41 KB of LDS: three workgroups per CU.
 //
 // The query is rotated in-kernel with the store's RoPE table and pairing
-// (compensated fp32, as in injection).  Keys outside [0, q_start + q_len), keys after the
-// row's own position (causal), and keys whose block is missing from the
-// table (reported in status bit 4) are masked.
+// (compensated fp32, as in injection).  Keys outside [0, q_start + q_len),
+// keys after the row's own position (causal), and keys whose block is
+// missing from the table (reported in status bit 4) are masked.
 
 #include <hip/hip_runtime.h>
 
@@ -45,7 +49,9 @@ namespace {
 using namespace prkv_dev;
 
 constexpr int kWave = 64;
-constexpr int kTile = 64;       // keys per tile (one compute step)
+constexpr int kTile = 32;       // keys per tile
+constexpr int kStages = 2;      // LDS ring of tiles; kStages - 1 are in flight
+constexpr int kSlotRing = 4;    // slot buffers (>= kStages + 1, a power of two)
 constexpr int kMaxRows = 64;    // query rows per workgroup
 constexpr int kThreads = kMaxRows / 16 * kWave;
 constexpr int kBtLds = 2048;    // block-table entries kept in LDS
@@ -70,6 +76,7 @@ struct AttnParams {
   float scale_log2;        // softmax scale * log2(e)
   int32_t n_req, q_len, num_q_heads, num_kv_heads, group, rows;
   int32_t bt_stride, block_size, max_position;
+  int32_t bs_shift;        // log2(block_size) when it is a power of two, else -1
 };
 
 __device__ __forceinline__ bf16x8 load8(const unsigned char* p) {
@@ -84,32 +91,38 @@ __device__ __forceinline__ uint2 read_tr(const unsigned char* p) {
   return __builtin_bit_cast(uint2, v);
 }
 
+// s_waitcnt immediate that waits until at most n vector-memory operations of
+// this wave are outstanding (expcnt and lgkmcnt left at their maxima).
+constexpr unsigned vmcnt_imm(unsigned n) {
+  return (n & 15u) | ((n >> 4) << 14) | (7u << 4) | (15u << 8);
+}
+
 // 16 bytes per lane from global memory straight into LDS: lane l's bytes land
-// at lds + 16 l (lds is wave-uniform; it goes to M0).  Written as inline
+// at lds + 16 l (lds is wave-uniform; the compiler puts it in M0, the s_nop covers the
+// M0-to-LDS-DMA hazard).  Written as inline
 // assembly on purpose: the compiler then does not track these loads, so it
 // does not make every later LDS read wait for them (it cannot tell that they
 // fill the other buffer).  The caller waits for them explicitly
 // (s_waitcnt vmcnt(0) before the barrier that publishes the tile).
-__device__ __forceinline__ void load_lds16(const void* src, unsigned char* lds) {
-  const uint32_t m0 =
-      __builtin_amdgcn_readfirstlane(uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(lds))));
-  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+__device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_addr) {
+  const uint32_t m0 = __builtin_amdgcn_readfirstlane(lds_addr);
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
                :
-               : "v"(src), "s"(m0)
-               : "memory", "m0");
+               : "v"(src), "{m0}"(m0)
+               : "memory");
 }
 
 template <int D, int STYLE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) void attend_kernel(AttnParams p, LayerCPtrs kc,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(AttnParams p, LayerCPtrs kc,
                                                           LayerCPtrs vc) {
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
   constexpr int ROWB = D * 2;           // bytes per K or V row
   constexpr int DC = D / 8;             // 16-byte chunks per row
   constexpr int TILEB = kTile * ROWB;   // bytes per K or V tile
-  // two tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
-  __shared__ __align__(1024) unsigned char s_kv[2][2][TILEB];
-  __shared__ __align__(16) int s_slots[3][kTile];  // per key: slot, -1 beyond ctx, -2 missing
+  // a ring of tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
+  __shared__ __align__(1024) unsigned char s_kv[kStages][2][TILEB];
+  __shared__ __align__(16) int s_slots[kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
   __shared__ int s_bt[kBtLds];          // the request's block table (first kBtLds entries)
 
   const int g = blockIdx.x % p.num_kv_heads;
@@ -177,6 +190,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
       }
     }
   }
+  // Pin the query rotation (and the waits for its loads) here, ahead of the
+  // direct tile loads, whose completion the compiler does not track: a wait
+  // for the query's loads placed after them would also wait for the tiles.
+#pragma unroll
+  for (int kb = 0; kb < KB; ++kb) asm volatile("" ::"v"(qh[kb]), "v"(ql[kb]));
 
   f32x4 o[MT];
 #pragma unroll
@@ -195,10 +213,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   __syncthreads();
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
   auto slot_of = [&](int pos) -> int {
-    const int bi = pos / p.block_size;
+    const int bi = p.bs_shift >= 0 ? pos >> p.bs_shift : pos / p.block_size;
+    const int off = pos - bi * p.block_size;
     const int64_t blk = s_bt[bi < nb ? bi : 0];
     const bool inb = bi < nb && blk >= 0 && blk < p.num_blocks;
-    return inb ? int(blk * p.block_size + pos % p.block_size) : -2;
+    return inb ? int(blk * p.block_size + off) : -2;
   };
   // Is any block of the context missing?  Its keys are masked and reported;
   // with none, a tile that ends at or before the first query position needs
@@ -223,25 +242,28 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   auto swk = [](int k) { return D == 128 ? k % 16 : (k / 2) % 8; };
   auto swv = [](int k) { return D == 128 ? 2 * (k % 8) : 2 * ((k / 2) % 4); };
 
-  // The slots of a tile, one per key, by the first kTile lanes two tiles
-  // ahead, in a ring of three buffers.
+  // The slots of a tile, one per key, by the first kTile lanes kStages tiles
+  // ahead, in a ring of kSlotRing buffers.
   auto fill_slots = [&](int t) {
     if (threadIdx.x < kTile) {
       const int pos = t * kTile + threadIdx.x;
-      s_slots[t % 3][threadIdx.x] = pos < ctx ? slot_of(pos) : -1;
+      s_slots[t % kSlotRing][threadIdx.x] = pos < ctx ? slot_of(pos) : -1;
     }
   };
-  // Issue the direct loads of tile t into buffer t % 2.  Instruction n of
-  // the tile (DC per tile for K, the same for V) fills rows n * (64 / DC) ..
-  // of 1 KB; lane l takes row n * (64 / DC) + l / DC, chunk position l % DC,
-  // i.e. logical chunk (l % DC) ^ swizzle.  Masked keys load slot 0 (a valid
-  // address) and are zeroed before use.
-  constexpr int RPI = 64 / DC;          // rows per load instruction
-  constexpr int NI = DC / 4;            // instructions per wave per tile, for K and for V
+  // Issue the direct loads of tile t into ring buffer t % kStages.
+  // Instruction n of the tile fills 1 KB = rows n * RPI .. n * RPI + RPI - 1;
+  // lane l takes row n * RPI + l / DC, chunk position l % DC, i.e. logical
+  // chunk (l % DC) ^ swizzle.  Masked keys load slot 0 (a valid address) and
+  // are zeroed before use.
+  constexpr int RPI = 64 / DC;                  // rows per load instruction
+  constexpr int NI = kTile * DC / 64 / 4;       // instructions per wave per tile, for K and for V
+  constexpr unsigned LPT = 2 * NI;              // loads per wave per tile
+  static_assert(NI >= 1 && kTile * DC % 256 == 0, "a tile must split over the 4 waves");
+  const uint32_t kv_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(&s_kv[0][0][0])));
   auto issue = [&](int t) {
-    const int* sl = s_slots[t % 3];
-    unsigned char* kd = s_kv[t & 1][0];
-    unsigned char* vd = s_kv[t & 1][1];
+    const int* sl = s_slots[t % kSlotRing];
+    const uint32_t kd = kv_lds + uint32_t(t % kStages) * (2 * TILEB);
+    const uint32_t vd = kd + TILEB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int n = i * 4 + wave;
@@ -268,10 +290,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
   // missing-block mask from the tile's slots.
   auto compute = [&](const unsigned char* kt_lds, const unsigned char* vt_lds, int base,
                      const int* sl, bool masked) {
+    constexpr int KT = kTile / 16;      // 16-key blocks of the tile
     // S^T = K Q^T: lane holds keys 16kt + 4a + i of its row
-    f32x4 s[4];
+    f32x4 s[KT];
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
       const int k = 16 * kt + c16;
 #pragma unroll
@@ -284,7 +307,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // mask, online softmax (scores are already scaled to log2 units)
     float mt_max = -INFINITY;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
       if (masked) {
         const int k0 = 16 * kt + 4 * a;
         const int4 s4 = *reinterpret_cast<const int4*>(sl + k0);
@@ -300,14 +323,23 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
     mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
-    const float m_new = fmaxf(m_run, mt_max);
-    const float m_use = m_new == -INFINITY ? 0.f : m_new;
-    const float alpha = __builtin_amdgcn_exp2f(m_run - m_use);
-    l_run *= alpha;
+    // Lazy rescale: the reference m_run only moves (and O, l are rescaled)
+    // when some row of the wave sees a score more than 2^kLazy above it;
+    // otherwise the probabilities are taken against the old reference and
+    // may exceed 1 (by at most 2^kLazy), which the final division by l
+    // cancels exactly.
+    constexpr float kLazy = 8.f;
+    if (__builtin_amdgcn_ballot_w64(mt_max > m_run + kLazy) != 0) {
+      const float m_new = fmaxf(m_run, mt_max);
+      const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
+      l_run *= alpha;
 #pragma unroll
-    for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
+      m_run = m_new;
+    }
+    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
-    for (int kt = 0; kt < 4; ++kt) {
+    for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const float e = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
@@ -315,7 +347,6 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
         l_run += e;
       }
     }
-    m_run = m_new;
     // O^T += V^T P^T over two 32-key halves.  The B operand P^T of lane
     // (a, c16) holds keys 32kk + 4a + i and 32kk + 16 + 4a + i (i = 0..3,
     // straight from the S^T accumulators); the A operand V^T needs the same
@@ -323,7 +354,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     // deliver: source lane c16 addresses key 32kk + 4a + c16 / 4 (+16), dims
     // 16mt + 4 (c16 % 4) .. + 3.
 #pragma unroll
-    for (int kk = 0; kk < 2; ++kk) {
+    for (int kk = 0; kk < KT / 2; ++kk) {
       bf16x8 ph, pl;
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
@@ -347,28 +378,32 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2))) v
     }
   };
 
-  // Pipeline: tile t+1 streams into the other buffer while tile t is
-  // computed; slots run two tiles ahead.
+  // Pipeline: tiles t+1 .. t+kStages-1 stream into the ring while tile t is
+  // computed; slots run kStages tiles ahead.
   if (ntiles > 0) {
-    fill_slots(0);
-    if (ntiles > 1) fill_slots(1);
+    for (int u = 0; u < kStages && u < ntiles; ++u) fill_slots(u);
     __syncthreads();
-    issue(0);
+    for (int u = 0; u < kStages - 1 && u < ntiles; ++u) issue(u);
   }
   for (int t = 0; t < ntiles; ++t) {
     const int base = t * kTile;
-    __builtin_amdgcn_s_waitcnt(0);   // this wave's loads of tile t have landed
+    // this wave's loads of tile t have landed (later tiles may still fly)
+    const int later = min(kStages - 2, ntiles - 1 - t);
+    static_assert(kStages <= 4, "extend the waits below");
+    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
     __syncthreads();                 // ... and every wave's; tile t-1 is consumed
     __asm__ volatile("" ::: "memory");
-    if (t + 2 < ntiles) fill_slots(t + 2);
-    if (t + 1 < ntiles) issue(t + 1);
-    const int* sl = s_slots[t % 3];
+    if (t + kStages < ntiles) fill_slots(t + kStages);
+    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+    const int* sl = s_slots[t % kSlotRing];
     const bool masked = any_missing || base + kTile - 1 > q0;
     if (masked) {
-      zero_masked(sl, t & 1);
+      zero_masked(sl, t % kStages);
       __syncthreads();
     }
-    compute(s_kv[t & 1][0], s_kv[t & 1][1], base, sl, masked);
+    compute(s_kv[t % kStages][0], s_kv[t % kStages][1], base, sl, masked);
   }
 
   // normalise and write O[layer][r][qi][hq][d], d = 16mt + 4a + i
@@ -463,6 +498,7 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
   p.rows = b->q_len * group;
   p.bt_stride = b->bt_stride;
   p.block_size = block_size;
+  p.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(uint32_t(block_size)) : -1;
   p.max_position = d.max_position;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = d.head_dim == 64 ? launch_attend<64>(p, kc, vc, grid, d.rope_style, s)

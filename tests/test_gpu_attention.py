@@ -182,3 +182,17 @@ def test_attention_missing_block_is_masked_and_reported():
     dw, qb, got, layers = run_attention(w, 16, 32, mutate_bt=drop_last)
     assert int(dw.status.item()) == 4
     assert np.all(np.isfinite(got))
+
+
+@pytest.mark.parametrize("bs,prefix,lens,q_len,hq,D", [
+    (24, 40, [[7, 33, 12, 50]], 8, 8, 128),      # block size not a power of two
+    (12, 5, [[9, 3]], 4, 4, 64),                 # context shorter than one key tile
+    (16, 20, [[12]], 32, 2, 64),                 # context of exactly one 64-key span
+    (16, 17, [[30, 31], [5]], 5, 6, 128),        # 15 rows per KV head (group 3), ragged
+])
+def test_attention_edge_shapes(bs, prefix, lens, q_len, hq, D):
+    w = context_workload(f"attn_edge_{bs}_{D}_{q_len}", 2, 2, D, bs, prefix, lens, q_len,
+                         n_req=len(lens), seed=bs + D)
+    dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu")
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, q_len, hq, layers, "cpu")
