@@ -40,6 +40,10 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--no-permute", action="store_true",
+                    help="skip timing the same batch with every request's facts reordered")
+    ap.add_argument("--pool-requests", type=int, default=8,
+                    help="requests in the sample of the multi-core CPU-oracle baseline (0: skip)")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip timing the query-prefill attention over the injected cache")
     ap.add_argument("--no-retrieve", action="store_true",
@@ -296,6 +300,80 @@ def cpu_baseline(w, budget_s):
     }
 
 
+def _pool_worker(task):
+    """One worker of the multi-core oracle baseline: the oracle's inject for a
+    range of layers of every sampled request.  Returns (token-layers, seconds)."""
+    import numpy as np
+
+    from oracle import inject as oinject
+
+    folder, layers, reqs, spec_vals = task
+    block_size, num_kv_heads, head_dim, theta = spec_vals
+    done, spent = 0, 0.0
+    for r, (ids, prefix, bt, rows) in enumerate(reqs):
+        k_ar = np.load(os.path.join(folder, f"k{r}.npy"), mmap_mode="r")[layers[0]:layers[1]]
+        v_ar = np.load(os.path.join(folder, f"v{r}.npy"), mmap_mode="r")[layers[0]:layers[1]]
+        k_ar, v_ar = np.ascontiguousarray(k_ar), np.ascontiguousarray(v_ar)
+        nl = layers[1] - layers[0]
+        img_k = oinject.PagedImage(nl, bt, block_size, num_kv_heads, head_dim, 0x7F7F)
+        img_v = oinject.PagedImage(nl, bt, block_size, num_kv_heads, head_dim, 0x7F7F)
+        t0 = time.perf_counter()
+        n = oinject.inject(k_ar, v_ar, rows, [(ids, prefix, bt)], block_size, theta, img_k, img_v)
+        spent += time.perf_counter() - t0
+        done += n * nl
+    return done, spent
+
+
+def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
+    """The same oracle spread over the host's cores (a process pool, split by
+    layer, as the work is independent per layer) on the first n_requests
+    requests: tokens/s = sampled tokens / the slowest worker's compute time."""
+    import multiprocessing
+    import shutil
+    import tempfile
+
+    import numpy as np
+
+    sp = w.spec
+    cores = min(len(os.sched_getaffinity(0)), max_workers, sp.num_layers)
+    folder = tempfile.mkdtemp(prefix="prkv_pool_")
+    try:
+        reqs = []
+        n_tok = 0
+        for r, (ids, prefix, bt) in enumerate(w.requests()[:n_requests]):
+            rows, ks, vs, row = {}, [], [], 0
+            for f in sorted(set(ids)):
+                k, v = w.fact_kv(f, device=gen_device)
+                ks.append(k.cpu().numpy().view(np.uint16))
+                vs.append(v.cpu().numpy().view(np.uint16))
+                rows[f] = (row, w.length_of(f))
+                row += w.length_of(f)
+            np.save(os.path.join(folder, f"k{r}.npy"), np.concatenate(ks, 1))
+            np.save(os.path.join(folder, f"v{r}.npy"), np.concatenate(vs, 1))
+            reqs.append(([int(f) for f in ids], int(prefix), [int(b) for b in bt], rows))
+            n_tok += sum(w.length_of(f) for f in ids)
+        edges = np.linspace(0, sp.num_layers, cores + 1).round().astype(int)
+        vals = (sp.block_size, sp.num_kv_heads, sp.head_dim, sp.rope_theta)
+        tasks = [(folder, (int(edges[i]), int(edges[i + 1])), reqs, vals) for i in range(cores)]
+        # fresh interpreters (spawn): the workers never touch the GPU
+        with multiprocessing.get_context("spawn").Pool(cores) as pool:
+            res = pool.map(_pool_worker, tasks)
+    finally:
+        shutil.rmtree(folder, ignore_errors=True)
+    token_layers = sum(d for d, _ in res)
+    assert token_layers == n_tok * sp.num_layers
+    slowest = max(t for _, t in res)
+    return {
+        "value": n_tok / slowest,
+        "unit": "injected KV tokens/s",
+        "cores": cores,
+        "kind": "oracle",
+        "sample": (f"{n_tok} tokens of the first {len(reqs)} request(s), all {sp.num_layers} "
+                   f"layers split over {cores} worker processes; rotate + scatter only; "
+                   f"slowest worker {slowest:.1f} s, {sum(t for _, t in res):.1f} core-s in all"),
+    }
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -397,6 +475,32 @@ def main():
     # the dominant kernel alone (same kernel, mapping already resident)
     _, per_ms, kernel_ms = timed(step_kernel)
     assert int(dw.status.item()) == 0
+
+    perm = None
+    if not args.no_permute:
+        # the same facts of every request in another order: other positions
+        # and slots for the same token count (assembly order is free)
+        import numpy as np
+        rng = np.random.default_rng(2024)
+        req_ptr, ids, _, _, _ = w.csr()
+        pids = ids.copy()
+        for r in range(len(req_ptr) - 1):
+            pids[req_ptr[r]:req_ptr[r + 1]] = rng.permutation(ids[req_ptr[r]:req_ptr[r + 1]])
+        d_pids = torch.from_numpy(pids).to(dw.device)
+        pbatch = prkv.device_batch(len(req_ptr) - 1, dw.d_bt.shape[1], dw.max_facts,
+                                   dw.max_tokens, dw.d_req_ptr, d_pids, dw.d_start, dw.d_bt,
+                                   dw.d_bt_len)
+        pargs = list(dargs)
+        pargs[2] = ctypes.byref(pbatch)
+
+        def step_perm():
+            call(lib.inject_topk_device, pargs, "inject_topk_device")
+
+        _, _, p_ms = timed(step_perm)
+        assert int(dw.status.item()) == 0
+        perm = {"what": "the step with every request's facts in a shuffled order",
+                "ms": p_ms, "ratio_to_step": p_ms / step_ms}
+        step_device()   # facts back in drawn order
 
     n_tok = dw.n_tokens
     alg_bytes = n_tok * spec.bytes_per_token
@@ -506,9 +610,11 @@ def main():
         }
         del out, qt
 
-    cpu = None
+    cpu = cpu_pool = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
+        if args.pool_requests > 0:
+            cpu_pool = cpu_baseline_pool(w, args.pool_requests)
 
     out = {
         "metric": METRIC,
@@ -555,6 +661,8 @@ def main():
             "bytes_per_launch": alg_bytes // 2,
         }),
         "cpu_baseline": cpu,
+        "cpu_baseline_all_cores": cpu_pool,
+        "permuted_order": perm,
         "retrieval": retrieval,
         "attention": attn,
         "e2e": e2e,
