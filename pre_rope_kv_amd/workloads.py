@@ -93,6 +93,13 @@ SPECS = {
         length_dist=("uniform", 20, 60), k=50, prefix=("fixed", 64),
         block_size=16, num_blocks=131072, resident="retrieved",
         store_seed=3, request_seed=3),
+    # one tensor-parallel rank's share of the 64-request batch (1 of 8 KV heads)
+    "llama3_8b_batch64_k50_h1": Spec(
+        name="llama3_8b_batch64_k50_h1", num_layers=32, num_kv_heads=1, head_dim=128,
+        rope_theta=5.0e5, n_requests=64, facts_per_store=2000,
+        length_dist=("uniform", 20, 60), k=50, prefix=("fixed", 64),
+        block_size=16, num_blocks=131072, resident="retrieved",
+        store_seed=3, request_seed=3),
     "llama3_70b_batch16_k50": Spec(
         name="llama3_70b_batch16_k50", num_layers=80, num_kv_heads=8, head_dim=128,
         rope_theta=5.0e5, n_requests=16, facts_per_store=20000,

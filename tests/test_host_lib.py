@@ -342,3 +342,15 @@ def test_retrieve_argument_errors(kw, name):
 
 def test_retrieve_workspace_bytes():
     assert prkv.retrieve_workspace_bytes(64, 2000) == 64 * 2000 * 8
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    # no fallback: without libprkv.so every entry point raises
+    monkeypatch.setattr(prkv, "LIB_PATH", str(tmp_path / "libprkv.so"))
+    monkeypatch.setattr(prkv, "_lib", None)
+    with pytest.raises(ImportError, match="no fallback"):
+        prkv.lib()
+    with pytest.raises(ImportError):
+        prkv.store_required_bytes(_desc())
+    with pytest.raises(ImportError):
+        prkv.store_create(_desc())
