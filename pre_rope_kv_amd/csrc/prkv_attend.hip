@@ -123,7 +123,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // a ring of tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
   __shared__ __align__(1024) unsigned char s_kv[kStages][2][TILEB];
   __shared__ __align__(16) int s_slots[kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
-  __shared__ int s_bt[kBtLds];          // the request's block table (first kBtLds entries)
+  extern __shared__ int s_bt[];         // the request's block table: bt_stride entries
 
   const int g = blockIdx.x % p.num_kv_heads;
   const int r = (blockIdx.x / p.num_kv_heads) % p.n_req;
@@ -208,7 +208,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int64_t row_elems = int64_t(p.num_kv_heads) * D;
   const int ntiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
 
-  // (the host checks bt_stride <= kBtLds, so nb <= kBtLds)
+  // (nb <= bt_stride, the dynamic LDS size; the host checks bt_stride <= kBtLds)
   for (int i = threadIdx.x; i < nb; i += kThreads) s_bt[i] = btr[i];
   __syncthreads();
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
@@ -421,12 +421,15 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 template <int D>
 hipError_t launch_attend(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
                          int64_t grid, int style, hipStream_t s) {
+  // the block table is the dynamic LDS: a short table leaves room for more
+  // workgroups per CU
+  const size_t lds = size_t(p.bt_stride > 0 ? p.bt_stride : 1) * sizeof(int32_t);
   if (style == PRKV_ROPE_INTERLEAVED)
     hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_INTERLEAVED>), dim3(unsigned(grid)),
-                       dim3(kThreads), 0, s, p, kc, vc);
+                       dim3(kThreads), lds, s, p, kc, vc);
   else
     hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_HALF_SPLIT>), dim3(unsigned(grid)),
-                       dim3(kThreads), 0, s, p, kc, vc);
+                       dim3(kThreads), lds, s, p, kc, vc);
   return hipGetLastError();
 }
 
