@@ -310,9 +310,10 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
  * cache are bf16; q and the probabilities are carried as bf16 hi + lo pairs
  * into the matrix cores, so the result is accurate to fp32 rounding.
  * Limits: head_dim 64 or 128; q_len * (num_q_heads / H) <= 64; bt_stride
- * <= 2048 (the table is staged in LDS).  Positions
- * whose block is missing from the table are masked and set bit 4 of
- * d_status.  One kernel launch on `stream`, asynchronous. */
+ * <= 2048 (the table is staged in LDS).  Positions whose block is missing
+ * from the table are masked and set bit 4 of d_status; a request whose query
+ * positions do not lie in [0, max_position) sets bit 2 and gets output 0.
+ * One kernel launch on `stream`, asynchronous. */
 typedef struct prkv_attn_batch {
   int32_t n_req;
   int32_t q_len;               /* query tokens per request */

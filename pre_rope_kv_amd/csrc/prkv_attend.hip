@@ -134,9 +134,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const bool row_ok = row < p.rows;
   const int qi = row_ok ? row / p.group : 0;
   const int hq = g * p.group + (row_ok ? row % p.group : 0);
-  const int q0 = p.q_start[r];
+  // The query's positions must lie in [0, max_position); a request whose
+  // do not is reported (status bit 2) and attends to nothing (output 0).
+  const int q_first = p.q_start[r];
+  const bool req_ok = q_first >= 0 && q_first <= p.max_position - p.q_len;
+  if (!req_ok && threadIdx.x == 0 && p.status) atomicOr(p.status, 2);
+  const int q0 = req_ok ? q_first : 0;
   const int qpos = q0 + qi;
-  const int ctx = q0 + p.q_len;  // keys [0, ctx)
+  const int ctx = req_ok ? q0 + p.q_len : 0;  // keys [0, ctx)
 
   // 1. The lane's dims 32kb + 8a + e of its rotated query row, as hi + lo bf16.
   bf16x8 qh[KB], ql[KB];

@@ -102,7 +102,8 @@ def from_cache(dw, q_bits, q_len, layers):
     return out
 
 
-def run_attention(w, q_len, hq, gen="cuda", layers=None, seed=1, mutate_bt=None):
+def run_attention(w, q_len, hq, gen="cuda", layers=None, seed=1, mutate_bt=None,
+                  mutate_q_start=None):
     sp = w.spec
     dw = harness.DeviceWorkload(w, gen_device=gen)
     dw.inject()
@@ -118,6 +119,8 @@ def run_attention(w, q_len, hq, gen="cuda", layers=None, seed=1, mutate_bt=None)
     bt_len = torch.from_numpy(dw.bt_len).cuda()
     if mutate_bt is not None:
         mutate_bt(bt, bt_len)
+    if mutate_q_start is not None:
+        mutate_q_start(q_start)
     q = q_bits.cuda()
     out = torch.full((sp.num_layers, sp.n_requests, q_len, hq, sp.head_dim), float("nan"),
                      dtype=torch.float32, device="cuda")
@@ -196,3 +199,22 @@ def test_attention_edge_shapes(bs, prefix, lens, q_len, hq, D):
     dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu")
     assert int(dw.status.item()) == 0
     check(dw, qb, got, q_len, hq, layers, "cpu")
+
+
+def test_attention_query_positions_out_of_range_are_reported():
+    # request 0 starts past max_position - q_len, request 1 before 0: both are
+    # reported (bit 2) and produce 0; request 2 is unaffected
+    rng = np.random.default_rng(3)
+    lens = [rng.integers(5, 40, size=4) for _ in range(3)]
+    w = context_workload("attn_qpos", 2, 2, 128, 16, 20, lens, 8, n_req=3, seed=3)
+    _, qb0, ref, layers = run_attention(w, 8, 8, gen="cpu")
+    max_pos = w.spec.max_position
+
+    def bad_starts(q_start):
+        q_start[0] = max_pos - 8 + 1
+        q_start[1] = -1
+
+    dw, qb, got, _ = run_attention(w, 8, 8, gen="cpu", mutate_q_start=bad_starts)
+    assert int(dw.status.item()) == 2
+    assert np.all(got[:, :2] == 0)
+    assert np.array_equal(got[:, 2], ref[:, 2])
