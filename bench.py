@@ -40,6 +40,9 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--graph", action="store_true",
+                    help="also time the step replayed from a captured HIP graph (launch-bound "
+                         "small batches)")
     ap.add_argument("--no-permute", action="store_true",
                     help="skip timing the same batch with every request's facts reordered")
     ap.add_argument("--pool-requests", type=int, default=8,
@@ -476,6 +479,24 @@ def main():
     _, per_ms, kernel_ms = timed(step_kernel)
     assert int(dw.status.item()) == 0
 
+    graph = None
+    if args.graph:
+        # the step captured once and replayed: kernels only, no host work
+        side = torch.cuda.Stream()
+        side.wait_stream(stream)
+        torch.cuda.synchronize()
+        gargs = list(dargs)
+        gargs[-1] = side.cuda_stream
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=side):
+            call(lib.inject_topk_device, gargs, "inject_topk_device")
+        torch.cuda.synchronize()
+        _, g_per, g_ms = timed(g.replay)
+        assert int(dw.status.item()) == 0
+        graph = {"what": "inject_topk_device captured in a HIP graph, replayed",
+                 "ms": g_ms, "median_ms": g_per[len(g_per) // 2],
+                 "tokens_per_s": dw.n_tokens / (g_ms * 1e-3)}
+
     perm = None
     if not args.no_permute:
         # the same facts of every request in another order: other positions
@@ -663,6 +684,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "permuted_order": perm,
+        "graph_replay": graph,
         "retrieval": retrieval,
         "attention": attn,
         "e2e": e2e,
