@@ -80,7 +80,8 @@ struct InjectParams {
   int32_t num_layers;
   int32_t num_heads;
   int32_t n_splits;          // workgroups per tile
-  int32_t iters_per_split;   // 64-chunk iterations per split
+  int32_t iters_per_split;   // 64-chunk iterations (layers when tpw > 1) per split
+  int32_t tpw;               // tokens per wave: 64 / (H * D/16) when that divides 64, else 1
 };
 
 // Half-split pairing: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
@@ -122,14 +123,15 @@ __device__ __forceinline__ int pair_slot(int j) {
   return (4 * hi + (jj & 3)) * CPH + (jj >> 2);
 }
 
-template <int D, int STYLE>
+template <int D, int STYLE, bool MULTI>
 __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerPtrs kc,
                                                           LayerPtrs vc) {
   constexpr int CPH = D / 16;   // 16-byte chunks per half head
   constexpr int HALF = D / 2;   // pairs per head
   extern __shared__ f32x4 smem[];
 
-  constexpr int tile_tokens = kWavesPerGroup;   // one token per wave
+  const int tpw = MULTI ? p.tpw : 1;
+  const int tile_tokens = kWavesPerGroup * tpw;
   int64_t n_tokens = p.n_tokens;
   if (p.n_tokens_dev) {
     const int64_t dev = *p.n_tokens_dev;
@@ -148,7 +150,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   const int total = p.num_layers * nc;    // chunks per token
   const int it0 = split * p.iters_per_split;
   int it1 = it0 + p.iters_per_split;
-  const int max_it = (total + kWave - 1) / kWave;
+  const int max_it = tpw > 1 ? p.num_layers : (total + kWave - 1) / kWave;
   if (it1 > max_it) it1 = max_it;
   const int64_t row_elems = int64_t(H) * D;
   const int64_t layer_elems = p.capacity_rows * row_elems;
@@ -191,7 +193,52 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     }
     __syncthreads();
 
-    // 3. Each wave streams its token through every layer of its split.
+    // 3a. Rows narrower than a wave (H * D/16 < 64 chunks): the wave covers
+    //     tpw consecutive tokens of the tile, one layer per iteration, so its
+    //     loads and stores cover whole consecutive rows.
+    if constexpr (MULTI) {
+      const int j = wave * tpw + lane / nc;     // the lane's token in the tile
+      const int h = (lane % nc) / CPH;
+      const int row = meta[3 * j + 0];
+      const int slot = meta[3 * j + 2];
+      f32x4 cs[8];
+#pragma unroll
+      for (int k = 0; k < 8; ++k) cs[k] = smem[j * HALF + k * CPH + c];
+      const int64_t in_row = int64_t(h) * D + c * 8;
+      const int64_t a0 = int64_t(row) * row_elems + in_row;
+      const int64_t s0 = int64_t(slot) * row_elems + in_row;
+      if (row >= 0) {
+        for (int l0 = it0; l0 < it1; l0 += kUnroll) {
+          u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            if (l0 + u < it1) {
+              const int64_t aoff = int64_t(l0 + u) * layer_elems + a0;
+              ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_arena + aoff));
+              kb[u] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4*>(p.k_arena + aoff + HALF));
+              va[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v_arena + aoff));
+              vb[u] = __builtin_nontemporal_load(
+                  reinterpret_cast<const u32x4*>(p.v_arena + aoff + HALF));
+            }
+          }
+#pragma unroll
+          for (int u = 0; u < kUnroll; ++u) {
+            if (l0 + u >= it1) continue;
+            if (STYLE == PRKV_ROPE_HALF_SPLIT) rotate8(ka[u], kb[u], cs);
+            else rotate8_interleaved(ka[u], kb[u], cs);
+            uint16_t* kd = kc.p[l0 + u] + s0;
+            uint16_t* vd = vc.p[l0 + u] + s0;
+            __builtin_nontemporal_store(ka[u], reinterpret_cast<u32x4*>(kd));
+            __builtin_nontemporal_store(kb[u], reinterpret_cast<u32x4*>(kd + HALF));
+            __builtin_nontemporal_store(va[u], reinterpret_cast<u32x4*>(vd));
+            __builtin_nontemporal_store(vb[u], reinterpret_cast<u32x4*>(vd + HALF));
+          }
+        }
+      }
+    } else {
+    // 3b. Otherwise each wave streams its one token through every layer of
+    //     its split.
     const int row = __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
     if (row >= 0) {
       const int slot = __builtin_amdgcn_readfirstlane(meta[3 * wave + 2]);
@@ -239,6 +286,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
         }
       }
     }
+    }  // MULTI
   }
 }
 
@@ -416,12 +464,22 @@ int compute_units() {
 template <int D>
 hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
                   int64_t grid, size_t lds, int style, hipStream_t s) {
-  if (style == PRKV_ROPE_INTERLEAVED)
-    hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED>), dim3(unsigned(grid)),
-                       dim3(kThreads), lds, s, p, kc, vc);
-  else
-    hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT>), dim3(unsigned(grid)),
-                       dim3(kThreads), lds, s, p, kc, vc);
+  const bool multi = p.tpw > 1;
+  if (style == PRKV_ROPE_INTERLEAVED) {
+    if (multi)
+      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED, true>), dim3(unsigned(grid)),
+                         dim3(kThreads), lds, s, p, kc, vc);
+    else
+      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED, false>), dim3(unsigned(grid)),
+                         dim3(kThreads), lds, s, p, kc, vc);
+  } else {
+    if (multi)
+      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT, true>), dim3(unsigned(grid)),
+                         dim3(kThreads), lds, s, p, kc, vc);
+    else
+      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT, false>), dim3(unsigned(grid)),
+                         dim3(kThreads), lds, s, p, kc, vc);
+  }
   return hipGetLastError();
 }
 
@@ -473,13 +531,16 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
     kc.p[l] = static_cast<uint16_t*>(k_cache_layers[l]);
     vc.p[l] = static_cast<uint16_t*>(v_cache_layers[l]);
   }
-  // Launch shape: tiles of 4 tokens; split each token's chunk range across
-  // workgroups until the grid holds enough waves to cover the chip.
+  // Launch shape: tiles of 4 waves x tpw tokens; split each token's work
+  // across workgroups until the grid holds enough waves to cover the chip.
   const int D = d.head_dim;
-  const int64_t chunks = int64_t(d.num_layers) * d.num_kv_heads * (D / 16);
-  const int iters = int((chunks + kWave - 1) / kWave);
+  const int nc = d.num_kv_heads * (D / 16);   // 16-byte chunk pairs per (token, layer)
+  const int tpw = (nc < kWave && kWave % nc == 0) ? kWave / nc : 1;
+  const int64_t chunks = int64_t(d.num_layers) * nc;
+  const int iters = tpw > 1 ? d.num_layers : int((chunks + kWave - 1) / kWave);
   const int64_t want_waves = int64_t(compute_units()) * 16;
-  const int64_t tiles = (n_tokens + kWavesPerGroup - 1) / kWavesPerGroup;
+  const int64_t tile_tokens = int64_t(kWavesPerGroup) * tpw;
+  const int64_t tiles = (n_tokens + tile_tokens - 1) / tile_tokens;
   int n_splits = 1;
   while (n_splits < iters && tiles * n_splits * kWavesPerGroup < want_waves) n_splits *= 2;
   if (n_splits > iters) n_splits = iters;
@@ -490,7 +551,7 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
                                                                     : (int64_t(1) << 20) / n_splits;
   const int64_t grid = grid_tiles * n_splits;
-  const size_t lds = size_t(kWavesPerGroup) * (size_t(D / 2) * 16 + 12);
+  const size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
 
   InjectParams p;
   p.k_arena = static_cast<const uint16_t*>(st->k_arena);
@@ -509,6 +570,7 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   p.num_heads = d.num_kv_heads;
   p.n_splits = n_splits;
   p.iters_per_split = per;
+  p.tpw = tpw;
 
   hipError_t e;
   switch (D) {
