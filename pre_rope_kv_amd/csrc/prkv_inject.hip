@@ -29,6 +29,11 @@
 //    since 64 is a multiple of D/16, a lane's c is fixed (lane % (D/16)) and
 //    its 8 (cos, sin) pairs are loaded once per token and kept in VGPRs for
 //    every layer.
+//  - When a (token, layer) row has fewer than 64 chunks (H * D/16 < 64 and
+//    dividing it), a wave instead covers 64 / (H * D/16) consecutive tokens
+//    of one layer per iteration (a tile is then 4 waves x that many tokens),
+//    so every load and store instruction still spans whole consecutive rows
+//    (a separate instantiation, MULTI).
 //  - Token metadata for the tile is gathered with one coalesced load per
 //    lane; each token's cos/sin row (read once per (position, pair) per tile)
 //    is staged in LDS, laid out so lanes with consecutive c read consecutive
