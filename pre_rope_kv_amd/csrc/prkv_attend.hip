@@ -125,9 +125,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   __shared__ __align__(16) int s_slots[kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
   extern __shared__ int s_bt[];         // the request's block table: bt_stride entries
 
-  const int g = blockIdx.x % p.num_kv_heads;
-  const int r = (blockIdx.x / p.num_kv_heads) % p.n_req;
-  const int layer = blockIdx.x / (p.num_kv_heads * p.n_req);
+  // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so
+  // logical id (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous run
+  // of (layer, request, head) work: the heads of one cache row share an L2.
+  const int nwg = gridDim.x;
+  const int bid = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int g = bid % p.num_kv_heads;
+  const int r = (bid / p.num_kv_heads) % p.n_req;
+  const int layer = bid / (p.num_kv_heads * p.n_req);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int a = lane / 16, c16 = lane % 16;
   const int row = wave * 16 + c16;
@@ -143,6 +148,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int qpos = q0 + qi;
   const int ctx = req_ok ? q0 + p.q_len : 0;  // keys [0, ctx)
 
+  // The first kThreads block-table entries are loaded now, so that their
+  // latency overlaps the query's (the host checks bt_stride >= 1).
+  const int32_t* btr = p.bt + int64_t(r) * p.bt_stride;
+  const int bt_first = btr[min(int(threadIdx.x), p.bt_stride - 1)];
+  const int nb = min(p.bt_len[r], p.bt_stride);
+
   // 1. The lane's dims 32kb + 8a + e of its rotated query row, as hi + lo bf16.
   bf16x8 qh[KB], ql[KB];
   {
@@ -157,18 +168,33 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
         x[kb][2 * d + 1] = hi_bf16(w[d]);
       }
     }
+    // The lane's D/4 (cos, sin) entries, loaded unconditionally (the row
+    // index is clamped into the table) so all loads are in flight together;
+    // an out-of-range position rotates by the identity.
     const bool pos_ok = qpos >= 0 && qpos < p.max_position;
     const f32x4* rrow = p.rope + int64_t(pos_ok ? qpos : 0) * (D / 2);
+    constexpr int NCS = D / 4;
+    f32x4 cs[NCS];
+#pragma unroll
+    for (int n = 0; n < NCS; ++n) {
+      // half split: n = 8kb + e -> pair 32kb + 8a + e; interleaved: n = 4kb + m
+      // -> pair 16kb + 4a + m
+      const int j = STYLE == PRKV_ROPE_HALF_SPLIT ? 32 * (n / 8) + 8 * a + n % 8
+                                                  : 16 * (n / 4) + 4 * a + n % 4;
+      cs[n] = rrow[j];
+    }
+#pragma unroll
+    for (int n = 0; n < NCS; ++n) cs[n] = pos_ok ? cs[n] : f32x4{1.f, 0.f, 0.f, 0.f};
     if (STYLE == PRKV_ROPE_HALF_SPLIT) {
 #pragma unroll
       for (int kb = 0; kb < KB / 2; ++kb) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
-          const int j = 32 * kb + 8 * a + e;  // pairs with j + D/2 (k-block kb + KB/2)
-          const f32x4 cs = pos_ok ? rrow[j] : f32x4{1.f, 0.f, 0.f, 0.f};
+          // pair 32kb + 8a + e: elements of k-blocks kb and kb + KB/2
+          const f32x4 c = cs[8 * kb + e];
           const float x1 = x[kb][e], x2 = x[kb + KB / 2][e];
-          x[kb][e] = rot_first(x1, x2, cs);
-          x[kb + KB / 2][e] = rot_second(x1, x2, cs);
+          x[kb][e] = rot_first(x1, x2, c);
+          x[kb + KB / 2][e] = rot_second(x1, x2, c);
         }
       }
     } else {
@@ -176,11 +202,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       for (int kb = 0; kb < KB; ++kb) {
 #pragma unroll
         for (int m = 0; m < 4; ++m) {
-          const int j = 16 * kb + 4 * a + m;  // dims 2j, 2j + 1 = e 2m, 2m + 1
-          const f32x4 cs = pos_ok ? rrow[j] : f32x4{1.f, 0.f, 0.f, 0.f};
+          // pair 16kb + 4a + m: dims 2j, 2j + 1 = e 2m, 2m + 1 of k-block kb
+          const f32x4 c = cs[4 * kb + m];
           const float x1 = x[kb][2 * m], x2 = x[kb][2 * m + 1];
-          x[kb][2 * m] = rot_first(x1, x2, cs);
-          x[kb][2 * m + 1] = rot_second(x1, x2, cs);
+          x[kb][2 * m] = rot_first(x1, x2, c);
+          x[kb][2 * m + 1] = rot_second(x1, x2, c);
         }
       }
     }
@@ -206,15 +232,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
   float m_run = -INFINITY, l_run = 0.f;
 
-  const int32_t* btr = p.bt + int64_t(r) * p.bt_stride;
-  const int nb = min(p.bt_len[r], p.bt_stride);
   const uint16_t* kl = kc.p[layer];
   const uint16_t* vl = vc.p[layer];
   const int64_t row_elems = int64_t(p.num_kv_heads) * D;
   const int ntiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
 
   // (nb <= bt_stride, the dynamic LDS size; the host checks bt_stride <= kBtLds)
-  for (int i = threadIdx.x; i < nb; i += kThreads) s_bt[i] = btr[i];
+  if (int(threadIdx.x) < nb) s_bt[threadIdx.x] = bt_first;
+  for (int i = threadIdx.x + kThreads; i < nb; i += kThreads) s_bt[i] = btr[i];
   __syncthreads();
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
   auto slot_of = [&](int pos) -> int {
@@ -454,6 +479,8 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
                       d.head_dim);
   if (b->n_req < 0 || b->q_len < 0 || b->num_q_heads < 1 || b->bt_stride < 0)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "bad batch sizes");
+  if (b->n_req > 0 && b->q_len > 0 && b->bt_stride < 1)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "bt_stride must be >= 1");
   if (b->bt_stride > kBtLds)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "bt_stride %d exceeds %d block-table entries",
                       b->bt_stride, kBtLds);
