@@ -288,10 +288,10 @@ def build_slot_mapping(st, req_fact_ptr, fact_ids, start_pos, block_tables, bt_l
 def inject_topk(st, n_tokens, d_src_row, d_pos, d_slot, k_cache_layers, v_cache_layers,
                 block_size, num_blocks, d_status=None, stream=None):
     L = len(k_cache_layers)
-    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
-    vp = (_vp * len(v_cache_layers))(*[_ptr(t) for t in v_cache_layers])
     if len(v_cache_layers) != L or L != st.desc.num_layers:
         raise ValueError("need one K and one V cache pointer per layer")
+    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
+    vp = (_vp * L)(*[_ptr(t) for t in v_cache_layers])
     _check(lib().inject_topk(st.handle, int(n_tokens), _ptr(d_src_row), _ptr(d_pos),
                              _ptr(d_slot), kp, vp, int(block_size), int(num_blocks),
                              _ptr(d_status), _stream(stream)), "inject_topk")
@@ -334,6 +334,8 @@ def workspace_layout(max_facts, max_tokens):
 
 def device_batch(n_req, bt_stride, max_facts, max_tokens, req_fact_ptr, fact_ids, start_pos,
                  block_tables, bt_len):
+    """prkv_device_batch over device tensors; it holds raw pointers only, so
+    the caller keeps the tensors alive while the batch is in use."""
     return DeviceBatch(int(n_req), int(bt_stride), int(max_facts), 0, int(max_tokens),
                        _ptr(req_fact_ptr), _ptr(fact_ids), _ptr(start_pos),
                        _ptr(block_tables), _ptr(bt_len))
@@ -370,6 +372,7 @@ def retrieve_topk(d_fact_emb, n_stores, facts_per_store, dim, d_query_emb, d_req
 
 
 def attn_batch(n_req, q_len, num_q_heads, bt_stride, q, q_start, block_tables, bt_len, out):
+    """prkv_attn_batch over device tensors (raw pointers: keep the tensors alive)."""
     return AttnBatch(int(n_req), int(q_len), int(num_q_heads), int(bt_stride), _ptr(q),
                      _ptr(q_start), _ptr(block_tables), _ptr(bt_len), _ptr(out))
 
