@@ -297,7 +297,8 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
   if (total > capacity)
     return fail(PRKV_ERR_BUFFER_TOO_SMALL, "%lld tokens, capacity %lld", (long long)total,
                 (long long)capacity);
-  if (total > 0 && (!src_row || !pos || !slot))
+  if (total == 0) return PRKV_OK;  // nothing to copy; the outputs may be NULL
+  if (!src_row || !pos || !slot)
     return fail(PRKV_ERR_INVALID_ARG, "output arrays must not be NULL");
   std::memcpy(src_row, s_row.data(), size_t(total) * 4);
   std::memcpy(pos, s_pos.data(), size_t(total) * 4);
