@@ -21,7 +21,8 @@
 // topk_kernel: one 1024-lane workgroup per request.  Each wave streams
 // 64-score chunks, sorts a chunk with an in-register bitonic network and
 // merges it into its running top-64 (elementwise best of the list and the
-// reversed chunk, then a bitonic merge); the 16 wave lists are merged in LDS.
+// reversed chunk, then a bitonic merge); the 16 wave lists are merged in LDS
+// as a tree (4 rounds).
 // Order: higher score first, then smaller fact id, so ties are deterministic.
 
 #include <hip/hip_runtime.h>
@@ -194,12 +195,21 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   s_key[threadIdx.x] = best.key;
   s_id[threadIdx.x] = best.id;
   __syncthreads();
-  if (wave == 0) {
-    Cand acc = {s_key[lane], s_id[lane]};
-    for (int w = 1; w < nw; ++w) {
-      const Cand other = {s_key[w * kWave + lane], s_id[w * kWave + lane]};
-      acc = merge64(acc, other, lane);
+  // tree merge of the wave lists: in each round wave w < half merges in the
+  // list of wave w + half (it writes only its own slots, which no wave reads
+  // in that round)
+  for (int half = nw / 2; half >= 1; half /= 2) {
+    if (wave < half) {
+      const Cand mine = {s_key[threadIdx.x], s_id[threadIdx.x]};
+      const Cand other = {s_key[(wave + half) * kWave + lane], s_id[(wave + half) * kWave + lane]};
+      const Cand m = merge64(mine, other, lane);
+      s_key[threadIdx.x] = m.key;
+      s_id[threadIdx.x] = m.id;
     }
+    __syncthreads();
+  }
+  if (wave == 0) {
+    const Cand acc = {s_key[lane], s_id[lane]};
     if (lane < p.k) {
       const int64_t o = int64_t(r) * p.k + lane;
       const bool real = ok && acc.id != INT32_MAX;
