@@ -40,6 +40,9 @@ def parse():
                     help="wall-clock budget of the CPU-oracle baseline sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-e2e", action="store_true")
+    ap.add_argument("--k-sweep", action="store_true",
+                    help="instead of the batch: one request on the 2,000-fact Llama-3-8B store, "
+                         "the device step timed for its first k = 5, 10, 20, 50 facts")
     ap.add_argument("--graph", action="store_true",
                     help="also time the step replayed from a captured HIP graph (launch-bound "
                          "small batches)")
@@ -377,6 +380,55 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
     }
 
 
+def k_sweep(args):
+    """The retrieval-budget sweep of the pages (k = 5 .. 50) on one request:
+    the device step (mapping + inject) for the first k facts of one drawn
+    request of the 2,000-fact store, each k timed over args.steps launches."""
+    import torch
+
+    from pre_rope_kv_amd import harness, prkv, workloads
+
+    lib = prkv.lib()
+    torch.cuda.set_device(0)
+    w = workloads.make("llama3_8b_k50")
+    dw = harness.DeviceWorkload(w)
+    dw.setup_device_batch()
+    stream = dw.stream
+    rows = []
+    for k in (5, 10, 20, 50):
+        ptr = torch.tensor([0, k], dtype=torch.int32, device=dw.device)
+        batch = prkv.device_batch(1, dw.d_bt.shape[1], k, dw.max_tokens, ptr, dw.d_ids,
+                                  dw.d_start, dw.d_bt, dw.d_bt_len)
+        a = list(dw.inject_device_args())
+        a[2] = ctypes.byref(batch)
+
+        def step():
+            rc = lib.inject_topk_device(*a)
+            if rc != 0:
+                raise prkv.PrkvError(rc, "inject_topk_device", lib.last_error_string().decode())
+
+        for _ in range(args.warmup):
+            step()
+        torch.cuda.synchronize()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        for _ in range(args.steps):
+            step()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ms = e0.elapsed_time(e1) / args.steps
+        assert int(dw.status.item()) == 0
+        n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
+        rows.append({"k": k, "tokens": n_tok, "step_ms": ms,
+                     "tokens_per_s": n_tok / (ms * 1e-3),
+                     "hbm_gbps": n_tok * w.spec.bytes_per_token / (ms * 1e-3) / 1e9})
+    print(json.dumps({"metric": "device step time vs retrieval budget k, 1 request, 1 MI355X",
+                      "unit": "ms", "higher_is_better": False, "n_gpus": 1,
+                      "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
+                      "data": "synthetic", "config": {"workload": "llama3_8b_k50 (first k facts)"},
+                      "sweep": rows}), flush=True)
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -397,6 +449,9 @@ def main():
         summarize_profile(args.workload, trace_dir, fetch_dir, write_dir, cmds)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.k_sweep and args.gpus == 1 and world == 1:
+        k_sweep(args)
+        return
     if args.gpus != 1 or world != 1:
         print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the inject path needs no collective and shards by "
