@@ -299,11 +299,24 @@ def cpu_baseline(w, budget_s):
         "value": done_tokens / elapsed,
         "unit": "injected KV tokens/s",
         "cores": 1,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{done_tokens} tokens ({done_facts} facts of the first {r_used} "
                    f"request(s)), all {sp.num_layers} layers, rotate + scatter only, "
                    f"{elapsed:.1f} s on 1 host core (NumPy float64, single-threaded)"),
     }
+
+
+def cpu_model():
+    """The host CPU's model name from /proc/cpuinfo (None if unreadable)."""
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for line in fh:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def _pool_worker(task):
@@ -373,6 +386,7 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
         "value": n_tok / slowest,
         "unit": "injected KV tokens/s",
         "cores": cores,
+        "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{n_tok} tokens of the first {len(reqs)} request(s), all {sp.num_layers} "
                    f"layers split over {cores} worker processes; rotate + scatter only; "
