@@ -364,6 +364,8 @@ EDGE = [
     ("h8_d64", 3, 8, 64, 16, {0: 20, 1: 3}, [([1, 0], 7)]),
     ("h4_d256", 2, 4, 256, 16, {0: 11, 1: 30}, [([0, 1], 1)]),
     ("h1_d16", 5, 1, 16, 8, {0: 11, 1: 30}, [([0, 1], 1)]),
+    ("h1_d512", 2, 1, 512, 16, {0: 11, 1: 30}, [([0, 1], 1)]),   # two tokens per wave
+    ("h2_d1024", 2, 2, 1024, 16, {0: 11, 1: 19}, [([1, 0], 5)]),  # two chunk rounds per layer
     ("h3_d128", 2, 3, 128, 16, {0: 11, 1: 30}, [([1, 0], 2)]),
     ("h16_d128", 2, 16, 128, 16, {0: 11, 1: 6}, [([1, 0], 2)]),
     ("many_layers_80", 80, 8, 128, 16, {0: 6, 1: 9}, [([1, 0], 40)]),
