@@ -397,7 +397,9 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
 def k_sweep(args):
     """The retrieval-budget sweep of the pages (k = 5 .. 50) on one request:
     the device step (mapping + inject) for the first k facts of one drawn
-    request of the 2,000-fact store, each k timed over args.steps launches."""
+    request of the 2,000-fact store, each k timed over args.steps launches,
+    with the fused mapping (one launch) and with the separate plan and mapping
+    kernels (forced by a max_facts bound above the fused limit)."""
     import torch
 
     from pre_rope_kv_amd import harness, prkv, workloads
@@ -409,12 +411,17 @@ def k_sweep(args):
     dw.setup_device_batch()
     stream = dw.stream
     rows = []
-    for k in (5, 10, 20, 50):
+    ptr_cap = 257        # a max_facts bound above the fused mapping's limit (256)
+    big_ws = torch.zeros(prkv.inject_device_workspace_bytes(ptr_cap, dw.max_tokens),
+                         dtype=torch.uint8, device=dw.device)
+
+    def time_step(k, max_facts, workspace):
         ptr = torch.tensor([0, k], dtype=torch.int32, device=dw.device)
-        batch = prkv.device_batch(1, dw.d_bt.shape[1], k, dw.max_tokens, ptr, dw.d_ids,
+        batch = prkv.device_batch(1, dw.d_bt.shape[1], max_facts, dw.max_tokens, ptr, dw.d_ids,
                                   dw.d_start, dw.d_bt, dw.d_bt_len)
         a = list(dw.inject_device_args())
         a[2] = ctypes.byref(batch)
+        a[7], a[8] = workspace.data_ptr(), workspace.numel()
 
         def step():
             rc = lib.inject_topk_device(*a)
@@ -430,12 +437,17 @@ def k_sweep(args):
             step()
         e1.record(stream)
         torch.cuda.synchronize()
-        ms = e0.elapsed_time(e1) / args.steps
         assert int(dw.status.item()) == 0
+        return e0.elapsed_time(e1) / args.steps
+
+    for k in (5, 10, 20, 50):
+        ms = time_step(k, k, dw.workspace)              # fused mapping: one launch
+        ms3 = time_step(k, ptr_cap, big_ws)             # plan + mapping + inject kernels
         n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
         rows.append({"k": k, "tokens": n_tok, "step_ms": ms,
                      "tokens_per_s": n_tok / (ms * 1e-3),
-                     "hbm_gbps": n_tok * w.spec.bytes_per_token / (ms * 1e-3) / 1e9})
+                     "hbm_gbps": n_tok * w.spec.bytes_per_token / (ms * 1e-3) / 1e9,
+                     "step_ms_three_kernels": ms3})
     print(json.dumps({"metric": "device step time vs retrieval budget k, 1 request, 1 MI355X",
                       "unit": "ms", "higher_is_better": False, "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "dtype": "f32",

@@ -49,6 +49,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <atomic>
 #include <cstdint>
 #include <vector>
@@ -69,6 +70,35 @@ struct LayerPtrs {
   uint16_t* p[prkv::kMaxLayers];
 };
 
+struct FactPlan {
+  int32_t tok_start, row0, len, pad;
+};
+
+struct DeviceBatch {
+  const int32_t* req_fact_ptr;
+  const int32_t* fact_ids;
+  const int32_t* start_pos;
+  const int32_t* block_tables;
+  const int32_t* bt_len;
+  const int2* fact_table;      // [store max_facts] (first row or -1, length)
+  FactPlan* plan;              // workspace
+  int64_t* n_tokens_out;       // workspace header
+  int32_t* n_facts_out;        // workspace header
+  int32_t* src_row;            // workspace, [max_tokens]
+  int32_t* pos;
+  int32_t* slot;
+  int32_t* status;
+  int64_t max_tokens;
+  int64_t num_blocks;
+  int32_t n_req;
+  int32_t bt_stride;
+  int32_t max_facts_batch;
+  int32_t store_max_facts;
+  int32_t block_size;
+  int32_t max_position;
+  int32_t chunk_local;         // rotation position = the fact's first position
+};
+
 struct InjectParams {
   const uint16_t* k_arena;
   const uint16_t* v_arena;
@@ -87,6 +117,7 @@ struct InjectParams {
   int32_t n_splits;          // workgroups per tile
   int32_t iters_per_split;   // 64-chunk iterations (layers when tpw > 1) per split
   int32_t tpw;               // tokens per wave: 64 / (H * D/16) when that divides 64, else 1
+  int32_t want_waves;        // waves that cover the chip
 };
 
 // Half-split pairing: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
@@ -128,24 +159,168 @@ __device__ __forceinline__ int pair_slot(int j) {
   return (4 * hi + (jj & 3)) * CPH + (jj >> 2);
 }
 
-template <int D, int STYLE, bool MULTI>
+__device__ __forceinline__ void flag(int32_t* status, int bits) {
+  if (status) atomicOr(status, bits);
+}
+
+// ---------------------------------------------------------------------------
+// Fused mapping for small batches (at most kFuseFacts facts and kFuseReqs
+// requests): every workgroup of the inject kernel rebuilds the batch plan in
+// LDS (one fact per thread) and maps its own tile's tokens, so the whole
+// device-side step is one launch instead of plan + mapping + inject.  The
+// plan, the per-token mapping and every status bit are exactly those of
+// plan_kernel and materialize_kernel below; workgroup 0 writes the plan and
+// the header to the workspace, and the workgroup with split 0 of each tile
+// writes that tile's mapping.
+// ---------------------------------------------------------------------------
+
+constexpr int kFuseFacts = kThreads;
+constexpr int kFuseReqs = kThreads;
+
+struct FusedLds {
+  int64_t pos0[kFuseFacts];      // serving position of the fact's first token
+  int32_t tok[kFuseFacts];       // first token of the fact (clamped to max_tokens)
+  int32_t row0[kFuseFacts];
+  int32_t req[kFuseFacts];
+  int32_t reqptr[kFuseReqs + 1];
+  int32_t n_facts;
+  int64_t wsum[kWavesPerGroup];
+};
+
+// Builds the plan in LDS; returns the batch's token count.
+__device__ int64_t fused_plan(const DeviceBatch& b, FusedLds& s) {
+  const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
+  const bool lead = blockIdx.x == 0;
+  for (int i = tid; i <= b.n_req; i += kThreads) s.reqptr[i] = b.req_fact_ptr[i];
+  __syncthreads();
+  int n_facts = s.reqptr[b.n_req];
+  if (n_facts < 0 || n_facts > b.max_facts_batch) {
+    if (lead && tid == 0) flag(b.status, 32);
+    n_facts = n_facts < 0 ? 0 : b.max_facts_batch;
+  }
+  int len = 0, row0 = -1;
+  if (tid < n_facts) {
+    const int f = b.fact_ids[tid];
+    if (f >= 0 && f < b.store_max_facts) {
+      const int2 e = b.fact_table[f];
+      if (e.x >= 0 && e.y > 0) {
+        row0 = e.x;
+        len = e.y;
+      }
+    }
+    if (len == 0 && lead) flag(b.status, 8);
+  }
+  int64_t x = len;  // inclusive scan within the wave, then across the 4 waves
+#pragma unroll
+  for (int d = 1; d < kWave; d <<= 1) {
+    const int64_t y = __shfl_up(x, d, kWave);
+    if (lane >= d) x += y;
+  }
+  if (lane == kWave - 1) s.wsum[wave] = x;
+  __syncthreads();
+  int64_t before = 0, total = 0;
+#pragma unroll
+  for (int w = 0; w < kWavesPerGroup; ++w) {
+    before += w < wave ? s.wsum[w] : 0;
+    total += s.wsum[w];
+  }
+  const int64_t excl = before + x - len;
+  const int32_t tok = int32_t(excl < b.max_tokens ? excl : b.max_tokens);
+  if (tid < n_facts) {
+    s.tok[tid] = tok;
+    s.row0[tid] = row0;
+  }
+  if (tid == 0) s.n_facts = n_facts;
+  __syncthreads();
+  if (tid < n_facts) {
+    int lo = 0, hi = b.n_req - 1;  // the last request r with reqptr[r] <= tid
+    while (lo < hi) {
+      const int mid = (lo + hi + 1) / 2;
+      if (s.reqptr[mid] <= tid) lo = mid; else hi = mid - 1;
+    }
+    int first = s.reqptr[lo];
+    if (first < 0 || first > tid) first = tid;
+    s.req[tid] = lo;
+    s.pos0[tid] = int64_t(b.start_pos[lo]) + (tok - s.tok[first]);
+    if (lead) {
+      FactPlan pl;
+      pl.tok_start = tok;
+      pl.row0 = row0;
+      pl.len = len;
+      pl.pad = 0;
+      b.plan[tid] = pl;
+    }
+  }
+  const int64_t n_tokens = total < b.max_tokens ? total : b.max_tokens;
+  if (lead && tid == 0) {
+    if (total > b.max_tokens) flag(b.status, 16);
+    *b.n_tokens_out = n_tokens;
+    *b.n_facts_out = n_facts;
+  }
+  __syncthreads();
+  return n_tokens;
+}
+
+// (arena row, rotation position, slot) of token t < n_tokens, validated as
+// materialize_kernel does; a token that fails gets row -1.  `report`: set
+// the status bits and write the mapping to the workspace.
+__device__ void fused_map_token(const DeviceBatch& b, const FusedLds& s, int64_t t, bool report,
+                                int& row, int& pos, int& slot) {
+  int lo = 0, hi = s.n_facts - 1;  // the fact of t: the last f with tok[f] <= t
+  while (lo < hi) {
+    const int mid = (lo + hi + 1) / 2;
+    if (s.tok[mid] <= t) lo = mid; else hi = mid - 1;
+  }
+  const int off = int(t - s.tok[lo]);
+  const int r = s.req[lo];
+  const int64_t ps = s.pos0[lo] + off;
+  int bad = 0;
+  row = s.row0[lo] + off;
+  slot = 0;
+  if (ps < 0 || ps >= b.max_position) {
+    bad = 2;
+  } else {
+    const int64_t bi = ps / b.block_size;
+    const int nb = b.bt_len[r];
+    const int64_t blk =
+        bi < nb && bi < b.bt_stride ? int64_t(b.block_tables[int64_t(r) * b.bt_stride + bi]) : -1;
+    if (blk < 0 || blk >= b.num_blocks) bad = 4;
+    else slot = int32_t(blk * b.block_size + ps % b.block_size);
+  }
+  if (bad) {
+    if (report) flag(b.status, bad);
+    row = -1;
+  }
+  pos = bad ? 0 : int32_t(b.chunk_local ? s.pos0[lo] : ps);
+  if (report) {
+    b.src_row[t] = row;
+    b.pos[t] = pos;
+    b.slot[t] = slot;
+  }
+}
+
+template <int D, int STYLE, bool MULTI, bool FUSED>
 __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerPtrs kc,
-                                                          LayerPtrs vc) {
+                                                          LayerPtrs vc, DeviceBatch fb) {
   constexpr int CPH = D / 16;   // 16-byte chunks per half head
   constexpr int HALF = D / 2;   // pairs per head
   extern __shared__ f32x4 smem[];
 
   const int tpw = MULTI ? p.tpw : 1;
   const int tile_tokens = kWavesPerGroup * tpw;
+  int* meta = reinterpret_cast<int*>(smem + tile_tokens * HALF);  // row, pos, slot
   int64_t n_tokens = p.n_tokens;
-  if (p.n_tokens_dev) {
+  FusedLds* fused = nullptr;
+  if constexpr (FUSED) {
+    // after meta, 16-byte aligned
+    fused = reinterpret_cast<FusedLds*>(smem + tile_tokens * HALF + (3 * tile_tokens + 3) / 4);
+    const int64_t planned = fused_plan(fb, *fused);
+    n_tokens = planned < n_tokens ? planned : n_tokens;
+  } else if (p.n_tokens_dev) {
     const int64_t dev = *p.n_tokens_dev;
     n_tokens = dev < n_tokens ? (dev < 0 ? 0 : dev) : n_tokens;
   }
   const int64_t n_tiles = (n_tokens + tile_tokens - 1) / tile_tokens;
-  const int split = blockIdx.x % p.n_splits;
-  const int64_t tile_stride = gridDim.x / p.n_splits;
-  int* meta = reinterpret_cast<int*>(smem + tile_tokens * HALF);  // row, pos, slot
 
   const int wave = threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -153,14 +328,36 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   const int H = p.num_heads;
   const int nc = H * CPH;                 // chunks per (token, layer) row
   const int total = p.num_layers * nc;    // chunks per token
-  const int it0 = split * p.iters_per_split;
-  int it1 = it0 + p.iters_per_split;
   const int max_it = tpw > 1 ? p.num_layers : (total + kWave - 1) / kWave;
+
+  // The host sized the grid for an upper bound of the token count; when the
+  // count is only known here (device mapping) and is smaller, split each
+  // tile's iterations over more workgroups, with the host's rule, so the
+  // whole grid works.
+  int n_splits = p.n_splits, per = p.iters_per_split;
+  if (FUSED || p.n_tokens_dev) {
+    int sp = n_splits;
+    while (sp < max_it && n_tiles * sp * 2 <= int64_t(gridDim.x) &&
+           n_tiles * sp * kWavesPerGroup < p.want_waves)
+      sp *= 2;
+    if (sp > max_it) sp = max_it;
+    if (sp != n_splits) {
+      per = (max_it + sp - 1) / sp;
+      per = (per + kUnroll - 1) / kUnroll * kUnroll;
+      n_splits = (max_it + per - 1) / per;
+    }
+  }
+  const int split = blockIdx.x % n_splits;
+  const int64_t tile_stride = gridDim.x / n_splits;
+  const int64_t first_tile =
+      blockIdx.x < tile_stride * n_splits ? blockIdx.x / n_splits : n_tiles;  // spare: none
+  const int it0 = split * per;
+  int it1 = it0 + per;
   if (it1 > max_it) it1 = max_it;
   const int64_t row_elems = int64_t(H) * D;
   const int64_t layer_elems = p.capacity_rows * row_elems;
 
-  for (int64_t tile = blockIdx.x / p.n_splits; tile < n_tiles; tile += tile_stride) {
+  for (int64_t tile = first_tile; tile < n_tiles; tile += tile_stride) {
     const int64_t tok0 = tile * tile_tokens;
     __syncthreads();  // LDS of the previous tile is no longer read
 
@@ -170,9 +367,13 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
       const int64_t t = tok0 + i;
       int row = -1, pos = 0, slot = 0;
       if (t < n_tokens) {
-        row = p.src_row[t];
-        pos = p.pos[t];
-        slot = p.slot[t];
+        if constexpr (FUSED) {
+          fused_map_token(fb, *fused, t, split == 0, row, pos, slot);
+        } else {
+          row = p.src_row[t];
+          pos = p.pos[t];
+          slot = p.slot[t];
+        }
         const int bad = row == -1 ? 0
                         : ((row < 0 || row >= p.capacity_rows) ? 1 : 0) |
                           ((pos < 0 || pos >= p.max_position) ? 2 : 0) |
@@ -308,40 +509,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
 // a token that fails is written with row -1 (skipped by the inject kernel).
 // ---------------------------------------------------------------------------
 
-struct FactPlan {
-  int32_t tok_start, row0, len, pad;
-};
-
-struct DeviceBatch {
-  const int32_t* req_fact_ptr;
-  const int32_t* fact_ids;
-  const int32_t* start_pos;
-  const int32_t* block_tables;
-  const int32_t* bt_len;
-  const int2* fact_table;      // [store max_facts] (first row or -1, length)
-  FactPlan* plan;              // workspace
-  int64_t* n_tokens_out;       // workspace header
-  int32_t* n_facts_out;        // workspace header
-  int32_t* src_row;            // workspace, [max_tokens]
-  int32_t* pos;
-  int32_t* slot;
-  int32_t* status;
-  int64_t max_tokens;
-  int64_t num_blocks;
-  int32_t n_req;
-  int32_t bt_stride;
-  int32_t max_facts_batch;
-  int32_t store_max_facts;
-  int32_t block_size;
-  int32_t max_position;
-  int32_t chunk_local;         // rotation position = the fact's first position
-};
-
 constexpr int kPlanThreads = 1024;
-
-__device__ __forceinline__ void flag(int32_t* status, int bits) {
-  if (status) atomicOr(status, bits);
-}
 
 __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DeviceBatch b) {
   __shared__ int wave_sums[kPlanThreads / kWave];
@@ -466,24 +634,27 @@ int compute_units() {
   return n;
 }
 
+template <int D, int STYLE, bool MULTI>
+void launch_one(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
+                const DeviceBatch* fused, int64_t grid, size_t lds, hipStream_t s) {
+  if (fused)
+    hipLaunchKernelGGL((inject_kernel<D, STYLE, MULTI, true>), dim3(unsigned(grid)),
+                       dim3(kThreads), lds, s, p, kc, vc, *fused);
+  else
+    hipLaunchKernelGGL((inject_kernel<D, STYLE, MULTI, false>), dim3(unsigned(grid)),
+                       dim3(kThreads), lds, s, p, kc, vc, DeviceBatch{});
+}
+
 template <int D>
 hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
-                  int64_t grid, size_t lds, int style, hipStream_t s) {
+                  const DeviceBatch* fused, int64_t grid, size_t lds, int style, hipStream_t s) {
   const bool multi = p.tpw > 1;
   if (style == PRKV_ROPE_INTERLEAVED) {
-    if (multi)
-      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED, true>), dim3(unsigned(grid)),
-                         dim3(kThreads), lds, s, p, kc, vc);
-    else
-      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_INTERLEAVED, false>), dim3(unsigned(grid)),
-                         dim3(kThreads), lds, s, p, kc, vc);
+    if (multi) launch_one<D, PRKV_ROPE_INTERLEAVED, true>(p, kc, vc, fused, grid, lds, s);
+    else launch_one<D, PRKV_ROPE_INTERLEAVED, false>(p, kc, vc, fused, grid, lds, s);
   } else {
-    if (multi)
-      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT, true>), dim3(unsigned(grid)),
-                         dim3(kThreads), lds, s, p, kc, vc);
-    else
-      hipLaunchKernelGGL((inject_kernel<D, PRKV_ROPE_HALF_SPLIT, false>), dim3(unsigned(grid)),
-                         dim3(kThreads), lds, s, p, kc, vc);
+    if (multi) launch_one<D, PRKV_ROPE_HALF_SPLIT, true>(p, kc, vc, fused, grid, lds, s);
+    else launch_one<D, PRKV_ROPE_HALF_SPLIT, false>(p, kc, vc, fused, grid, lds, s);
   }
   return hipGetLastError();
 }
@@ -525,11 +696,14 @@ int check_cache_args(const prkv_store* st, int32_t block_size, int64_t num_block
 }
 
 // Enqueues the inject kernel for up to n_tokens tokens (the exact count is
-// *n_tokens_dev when that is set).  Arguments are already validated.
+// *n_tokens_dev when that is set).  With `fused` set, the kernel maps the
+// batch itself (small batches, see fused_plan).  Arguments are already
+// validated.
 int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_tokens_dev,
                   const int32_t* d_src_row, const int32_t* d_pos, const int32_t* d_slot,
                   void* const* k_cache_layers, void* const* v_cache_layers, int32_t block_size,
-                  int64_t num_blocks, int32_t* d_status, hipStream_t s) {
+                  int64_t num_blocks, int32_t* d_status, hipStream_t s,
+                  const DeviceBatch* fused = nullptr) {
   const prkv_store_desc& d = st->desc;
   LayerPtrs kc{}, vc{};
   for (int l = 0; l < d.num_layers; ++l) {
@@ -555,8 +729,18 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   // at most 2^20 workgroups; each loops over tiles with a grid stride
   const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
                                                                     : (int64_t(1) << 20) / n_splits;
-  const int64_t grid = grid_tiles * n_splits;
-  const size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
+  int64_t grid = grid_tiles * n_splits;
+  if (n_tokens_dev || fused) {
+    // The count is known only on the device and may be far below n_tokens:
+    // launch enough workgroups for the kernel to spread a small batch over
+    // the chip (its rule stops below 2 * want_waves / 4 workgroups).
+    const int64_t spread = std::min<int64_t>(want_waves / kWavesPerGroup * 2, tiles * iters);
+    if (grid < spread) grid = spread;
+  }
+  size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
+  if (fused)  // the plan follows the metadata at the next 16-byte boundary
+    lds = size_t(tile_tokens) * size_t(D / 2) * 16 + size_t((3 * tile_tokens + 3) / 4) * 16 +
+          sizeof(FusedLds);
 
   InjectParams p;
   p.k_arena = static_cast<const uint16_t*>(st->k_arena);
@@ -576,16 +760,17 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   p.n_splits = n_splits;
   p.iters_per_split = per;
   p.tpw = tpw;
+  p.want_waves = int32_t(want_waves);
 
   hipError_t e;
   switch (D) {
-    case 16: e = launch<16>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 32: e = launch<32>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 64: e = launch<64>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 128: e = launch<128>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 256: e = launch<256>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 512: e = launch<512>(p, kc, vc, grid, lds, d.rope_style, s); break;
-    case 1024: e = launch<1024>(p, kc, vc, grid, lds, d.rope_style, s); break;
+    case 16: e = launch<16>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 32: e = launch<32>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 64: e = launch<64>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 128: e = launch<128>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 256: e = launch<256>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 512: e = launch<512>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
+    case 1024: e = launch<1024>(p, kc, vc, fused, grid, lds, d.rope_style, s); break;
     default: return prkv::fail(PRKV_ERR_INVALID_ARG, "head_dim %d unsupported", D);
   }
   if (e != hipSuccess) return hip_fail(e, "inject launch");
@@ -783,6 +968,9 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
   db.chunk_local = st->desc.key_layout == PRKV_KEYS_CHUNK_LOCAL;
 
   hipStream_t s = static_cast<hipStream_t>(stream);
+  if (b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs)   // one launch
+    return launch_inject(st, b.max_tokens, nullptr, nullptr, nullptr, nullptr, k_cache_layers,
+                         v_cache_layers, block_size, num_blocks, d_status, s, &db);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "plan launch");

@@ -1,7 +1,10 @@
 """GPU tests specific to the device-resident path (inject_topk_device):
 validation on the device never faults, reports what it skipped, and
 everything it did not skip matches the oracle bit for bit (V, untouched
-slots) or within 2 ulp (K).
+slots) or within 2 ulp (K).  Each runs on both device mappings: the fused
+single launch (batches of at most 256 facts and 256 requests) and the
+plan + mapping + inject kernels (forced by a larger max_facts bound); the two
+must also agree with each other bit for bit, workspace included.
 
 Expected images come from the oracle over the same requests, with the slots
 of the tokens the device must skip put back to the sentinel.
@@ -61,20 +64,25 @@ def _check(dw, w_oracle, skip_slots=()):
 
 
 FACTS = {0: 9, 1: 14, 2: 5}
+FUSE_LIMIT = 256           # the library's bound for the fused mapping
+MAPPINGS = {"fused": {}, "kernels": {"max_facts": FUSE_LIMIT + 44}}
+mapping = pytest.mark.parametrize("kw", list(MAPPINGS.values()), ids=list(MAPPINGS))
 
 
+@mapping
 @pytest.mark.parametrize("bad_id", [999, -1])
-def test_unknown_fact_is_dropped(bad_id):
+def test_unknown_fact_is_dropped(bad_id, kw):
     """An unknown id contributes no tokens; the next fact follows directly."""
     w = custom_workload("unknown", 2, 8, 128, 16, FACTS, [([0, 1, 2], 7)])
-    dw = _device_run(w, patch=lambda dw: dw.d_ids.__setitem__(1, bad_id))
+    dw = _device_run(w, patch=lambda dw: dw.d_ids.__setitem__(1, bad_id), **kw)
     assert int(dw.status.item()) == 8
     _check(dw, dataclasses.replace(w, retrieved=[[0, 2]]))
 
 
-def test_position_out_of_range_is_skipped():
+@mapping
+def test_position_out_of_range_is_skipped(kw):
     w = custom_workload("pos_oob", 2, 8, 128, 16, FACTS, [([0, 1, 2], 40)], max_position=64)
-    dw = _device_run(w)
+    dw = _device_run(w, **kw)
     assert int(dw.status.item()) == 2
     _, pos, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
     skip = [s for p, s in zip(pos, slot) if p >= 64]
@@ -82,10 +90,11 @@ def test_position_out_of_range_is_skipped():
     _check(dw, w, skip)
 
 
-def test_short_block_table_is_skipped():
+@mapping
+def test_short_block_table_is_skipped(kw):
     w = custom_workload("bt_short", 2, 8, 128, 16, FACTS, [([0, 1, 2], 7)])
     nb = len(w.block_tables[0])
-    dw = _device_run(w, patch=lambda dw: dw.d_bt_len.__setitem__(0, nb - 1))
+    dw = _device_run(w, patch=lambda dw: dw.d_bt_len.__setitem__(0, nb - 1), **kw)
     assert int(dw.status.item()) == 4
     _, pos, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
     skip = [s for p, s in zip(pos, slot) if p // 16 >= nb - 1]
@@ -93,46 +102,113 @@ def test_short_block_table_is_skipped():
     _check(dw, w, skip)
 
 
-def test_block_id_out_of_range_is_skipped():
+@mapping
+def test_block_id_out_of_range_is_skipped(kw):
     w = custom_workload("bt_bad_id", 2, 8, 128, 16, FACTS, [([0, 1, 2], 7)])
-    dw = _device_run(w, patch=lambda dw: dw.d_bt.__setitem__((0, 1), w.num_blocks + 3))
+    dw = _device_run(w, patch=lambda dw: dw.d_bt.__setitem__((0, 1), w.num_blocks + 3), **kw)
     assert int(dw.status.item()) == 4
     _, pos, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
     skip = [s for p, s in zip(pos, slot) if p // 16 == 1]
     _check(dw, w, skip)
 
 
-def test_max_tokens_drops_the_excess():
+@mapping
+def test_max_tokens_drops_the_excess(kw):
     w = custom_workload("max_tok", 2, 8, 128, 16, FACTS, [([0, 1, 2], 7)])
     n = w.n_tokens
-    dw = _device_run(w, max_tokens=n - 5)
+    dw = _device_run(w, max_tokens=n - 5, **kw)
     assert int(dw.status.item()) == 16
     _, _, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
     assert dw.device_mapping()[0] == n - 5
     _check(dw, w, slot[n - 5:])
 
 
-def test_max_facts_drops_the_excess():
-    w = custom_workload("max_facts", 2, 8, 128, 16, FACTS, [([0, 1, 2], 7)])
-    dw = _device_run(w, max_facts=2)
+@mapping
+@pytest.mark.parametrize("heads", [8, 1])
+def test_loose_max_tokens_bound(heads, kw):
+    """max_tokens far above the batch's count: the grid is sized for the bound
+    and the kernel spreads the real tokens over it (split count chosen on the
+    device); every token is still injected exactly once."""
+    w = custom_workload(f"loose_h{heads}", 6, heads, 128, 16, FACTS, [([2, 0, 1], 3), ([1], 20)],
+                        num_blocks=4096)
+    dw = _device_run(w, max_tokens=64 * w.n_tokens, **kw)
+    assert int(dw.status.item()) == 0
+    assert dw.device_mapping()[0] == w.n_tokens
+    _check(dw, w)
+
+
+@pytest.mark.parametrize("bound", [2, FUSE_LIMIT, FUSE_LIMIT + 1])
+def test_max_facts_drops_the_excess(bound):
+    """More facts than max_facts: the excess facts are dropped (the first two
+    bounds take the fused mapping, the last the separate kernels)."""
+    ids = [0, 1, 2] * ((bound + 2) // 3 + 1)            # repeats are legal
+    w = custom_workload(f"max_facts_{bound}", 2, 8, 128, 16, FACTS, [(ids, 7)],
+                        num_blocks=2048)
+    dw = _device_run(w, max_facts=bound)
     assert int(dw.status.item()) == 32
-    _check(dw, dataclasses.replace(w, retrieved=[[0, 1]]))
+    _check(dw, dataclasses.replace(w, retrieved=[ids[:bound]]))
 
 
-def test_two_batches_reuse_store_and_workspace():
+@pytest.mark.parametrize("max_facts", [8, FUSE_LIMIT + 1], ids=["fused", "kernels"])
+def test_two_batches_reuse_store_and_workspace(max_facts):
     """Two different batches through one store and one workspace."""
     facts = {0: 9, 1: 14, 2: 5, 3: 21}
     w1 = custom_workload("batch_a", 3, 8, 128, 16, facts, [([3, 0], 5), ([1, 2, 1], 11)])
-    dw = _device_run(w1, max_tokens=200, max_facts=8)
+    dw = _device_run(w1, max_tokens=200, max_facts=max_facts)
     assert int(dw.status.item()) == 0
     _check(dw, w1)
     # second batch: other order and prefix, same blocks
     w2 = dataclasses.replace(w1, retrieved=[[2, 3], [0]], prefix=np.array([0, 30]))
     dw.w = w2
     dw.reset_cache()
-    dw.setup_device_batch(max_tokens=200, max_facts=8)
+    dw.setup_device_batch(max_tokens=200, max_facts=max_facts)
     dw.status.zero_()
     dw.inject_device()
     torch.cuda.synchronize()
     assert int(dw.status.item()) == 0
     _check(dw, w2)
+
+
+def _workspace_parts(dw):
+    """Header, plan and per-token mapping the device path left in its workspace."""
+    ws = dw.workspace.cpu().numpy()
+    lay = dw.ws_layout
+    n_tok = int(ws[0:8].view(np.int64)[0])
+    n_facts = int(ws[8:12].view(np.int32)[0])
+    plan = ws[lay["plan"]:lay["plan"] + 16 * n_facts].view(np.int32).reshape(n_facts, 4)
+    arr = [ws[lay[k]:lay[k] + 4 * n_tok].view(np.int32).copy() for k in ("src_row", "pos", "slot")]
+    return n_tok, n_facts, plan.copy(), arr
+
+
+AGREE = [
+    ("tiny_L1_H2_D64", {}),
+    ("llama3_8b_k5", {}),
+    ("llama3_8b_k50", {}),
+    ("llama3_8b_k5", {"rope_style": 1, "key_layout": 1}),          # interleaved, chunk-local
+    ("llama3_8b_k5", {"num_kv_heads": 1}),                          # 8 tokens per wave
+]
+
+
+@pytest.mark.parametrize("name,changes", AGREE,
+                         ids=[n + "".join(f"_{k}{v}" for k, v in c.items()) for n, c in AGREE])
+def test_fused_mapping_equals_separate_kernels(name, changes):
+    w = workloads.make(workloads.with_spec(name, **changes))
+    dw = harness.DeviceWorkload(w, host_mapping=False, gen_device="cuda")
+    results = []
+    for kw in MAPPINGS.values():
+        dw.reset_cache()
+        dw.setup_device_batch(**kw)
+        dw.status.zero_()
+        dw.inject_device()
+        torch.cuda.synchronize()
+        gk, gv = dw.listed_blocks_host(w.listed_blocks())
+        results.append((int(dw.status.item()), _workspace_parts(dw), gk, gv,
+                        dw.count_non_sentinel()))
+    (s1, (n1, f1, p1, m1), k1, v1, c1), (s2, (n2, f2, p2, m2), k2, v2, c2) = results
+    assert s1 == s2 == 0
+    assert n1 == n2 == w.n_tokens and f1 == f2
+    assert np.array_equal(p1, p2)
+    assert all(np.array_equal(a, b) for a, b in zip(m1, m2))
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2) and c1 == c2
+    sp = w.spec
+    assert c1 == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
