@@ -371,6 +371,10 @@ EDGE = [
     ("many_layers_80", 80, 8, 128, 16, {0: 6, 1: 9}, [([1, 0], 40)]),
     ("bs1", 2, 8, 128, 1, {0: 6, 1: 9}, [([1, 0], 3)]),
     ("far_positions", 2, 8, 128, 16, {0: 40, 1: 9}, [([1, 0], 16000)]),
+    # 250 facts: the fused device mapping, 2,500 tiles on its 2,048-workgroup
+    # grid, so some workgroups take a second tile by the grid stride
+    ("fused_grid_stride", 2, 8, 128, 16, {i: 40 for i in range(250)},
+     [(list(range(250)), 3)]),
 ]
 
 
@@ -378,7 +382,7 @@ EDGE = [
 @pytest.mark.parametrize("case", EDGE, ids=[c[0] for c in EDGE])
 def test_edge_case(case, path):
     name, L, H, D, bs, facts, reqs = case
-    nb = 2048 if name == "far_positions" else 512
+    nb = 2048 if name in ("far_positions", "fused_grid_stride") else 512
     w = custom_workload(name, L, H, D, bs, facts, reqs, theta=5e5, num_blocks=nb)
     dw, rep, (img_k, img_v, gk, gv) = run_full(w, gen_device="cuda", path=path)
     if name == "prefix0_len1":
