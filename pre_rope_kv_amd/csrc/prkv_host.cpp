@@ -120,6 +120,7 @@ void commit_put(prkv_store* st, int32_t fact_id, int32_t len) {
   st->first_row[fact_id] = st->rows_used;
   st->length[fact_id] = len;
   st->rows_used += len;
+  st->facts_put += 1;
 }
 
 }  // namespace prkv

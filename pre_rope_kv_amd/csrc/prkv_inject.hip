@@ -333,15 +333,13 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   const int total = p.num_layers * nc;    // chunks per token
   const int max_it = tpw > 1 ? p.num_layers : (total + kWave - 1) / kWave;
 
-  // The host sized the grid for an upper bound of the token count; when the
-  // count is only known here (device mapping), re-derive the split count:
-  // fewer splits if the tiles would not fit the grid in one pass (a fused
-  // launch has a capped grid), more, with the host's rule, if a small batch
-  // would leave most of the grid idle.
+  // When the count is only known here (device mapping), the host sized the
+  // grid for an estimate of it: a larger batch is covered by the grid
+  // stride, and a small one gets more splits, with the host's rule, so it
+  // does not leave most of the grid idle.
   int n_splits = p.n_splits, per = p.iters_per_split;
   if (FUSED || p.n_tokens_dev) {
     int sp = n_splits;
-    while (sp > 1 && n_tiles * sp > int64_t(gridDim.x)) sp = (sp + 1) / 2;
     while (sp < max_it && n_tiles * sp * 2 <= int64_t(gridDim.x) &&
            n_tiles * sp * kWavesPerGroup < p.want_waves)
       sp *= 2;
@@ -701,14 +699,14 @@ int check_cache_args(const prkv_store* st, int32_t block_size, int64_t num_block
 }
 
 // Enqueues the inject kernel for up to n_tokens tokens (the exact count is
-// *n_tokens_dev when that is set).  With `fused` set, the kernel maps the
-// batch itself (small batches, see fused_plan).  Arguments are already
-// validated.
+// *n_tokens_dev when that is set, and the grid is then sized for
+// expect_tokens).  With `fused` set, the kernel maps the batch itself (small
+// batches, see fused_plan).  Arguments are already validated.
 int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_tokens_dev,
                   const int32_t* d_src_row, const int32_t* d_pos, const int32_t* d_slot,
                   void* const* k_cache_layers, void* const* v_cache_layers, int32_t block_size,
                   int64_t num_blocks, int32_t* d_status, hipStream_t s,
-                  const DeviceBatch* fused = nullptr) {
+                  const DeviceBatch* fused = nullptr, int64_t expect_tokens = -1) {
   const prkv_store_desc& d = st->desc;
   LayerPtrs kc{}, vc{};
   for (int l = 0; l < d.num_layers; ++l) {
@@ -724,7 +722,11 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   const int iters = tpw > 1 ? d.num_layers : int((chunks + kWave - 1) / kWave);
   const int64_t want_waves = int64_t(compute_units()) * 16;
   const int64_t tile_tokens = int64_t(kWavesPerGroup) * tpw;
-  const int64_t tiles = (n_tokens + tile_tokens - 1) / tile_tokens;
+  const bool device_count = n_tokens_dev || fused;
+  const int64_t sized_for =
+      device_count && expect_tokens >= 0 && expect_tokens < n_tokens ? expect_tokens : n_tokens;
+  const int64_t tiles = std::max<int64_t>(1, (sized_for + tile_tokens - 1) / tile_tokens);
+  const int64_t tiles_bound = (n_tokens + tile_tokens - 1) / tile_tokens;
   // At least one split per XCD: workgroups are dealt to the 8 XCDs round
   // robin, so split = blockIdx % 8 gives each XCD's L2 and translation caches
   // one range of layers (measured on MI355X: 2-3 % faster than whole tokens
@@ -739,15 +741,17 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   const int64_t grid_tiles = tiles < (int64_t(1) << 20) / n_splits ? tiles
                                                                     : (int64_t(1) << 20) / n_splits;
   int64_t grid = grid_tiles * n_splits;
-  if (n_tokens_dev || fused) {
-    // The count is known only on the device and may be far below n_tokens:
-    // launch enough workgroups for the kernel to spread a small batch over
-    // the chip (its rule stops below 2 * want_waves / 4 workgroups).  A
-    // fused launch takes exactly that many: each of its workgroups rebuilds
-    // the plan before it knows whether it has a tile, so spare ones are not
-    // free; a larger batch is covered by the grid stride.
-    const int64_t spread = std::min<int64_t>(want_waves / kWavesPerGroup * 2, tiles * iters);
-    if (grid < spread || fused) grid = spread;
+  if (device_count) {
+    // The grid is sized for the expected count rather than the bound: a
+    // spare workgroup still loads the count before it can exit, and spare
+    // ones run last, so a grid sized for a loose bound costs ~0.6 ns per
+    // spare workgroup at the end of the kernel (measured: +8 % at 4 x the
+    // count).  At least enough workgroups for the kernel to spread a small
+    // batch over the chip (its rule stops below 2 * want_waves / 4), which
+    // also keeps the chip covered if the estimate is far too low.
+    const int64_t spread =
+        std::min<int64_t>(want_waves / kWavesPerGroup * 2, tiles_bound * iters);
+    if (grid < spread) grid = spread;
   }
   size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
   if (fused)  // the plan follows the metadata at the next 16-byte boundary
@@ -979,10 +983,17 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
   db.max_position = st->desc.max_position;
   db.chunk_local = st->desc.key_layout == PRKV_KEYS_CHUNK_LOCAL;
 
+  // Expected token count: max_facts facts of the store's mean length, plus
+  // 10 %.  The kernels stay correct for any count up to max_tokens.
+  int64_t expect = b.max_tokens;
+  if (st->facts_put > 0) {
+    const double mean = double(st->rows_used) / double(st->facts_put);
+    expect = std::min<int64_t>(b.max_tokens, int64_t(1.1 * mean * b.max_facts) + 1);
+  }
   hipStream_t s = static_cast<hipStream_t>(stream);
   if (b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs)   // one launch
     return launch_inject(st, b.max_tokens, nullptr, nullptr, nullptr, nullptr, k_cache_layers,
-                         v_cache_layers, block_size, num_blocks, d_status, s, &db);
+                         v_cache_layers, block_size, num_blocks, d_status, s, &db, expect);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "plan launch");
@@ -991,7 +1002,8 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "materialize launch");
   return launch_inject(st, b.max_tokens, db.n_tokens_out, db.src_row, db.pos, db.slot,
-                       k_cache_layers, v_cache_layers, block_size, num_blocks, d_status, s);
+                       k_cache_layers, v_cache_layers, block_size, num_blocks, d_status, s,
+                       nullptr, expect);
 }
 
 }  // extern "C"

@@ -13,6 +13,7 @@ struct prkv_store {
   void* v_arena = nullptr;
   void* rope = nullptr;     // device, [max_position][D/2] x (cos_hi, cos_lo, sin_hi, sin_lo)
   int64_t rows_used = 0;
+  int64_t facts_put = 0;
   std::vector<int64_t> first_row;  // per fact id; -1 when absent
   std::vector<int32_t> length;     // per fact id
   bool device_backed() const { return k_arena != nullptr; }

@@ -137,6 +137,19 @@ def test_loose_max_tokens_bound(heads, kw):
     _check(dw, w)
 
 
+@mapping
+def test_expected_count_far_too_low(kw):
+    """The grid is sized for max_facts facts of the store's mean length; a
+    batch of the one long fact (mean length ~7, batch 600 tokens) is ~25 x
+    that, covered by the grid stride."""
+    facts = {0: 200, **{i: 1 for i in range(1, 31)}}
+    w = custom_workload("long_fact", 4, 8, 128, 16, facts, [([0, 0, 0], 5)], num_blocks=1024)
+    dw = _device_run(w, **kw)
+    assert int(dw.status.item()) == 0
+    assert dw.device_mapping()[0] == 600
+    _check(dw, w)
+
+
 @pytest.mark.parametrize("bound", [2, FUSE_LIMIT, FUSE_LIMIT + 1])
 def test_max_facts_drops_the_excess(bound):
     """More facts than max_facts: the excess facts are dropped (the first two
