@@ -256,7 +256,10 @@ int inject_device_workspace_bytes(int32_t max_facts, int64_t max_tokens, size_t*
  * Kernels on `stream`: when batch->max_facts <= 256 and n_req <= 256, one
  * launch (every inject workgroup maps its own tokens from the batch); larger
  * batches take three (plan, per-token mapping, inject).  Both fill the
- * workspace and d_status identically.  Asynchronous, never synchronizes.  d_workspace: caller-owned device memory of
+ * workspace and d_status identically.  The launch is sized for max_facts
+ * facts of the store's mean stored length; any count up to max_tokens is
+ * handled, a larger one with more work per workgroup.  Asynchronous, never
+ * synchronizes.  d_workspace: caller-owned device memory of
  * inject_device_workspace_bytes(batch->max_facts, batch->max_tokens), 256-byte
  * aligned; d_fact_table from store_upload_fact_table.  Invalid input found on
  * the device never faults: the token is skipped and d_status (optional) gets
