@@ -17,7 +17,7 @@ import pytest
 import torch
 
 from oracle import paged
-from pre_rope_kv_amd import harness, workloads
+from pre_rope_kv_amd import harness, prkv, workloads
 
 from test_gpu_parity import (_release_device_memory, compare, custom_workload,  # noqa: F401
                              oracle_images, written_mask)
@@ -225,3 +225,57 @@ def test_fused_mapping_equals_separate_kernels(name, changes):
     assert np.array_equal(k1, k2) and np.array_equal(v1, v2) and c1 == c2
     sp = w.spec
     assert c1 == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
+
+
+SHAPES = [(2, 1, 16), (3, 2, 64), (2, 8, 128)]      # (layers, KV heads, head_dim)
+FAULTS = [None, "unknown_id", "short_table", "bad_block"]
+
+
+@pytest.mark.parametrize("seed", range(24))
+def test_random_small_batches_both_mappings(seed):
+    """Seeded random small batches (repeated and absent ids, empty requests,
+    block sizes 1-32, three head shapes), a quarter of them valid and the
+    rest with one planted fault.  Valid: both device mappings equal the host
+    library's build_slot_mapping and the caches meet the oracle.  Always:
+    the fused and the separate-kernel mappings agree bit for bit (cache,
+    workspace, status)."""
+    rng = np.random.default_rng(5000 + seed)
+    L, H, D = SHAPES[seed % len(SHAPES)]
+    fault = FAULTS[(seed // len(SHAPES)) % len(FAULTS)]
+    n_facts = int(rng.integers(1, 12))
+    facts = {f: int(rng.integers(1, 40)) for f in range(n_facts)}
+    reqs = []
+    for r in range(int(rng.integers(1, 6))):
+        k = int(rng.integers(1 if r == 0 else 0, 6))
+        reqs.append(([int(x) for x in rng.integers(0, n_facts, size=k)], int(rng.integers(0, 100))))
+    bs = int(rng.choice([1, 4, 16, 32]))
+    w = custom_workload(f"rand{seed}", L, H, D, bs, facts, reqs, num_blocks=4096)
+
+    def plant(dw):
+        if fault == "unknown_id":
+            dw.d_ids[int(rng.integers(0, len(dw.d_ids)))] = n_facts + 7
+        elif fault == "short_table":
+            dw.d_bt_len[0] = max(0, int(dw.d_bt_len[0].item()) - 1)
+        elif fault == "bad_block":              # the block of request 0's first fact token
+            dw.d_bt[0, reqs[0][1] // bs] = w.num_blocks + 1
+
+    runs = []
+    for kw in MAPPINGS.values():
+        rng_state = rng.bit_generator.state
+        dw = _device_run(w, patch=plant, **kw)
+        rng.bit_generator.state = rng_state          # the same fault for both mappings
+        gk, gv = dw.listed_blocks_host(w.listed_blocks())
+        runs.append((int(dw.status.item()), _workspace_parts(dw), gk, gv, dw))
+    (s1, (n1, f1, p1, m1), k1, v1, dw1), (s2, (n2, f2, p2, m2), k2, v2, _) = runs
+    assert s1 == s2 and n1 == n2 and f1 == f2 and np.array_equal(p1, p2)
+    assert all(np.array_equal(a, b) for a, b in zip(m1, m2))
+    assert np.array_equal(k1, k2) and np.array_equal(v1, v2)
+    if fault is None:
+        assert s1 == 0 and n1 == w.n_tokens
+        req_ptr, ids, start, bt, bt_len = w.csr()
+        host = prkv.build_slot_mapping(dw1.store, req_ptr, ids, start, bt, bt_len, bs,
+                                       w.num_blocks)
+        assert all(np.array_equal(a, b) for a, b in zip(m1, host))
+        _check(dw1, w)
+    else:
+        assert s1 != 0
