@@ -399,7 +399,8 @@ def k_sweep(args):
     the device step (mapping + inject) for the first k facts of one drawn
     request of the 2,000-fact store, each k timed over args.steps launches,
     with the fused mapping (one launch) and with the separate plan and mapping
-    kernels (forced by a max_facts bound above the fused limit)."""
+    kernels (forced by a max_facts bound above the fused limit), back to back
+    and cold (each launch after a 1 GiB fill that evicts the MALL)."""
     import torch
 
     from pre_rope_kv_amd import harness, prkv, workloads
@@ -415,7 +416,9 @@ def k_sweep(args):
     big_ws = torch.zeros(prkv.inject_device_workspace_bytes(ptr_cap, dw.max_tokens),
                          dtype=torch.uint8, device=dw.device)
 
-    def time_step(k, max_facts, workspace):
+    scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+
+    def time_step(k, max_facts, workspace, cold=False):
         ptr = torch.tensor([0, k], dtype=torch.int32, device=dw.device)
         batch = prkv.device_batch(1, dw.d_bt.shape[1], max_facts, dw.max_tokens, ptr, dw.d_ids,
                                   dw.d_start, dw.d_bt, dw.d_bt_len)
@@ -431,6 +434,20 @@ def k_sweep(args):
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
+        if cold:
+            # one launch at a time, each after a 1 GiB fill that evicts the 256 MB MALL
+            n = min(args.steps, 50)
+            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+                  for _ in range(n)]
+            for i in range(n):
+                with torch.cuda.stream(stream):
+                    scratch.fill_(i)
+                ev[i][0].record(stream)
+                step()
+                ev[i][1].record(stream)
+            torch.cuda.synchronize()
+            assert int(dw.status.item()) == 0
+            return sum(a.elapsed_time(b) for a, b in ev) / n
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         e0.record(stream)
         for _ in range(args.steps):
@@ -443,11 +460,13 @@ def k_sweep(args):
     for k in (5, 10, 20, 50):
         ms = time_step(k, k, dw.workspace)              # fused mapping: one launch
         ms3 = time_step(k, ptr_cap, big_ws)             # plan + mapping + inject kernels
+        ms_cold = time_step(k, k, dw.workspace, cold=True)
         n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
         rows.append({"k": k, "tokens": n_tok, "step_ms": ms,
                      "tokens_per_s": n_tok / (ms * 1e-3),
                      "hbm_gbps": n_tok * w.spec.bytes_per_token / (ms * 1e-3) / 1e9,
-                     "step_ms_three_kernels": ms3})
+                     "step_ms_three_kernels": ms3,
+                     "step_ms_cold": ms_cold})
     print(json.dumps({"metric": "device step time vs retrieval budget k, 1 request, 1 MI355X",
                       "unit": "ms", "higher_is_better": False, "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
