@@ -30,10 +30,12 @@
 // fp32 rounding; K and V are the cache's bf16 values.  At 16 query tokens
 // the kernel does about 64 flop per byte of cache (128 with the doubled
 // products), below the MFMA ridge: it is bound by reading the cache.
-// At most 128 VGPRs (one 8-byte value spilled around the key loop) and
-// 33.5 KB of LDS plus the block table: four workgroups per CU while the
-// table has <= ~1,600 entries (measured on MI355X: 1.3-2 % faster than three
-// workgroups per CU at ~145 VGPRs).
+// A three-tile LDS ring (49.5 KB with the slot buffers, plus the block
+// table): three workgroups per CU, each with two tiles in flight while it
+// computes the third.  Bytes in flight decide the rate: measured on MI355X,
+// the kernel with its compute removed reads 5.6 TB/s with a two-tile ring
+// at four workgroups per CU, and the full kernel with three tiles at three
+// per CU is 2 % faster than with two tiles at four per CU.
 //
 // The query is rotated in-kernel with the store's RoPE table and pairing
 // (compensated fp32, as in injection).  Keys outside [0, q_start + q_len),
@@ -53,7 +55,7 @@ using namespace prkv_dev;
 
 constexpr int kWave = 64;
 constexpr int kTile = 32;       // keys per tile
-constexpr int kStages = 2;      // LDS ring of tiles; kStages - 1 are in flight
+constexpr int kStages = 3;      // LDS ring of tiles; kStages - 1 are in flight
 constexpr int kSlotRing = 4;    // slot buffers (>= kStages + 1, a power of two)
 constexpr int kMaxRows = 64;    // query rows per workgroup
 constexpr int kThreads = kMaxRows / 16 * kWave;
@@ -116,7 +118,7 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_addr) {
 }
 
 template <int D, int STYLE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(4))) void attend_kernel(AttnParams p, LayerCPtrs kc,
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(AttnParams p, LayerCPtrs kc,
                                                           LayerCPtrs vc) {
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
