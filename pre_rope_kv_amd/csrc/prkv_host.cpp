@@ -13,6 +13,7 @@
 //  - RoPE table: ledger axiom R_a^T R_b = R_{b-a} (Theorem 6, section 5.1);
 //    frequencies of RoFormer (reference [20]) with half-split pairing.
 
+#include <algorithm>
 #include <cmath>
 #include <cstdarg>
 #include <cstdio>
@@ -232,18 +233,45 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
   if (req_fact_ptr[n_req] > 0 && !fact_ids) return fail(PRKV_ERR_INVALID_ARG, "fact_ids is NULL");
   if (!block_tables && bt_stride > 0) return fail(PRKV_ERR_INVALID_ARG, "block_tables is NULL");
 
-  // Pass 1: resolve, place and validate into per-thread scratch; detect
-  // duplicate slots with a bitmap over all slots (bits are cleared again below).
-  static thread_local std::vector<int32_t> s_row, s_pos, s_slot;
+  // Pass 1: resolve, place and validate, run by run (a run = consecutive
+  // tokens of one fact inside one block: one division, one table lookup and
+  // one or two bitmap words per run).  Duplicate slots are found with a
+  // bitmap over all slots; a run's bits are set only once its whole range
+  // is free, and every run set is cleared again before returning.  Nothing
+  // is written to the outputs unless the whole batch is valid.
+  struct Run {
+    int64_t s0;
+    int32_t len;
+  };
   static thread_local std::vector<uint64_t> seen;
-  s_row.clear();
-  s_pos.clear();
-  s_slot.clear();
+  static thread_local std::vector<Run> runs;
+  runs.clear();
   const size_t words = size_t((num_slots + 63) / 64);
   if (seen.size() < words) seen.resize(words, 0);
   const prkv_store_desc& d = st->desc;
   const bool chunk_local = d.key_layout == PRKV_KEYS_CHUNK_LOCAL;
+  // first slot in [s0, s0 + n) already taken, or -1
+  auto first_taken = [&](int64_t s0, int64_t n) -> int64_t {
+    for (int64_t s = s0; s < s0 + n;) {
+      const int64_t b0 = s & 63, take = std::min<int64_t>(64 - b0, s0 + n - s);
+      const uint64_t mask = (take == 64 ? ~uint64_t(0) : ((uint64_t(1) << take) - 1)) << b0;
+      const uint64_t hit = seen[size_t(s >> 6)] & mask;
+      if (hit) return (s & ~int64_t(63)) + __builtin_ctzll(hit);
+      s += take;
+    }
+    return -1;
+  };
+  auto mark = [&](int64_t s0, int64_t n, bool set) {
+    for (int64_t s = s0; s < s0 + n;) {
+      const int64_t b0 = s & 63, take = std::min<int64_t>(64 - b0, s0 + n - s);
+      const uint64_t mask = (take == 64 ? ~uint64_t(0) : ((uint64_t(1) << take) - 1)) << b0;
+      if (set) seen[size_t(s >> 6)] |= mask;
+      else seen[size_t(s >> 6)] &= ~mask;
+      s += take;
+    }
+  };
   int rc = PRKV_OK;
+  int64_t total = 0;
   for (int32_t r = 0; r < n_req && rc == PRKV_OK; ++r) {
     const int32_t* bt = block_tables + int64_t(r) * bt_stride;
     int64_t p = start_pos[r];
@@ -254,16 +282,15 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
                   i - req_fact_ptr[r], f);
         break;
       }
-      const int64_t row0 = st->first_row[f];
       const int32_t len = st->length[f];
-      const int64_t fact_start = p;
       if (p + len > d.max_position) {
         rc = fail(PRKV_ERR_OUT_OF_RANGE, "request %d: position %lld >= max_position %d", r,
                   (long long)(p + len - 1), d.max_position);
         break;
       }
-      for (int32_t t = 0; t < len; ++t, ++p) {
+      for (int32_t t = 0; t < len;) {
         const int64_t bi = p / block_size;
+        const int64_t off = p - bi * block_size;
         if (bi >= bt_len[r]) {
           rc = fail(PRKV_ERR_OUT_OF_RANGE,
                     "request %d: position %lld needs block index %lld, table has %d", r,
@@ -276,34 +303,55 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
                     (long long)b, (long long)num_blocks);
           break;
         }
-        const int64_t s = b * block_size + p % block_size;
-        uint64_t& w = seen[size_t(s >> 6)];
-        const uint64_t bit = uint64_t(1) << (s & 63);
-        if (w & bit) {
+        const int32_t run = int32_t(std::min<int64_t>(block_size - off, len - t));
+        const int64_t s0 = b * block_size + off;
+        const int64_t dup = first_taken(s0, run);
+        if (dup >= 0) {
           rc = fail(PRKV_ERR_DUPLICATE_SLOT, "request %d: slot %lld written twice", r,
-                    (long long)s);
+                    (long long)dup);
           break;
         }
-        w |= bit;
-        s_row.push_back(int32_t(row0 + t));
-        s_pos.push_back(int32_t(chunk_local ? fact_start : p));
-        s_slot.push_back(int32_t(s));
+        mark(s0, run, true);
+        runs.push_back(Run{s0, run});
+        total += run;
+        t += run;
+        p += run;
       }
     }
   }
-  for (int32_t s : s_slot) seen[size_t(s) >> 6] = 0;
-  const int64_t total = int64_t(s_row.size());
+  for (const Run& u : runs) mark(u.s0, u.len, false);
   if (rc != PRKV_OK) return rc;
   *n_tokens = total;
   if (total > capacity)
     return fail(PRKV_ERR_BUFFER_TOO_SMALL, "%lld tokens, capacity %lld", (long long)total,
                 (long long)capacity);
-  if (total == 0) return PRKV_OK;  // nothing to copy; the outputs may be NULL
+  if (total == 0) return PRKV_OK;  // nothing to write; the outputs may be NULL
   if (!src_row || !pos || !slot)
     return fail(PRKV_ERR_INVALID_ARG, "output arrays must not be NULL");
-  std::memcpy(src_row, s_row.data(), size_t(total) * 4);
-  std::memcpy(pos, s_pos.data(), size_t(total) * 4);
-  std::memcpy(slot, s_slot.data(), size_t(total) * 4);
+
+  // Pass 2: the batch is valid; write (arena row, rotation position, slot)
+  // per token in request, fact-list and token order, run by run.
+  int64_t k = 0;
+  size_t u = 0;
+  for (int32_t r = 0; r < n_req; ++r) {
+    int64_t p = start_pos[r];
+    for (int32_t i = req_fact_ptr[r]; i < req_fact_ptr[r + 1]; ++i) {
+      const int32_t f = fact_ids[i];
+      const int64_t row0 = st->first_row[f];
+      const int32_t len = st->length[f];
+      const int64_t fact_start = p;
+      for (int32_t t = 0; t < len; ++u) {
+        const Run& run = runs[u];
+        for (int32_t j = 0; j < run.len; ++j, ++k) {
+          src_row[k] = int32_t(row0 + t + j);
+          pos[k] = int32_t(chunk_local ? fact_start : p + j);
+          slot[k] = int32_t(run.s0 + j);
+        }
+        t += run.len;
+        p += run.len;
+      }
+    }
+  }
   return PRKV_OK;
 }
 
