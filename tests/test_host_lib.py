@@ -354,3 +354,46 @@ def test_missing_library_fails_loudly(monkeypatch, tmp_path):
         prkv.store_required_bytes(_desc())
     with pytest.raises(ImportError):
         prkv.store_create(_desc())
+
+
+def _wide_block_store():
+    d = _desc(max_facts=4, capacity_rows=1000, max_position=1024)
+    st = prkv.store_create(d)
+    prkv.store_put_fact(st, 0, 150)   # rows 0..149
+    prkv.store_put_fact(st, 1, 90)    # rows 150..239
+    return st
+
+
+def test_slot_mapping_block_wider_than_a_bitmap_word():
+    """block_size 100: a run of one fact inside a block covers several
+    64-slot words of the duplicate bitmap; the mapping is still the closed
+    form slot = bt[p // bs] * bs + p % bs."""
+    st = _wide_block_store()
+    bt = np.array([[3, 0, 5], [2, 4, -1]], np.int32)
+    src, pos, slot = prkv.build_slot_mapping(st, [0, 1, 2], [0, 1], [37, 5], bt, [3, 2], 100, 8)
+    want_pos = list(range(37, 187)) + list(range(5, 95))
+    want_row = list(range(0, 150)) + list(range(150, 240))
+    want_slot = [int(bt[0][q // 100]) * 100 + q % 100 for q in range(37, 187)] + \
+                [int(bt[1][q // 100]) * 100 + q % 100 for q in range(5, 95)]
+    assert pos.tolist() == want_pos and src.tolist() == want_row and slot.tolist() == want_slot
+
+
+@pytest.mark.parametrize("start0,start1,first_dup", [(37, 63, 263), (37, 0, 237), (70, 0, 270)])
+def test_duplicate_slot_reports_the_first_one(start0, start1, first_dup):
+    """Two requests share block 2 (slots 200..299).  Request 0 takes slots
+    200 + start0 .. 299 with its fact 0; request 1 writes fact 1 from position
+    start1 in block 2, so its first clash is the lowest slot both cover, in
+    token order (270: request 1's run starts in bitmap word 3, the clash is in
+    word 4)."""
+    st = _wide_block_store()
+    bt = np.array([[2, 7, 6], [2, 5, -1]], np.int32)
+    outs = tuple(np.full(400, -7, np.int32) for _ in range(3))
+    with pytest.raises(prkv.PrkvError) as ei:
+        prkv.build_slot_mapping(st, [0, 1, 2], [0, 1], [start0, start1], bt, [3, 2], 100, 8,
+                                out=outs)
+    assert ei.value.name == "DUPLICATE_SLOT"
+    assert f"slot {first_dup} written twice" in str(ei.value)
+    assert all(np.all(o == -7) for o in outs)
+    # every bit set before the failure was cleared: the same blocks map cleanly now
+    src, pos, slot = prkv.build_slot_mapping(st, [0, 1], [1], [start1], bt[1:], [2], 100, 8)
+    assert slot.tolist() == [200 + q if q < 100 else 500 + q - 100 for q in range(start1, start1 + 90)]
