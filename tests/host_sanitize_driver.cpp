@@ -109,7 +109,8 @@ int main() {
     // random batches through build_slot_mapping
     for (int b = 0; b < 8; ++b) {
       const int n_req = u(rng) % 4;
-      const int bs = 1 + u(rng) % 16;
+      const int sizes[] = {1, 2, 5, 16, 63, 64, 65, 100, 130};
+      const int bs = sizes[u(rng) % 9];   // runs up to 130 slots span several bitmap words
       const int64_t num_blocks = 1 + u(rng) % 64;
       const int stride = u(rng) % 24;
       std::vector<int32_t> ptr(n_req + 1, 0), start(n_req), bt_len(n_req);
