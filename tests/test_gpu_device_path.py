@@ -227,6 +227,24 @@ def test_fused_mapping_equals_separate_kernels(name, changes):
     assert c1 == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
 
 
+@pytest.mark.parametrize("n_req", [FUSE_LIMIT, FUSE_LIMIT + 1])
+def test_many_requests_at_the_fused_limit(n_req):
+    """256 requests of one fact each fill the fused plan's request and fact
+    arrays exactly; 257 take the separate kernels.  Both must meet the oracle
+    and equal the host library's mapping."""
+    facts = {f: 1 + f % 5 for f in range(16)}
+    reqs = [([r % 16], r % 7) for r in range(n_req)]
+    w = custom_workload(f"req{n_req}", 2, 2, 64, 16, facts, reqs, num_blocks=4096)
+    dw = _device_run(w)
+    assert int(dw.status.item()) == 0
+    n, src, pos, slot = dw.device_mapping()
+    req_ptr, ids, start, bt, bt_len = w.csr()
+    host = prkv.build_slot_mapping(dw.store, req_ptr, ids, start, bt, bt_len, 16, w.num_blocks)
+    assert n == w.n_tokens
+    assert all(np.array_equal(a, b) for a, b in zip((src, pos, slot), host))
+    _check(dw, w)
+
+
 SHAPES = [(2, 1, 16), (3, 2, 64), (2, 8, 128)]      # (layers, KV heads, head_dim)
 FAULTS = [None, "unknown_id", "short_table", "bad_block"]
 
