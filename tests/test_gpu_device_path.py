@@ -249,7 +249,7 @@ SHAPES = [(2, 1, 16), (3, 2, 64), (2, 8, 128)]      # (layers, KV heads, head_di
 FAULTS = [None, "unknown_id", "short_table", "bad_block"]
 
 
-@pytest.mark.parametrize("seed", range(24))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_small_batches_both_mappings(seed):
     """Seeded random small batches (repeated and absent ids, empty requests,
     block sizes 1-32, three head shapes), a quarter of them valid and the

@@ -20,7 +20,7 @@ pytestmark = pytest.mark.gpu
 LLAMA31 = (8.0, 1.0, 4.0, 8192)
 
 
-@pytest.mark.parametrize("seed", range(16))
+@pytest.mark.parametrize("seed", range(64))
 def test_random_shape_and_options(seed):
     rng = np.random.default_rng(9000 + seed)
     L = int(rng.integers(1, 7))
