@@ -479,14 +479,15 @@ def main():
     if args.summarize_profile:
         trace_dir, fetch_dir, write_dir = args.summarize_profile
         regex = "|".join(list(PROFILED) + ["copyBuffer"])
+        wl = "" if args.workload == DEFAULT_WORKLOAD else f"--workload {args.workload} "
         cmds = [
             f"rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o inject -f csv -- "
-            "python -u bench.py --steps 20 --warmup 5 --no-cpu-baseline --no-e2e",
+            f"python -u bench.py {wl}--steps 20 --warmup 5 --no-cpu-baseline --no-e2e",
             f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"{regex}\" "
-            f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py --steps 3 --warmup 1 "
+            f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
             "--no-cpu-baseline --no-e2e",
             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"{regex}\" "
-            f"-T -d {write_dir} -o write -f csv -- python -u bench.py --steps 3 --warmup 1 "
+            f"-T -d {write_dir} -o write -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
             "--no-cpu-baseline --no-e2e",
             f"python bench.py --workload {args.workload} --summarize-profile {trace_dir} "
             f"{fetch_dir} {write_dir}",
