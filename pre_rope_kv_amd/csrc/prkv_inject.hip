@@ -48,6 +48,11 @@
 //    (v_cvt_pk_bf16_f32).
 //  - 16-byte nontemporal loads and stores; 64-bit addressing (one layer of
 //    a large cache exceeds 4 GiB).
+//  - With the mapping built on the device the token count is known only to
+//    the kernel: the host sizes the grid for an expected count (the store's
+//    mean fact length), the kernel covers more tokens by its grid stride and
+//    gives a small batch more splits; batches of up to 256 facts build the
+//    mapping inside this kernel (fused_plan below), one launch in all.
 
 #include <hip/hip_runtime.h>
 
