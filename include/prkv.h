@@ -253,9 +253,11 @@ int inject_device_workspace_bytes(int32_t max_facts, int64_t max_tokens, size_t*
  * Source: as build_slot_mapping and inject_topk (InferScale review, "If this
  * is right" bullet 2, KV-connector axiom of section 3.4, "What carries the
  * argument", "Referee Report" Summary).
- * Kernels on `stream`: when batch->max_facts <= 256 and n_req <= 256, one
- * launch (every inject workgroup maps its own tokens from the batch); larger
- * batches take three (plan, per-token mapping, inject).  Both fill the
+ * Kernels on `stream`: when batch->max_facts <= 256, n_req <= 256 and the
+ * expected token count (max_facts x the store's mean stored fact length,
+ * + 10 %) is <= 4096, one launch (every inject workgroup maps its own tokens
+ * from the batch); other batches take three (plan, per-token mapping,
+ * inject).  Both fill the
  * workspace and d_status identically.  The launch is sized for max_facts
  * facts of the store's mean stored length; any count up to max_tokens is
  * handled, a larger one with more work per workgroup.  Asynchronous, never

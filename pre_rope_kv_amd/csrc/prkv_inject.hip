@@ -51,8 +51,9 @@
 //  - With the mapping built on the device the token count is known only to
 //    the kernel: the host sizes the grid for an expected count (the store's
 //    mean fact length), the kernel covers more tokens by its grid stride and
-//    gives a small batch more splits; batches of up to 256 facts build the
-//    mapping inside this kernel (fused_plan below), one launch in all.
+//    gives a small batch more splits; small batches (up to 256 facts and
+//    ~4k tokens) build the mapping inside this kernel (fused_plan below),
+//    one launch in all.
 
 #include <hip/hip_runtime.h>
 
@@ -172,10 +173,11 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
 }
 
 // ---------------------------------------------------------------------------
-// Fused mapping for small batches (at most kFuseFacts facts and kFuseReqs
-// requests): every workgroup of the inject kernel rebuilds the batch plan in
-// LDS (one fact per thread) and maps its own tile's tokens, so the whole
-// device-side step is one launch instead of plan + mapping + inject.  The
+// Fused mapping for small batches (at most kFuseFacts facts, kFuseReqs
+// requests and kFuseTokens expected tokens): every workgroup of the inject
+// kernel rebuilds the batch plan in LDS (one fact per thread) and maps its
+// own tile's tokens, so the whole device-side step is one launch instead of
+// plan + mapping + inject.  The
 // plan, the per-token mapping and every status bit are exactly those of
 // plan_kernel and materialize_kernel below; workgroup 0 writes the plan and
 // the header to the workspace, and the workgroup with split 0 of each tile
@@ -184,6 +186,10 @@ __device__ __forceinline__ void flag(int32_t* status, int bits) {
 
 constexpr int kFuseFacts = kThreads;
 constexpr int kFuseReqs = kThreads;
+// Above ~4k expected tokens every workgroup rebuilding the plan costs more
+// than the two extra launches (measured on MI355X: fused 4 % faster at 50
+// facts / 1.9k tokens, 0.5-2 % slower from 100 facts / 3.8k tokens up).
+constexpr int64_t kFuseTokens = 4096;
 
 struct FusedLds {
   int64_t pos0[kFuseFacts];      // serving position of the fact's first token
@@ -996,7 +1002,7 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
     expect = std::min<int64_t>(b.max_tokens, int64_t(1.1 * mean * b.max_facts) + 1);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs)   // one launch
+  if (b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs && expect <= kFuseTokens)  // one launch
     return launch_inject(st, b.max_tokens, nullptr, nullptr, nullptr, nullptr, k_cache_layers,
                          v_cache_layers, block_size, num_blocks, d_status, s, &db, expect);
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);
