@@ -499,7 +499,7 @@ def main():
         k_sweep(args)
         return
     if args.gpus != 1 or world != 1:
-        print(f"bench.py: this build runs on one GPU only (asked for --gpus {args.gpus}, "
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "
               f"WORLD_SIZE {world}); the inject path needs no collective and shards by "
               "request, KV head or layer range with no exchange step.", file=sys.stderr)
         sys.exit(2)
