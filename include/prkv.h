@@ -27,8 +27,11 @@
  * Layouts
  *  - Store arenas (K and V separately): [L][capacity_rows][H][D] bf16,
  *    layer-major; a fact owns the same contiguous row range in every layer.
- *  - Paged cache, one K and one V tensor per layer:
- *    [num_blocks][block_size][H][D] bf16; slot = block * block_size + offset.
+ *  - Paged cache, one K and one V tensor per layer, slot = block *
+ *    block_size + offset, in one of two layouts (prkv_cache_layout):
+ *    NHD [num_blocks][block_size][H][D] bf16 (vLLM's paged layout: a slot's
+ *    heads are contiguous) or HND [num_blocks][H][block_size][D] bf16 (each
+ *    head's part of a block is contiguous).
  *  - RoPE: pair j (j = 0 .. D/2-1) is the complex number z_j = x_a + i x_b
  *    with (a, b) = (j, j + D/2) for half-split pairing (GPT-NeoX style) or
  *    (2j, 2j + 1) for interleaved pairing (GPT-J style); rotation to position
@@ -90,8 +93,19 @@ enum prkv_rope_scaling { PRKV_SCALING_NONE = 0, PRKV_SCALING_LLAMA3 = 1 };
  * already rounded to bf16 once. */
 enum prkv_key_layout { PRKV_KEYS_PRE_ROPE = 0, PRKV_KEYS_CHUNK_LOCAL = 1 };
 
+/* Element order inside one block of the paged cache (the same for every
+ * layer, K and V).  NHD: [block_size][H][D], the paged layout of vLLM that
+ * the InferScale review scatters into ("Referee Report", Summary); element
+ * (block b, offset o, head h, dim d) is at ((b * block_size + o) * H + h) * D
+ * + d.  HND: [H][block_size][D]; the same element is at ((b * H + h) *
+ * block_size + o) * D + d, so one head's keys of a block are contiguous
+ * (block_size * D * 2 bytes), which suits per-head attention reads.  Slots
+ * and block tables mean the same in both. */
+enum prkv_cache_layout { PRKV_CACHE_NHD = 0, PRKV_CACHE_HND = 1 };
+
 /* Shape of a store and of the model it serves.  Zero-initialised trailing
- * fields select the defaults (pre-RoPE keys, no frequency scaling). */
+ * fields select the defaults (pre-RoPE keys, no frequency scaling, NHD
+ * cache). */
 typedef struct prkv_store_desc {
   int32_t num_layers;    /* L, 1..128                                         */
   int32_t num_kv_heads;  /* H >= 1                                            */
@@ -107,7 +121,9 @@ typedef struct prkv_store_desc {
   double low_freq_factor;  /* LLAMA3: > 0                                     */
   double high_freq_factor; /* LLAMA3: > low_freq_factor                       */
   int32_t original_max_position; /* LLAMA3: W >= 1                            */
-  int32_t reserved_;     /* must be 0                                         */
+  int32_t cache_layout;  /* prkv_cache_layout of the paged caches this store
+                            injects into (inject_topk, inject_topk_device) and
+                            attend_paged reads                                 */
 } prkv_store_desc;
 
 typedef struct prkv_store prkv_store; /* opaque host-side store handle */
@@ -197,7 +213,9 @@ int build_slot_mapping(const prkv_store* st, int32_t n_req, const int32_t* req_f
  * float32 with compensated (hi/lo) cos/sin and rounded to nearest-even bf16.
  * d_src_row, d_pos, d_slot: device int32[n_tokens] (from build_slot_mapping).
  * k_cache_layers, v_cache_layers: HOST arrays of L device pointers, each a
- * [num_blocks][block_size][H][D] bf16 tensor.  d_status: optional device
+ * bf16 tensor of num_blocks blocks in the store's cache_layout
+ * ([num_blocks][block_size][H][D] for NHD, [num_blocks][H][block_size][D]
+ * for HND).  d_status: optional device
  * int32; if non-NULL the kernel ORs 1 (row out of range), 2 (position out of
  * range) or 4 (slot out of range) into it for any token it skipped; tokens
  * out of range are never read or written, and a row of -1 skips a token
@@ -310,9 +328,10 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
  * For every layer l, request r, query token i (position q_start[r] + i) and
  * query head h (KV head h / (num_q_heads / H)):
  *   out[l][r][i][h] = softmax_j(scale * <RoPE(q), K_l[j]>) V_l[j] over the
- *   positions j <= q_start[r] + i, K/V read from the paged cache through the
- *   request's block table (every such position must have been written:
- *   prefix, injected facts and the query's own K/V).
+ *   positions j <= q_start[r] + i, K/V read from the paged cache (in the
+ *   store's cache_layout) through the request's block table (every such
+ *   position must have been written: prefix, injected facts and the query's
+ *   own K/V).
  * q: pre-RoPE, rotated in the kernel with the store's table.  K and V of the
  * cache are bf16; q and the probabilities are carried as bf16 hi + lo pairs
  * into the matrix cores, so the result is accurate to fp32 rounding.

@@ -8,6 +8,10 @@
 // (injected KV at the intended positions is equivalent to prompt-injecting
 // the same tokens), reference [1] (grouped-query attention).
 //
+// The cache is NHD ([block][bs][H][D]: a key's head rows are 256 B apart
+// from those of the other heads) or HND ([block][H][bs][D]: one head's keys
+// of a block are contiguous); only the address of a key's row differs.
+//
 // Work unit: one workgroup per (layer, request, KV head).  Its rows are the
 // q_len query tokens x the `group` query heads sharing that KV head (at most
 // 64 rows, 16 per wave).  Keys stream in tiles of 32 positions through a
@@ -82,6 +86,7 @@ struct AttnParams {
   int32_t n_req, q_len, num_q_heads, num_kv_heads, group, rows;
   int32_t bt_stride, block_size, max_position;
   int32_t bs_shift;        // log2(block_size) when it is a power of two, else -1
+  int32_t hnd;             // cache layout HND ([block][H][bs][D]) instead of NHD
 };
 
 __device__ __forceinline__ bf16x8 load8(const unsigned char* p) {
@@ -304,8 +309,16 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       const int n = i * 4 + wave;
       const int k = n * RPI + lane / DC;
       const int pk = lane % DC;
-      const int sk = sl[k];
-      const int64_t off = int64_t(sk >= 0 ? sk : 0) * row_elems + g * D;
+      const int sk = sl[k] >= 0 ? sl[k] : 0;
+      // element offset of (slot sk, head g): NHD sk * H * D + g * D; HND
+      // (with sk = b * bs + o) ((sk - o) * H + o) * D + g * bs * D
+      int64_t off;
+      if (p.hnd) {
+        const int o = p.bs_shift >= 0 ? (sk & (p.block_size - 1)) : sk % p.block_size;
+        off = (int64_t(sk - o) * p.num_kv_heads + o) * D + int64_t(g) * p.block_size * D;
+      } else {
+        off = int64_t(sk) * row_elems + g * D;
+      }
       load_lds16(kl + off + 8 * (pk ^ swk(k)), kd + n * 1024);
       load_lds16(vl + off + 8 * (pk ^ swv(k)), vd + n * 1024);
     }
@@ -540,6 +553,7 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
   p.block_size = block_size;
   p.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(uint32_t(block_size)) : -1;
   p.max_position = d.max_position;
+  p.hnd = d.cache_layout == PRKV_CACHE_HND;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const hipError_t e = d.head_dim == 64 ? launch_attend<64>(p, kc, vc, grid, d.rope_style, s)
                                         : launch_attend<128>(p, kc, vc, grid, d.rope_style, s);

@@ -74,7 +74,8 @@ int validate_desc(const prkv_store_desc* d) {
   } else if (d->rope_scaling != PRKV_SCALING_NONE) {
     return fail(PRKV_ERR_INVALID_ARG, "rope_scaling %d unsupported", d->rope_scaling);
   }
-  if (d->reserved_ != 0) return fail(PRKV_ERR_INVALID_ARG, "reserved_ must be 0");
+  if (d->cache_layout != PRKV_CACHE_NHD && d->cache_layout != PRKV_CACHE_HND)
+    return fail(PRKV_ERR_INVALID_ARG, "cache_layout %d unsupported", d->cache_layout);
   const double heads_dim = double(d->num_kv_heads) * d->head_dim;
   if (heads_dim * d->capacity_rows * d->num_layers * 2.0 > 9.0e18)
     return fail(PRKV_ERR_INVALID_ARG, "arena size overflows");

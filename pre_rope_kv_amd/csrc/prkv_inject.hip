@@ -47,7 +47,10 @@
 //    (plus terms ~2^-48 |x|).  Rounding to bf16 is nearest-even
 //    (v_cvt_pk_bf16_f32).
 //  - 16-byte nontemporal loads and stores; 64-bit addressing (one layer of
-//    a large cache exceeds 4 GiB).
+//    a large cache exceeds 4 GiB).  The cache is NHD ([block][bs][H][D]: a
+//    token's K row is H * D contiguous elements, like the arena's) or HND
+//    ([block][H][bs][D]: each head's D elements land block_size * D apart);
+//    only the store address differs.
 //  - With the mapping built on the device the token count is known only to
 //    the kernel: the host sizes the grid for an expected count (the store's
 //    mean fact length), the kernel covers more tokens by its grid stride and
@@ -127,7 +130,20 @@ struct InjectParams {
   int32_t iters_per_split;   // 64-chunk iterations (layers when tpw > 1) per split
   int32_t tpw;               // tokens per wave: 64 / (H * D/16) when that divides 64, else 1
   int32_t want_waves;        // waves that cover the chip
+  int32_t block_size;
+  int32_t hnd;               // cache layout HND ([block][H][bs][D]) instead of NHD
 };
+
+// Element offset of (slot, head 0, dim 0) in a layer's cache, and the
+// distance between consecutive heads of one slot.  NHD [block][bs][H][D]:
+// slot * H * D and D.  HND [block][H][bs][D]: with slot = b * bs + o,
+// (b * H * bs + o) * D = ((slot - o) * H + o) * D and bs * D.
+template <int D>
+__device__ __forceinline__ int64_t cache_slot_base(const InjectParams& p, int slot) {
+  if (!p.hnd) return int64_t(slot) * p.num_heads * D;
+  const int o = slot % p.block_size;
+  return (int64_t(slot - o) * p.num_heads + o) * D;
+}
 
 // Half-split pairing: lo holds x1 of pairs 0..7, hi holds x2 of pairs 0..7.
 __device__ __forceinline__ void rotate8(u32x4& lo, u32x4& hi, const f32x4 (&cs)[8]) {
@@ -370,6 +386,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
   if (it1 > max_it) it1 = max_it;
   const int64_t row_elems = int64_t(H) * D;
   const int64_t layer_elems = p.capacity_rows * row_elems;
+  const int64_t head_stride = p.hnd ? int64_t(p.block_size) * D : D;  // in the cache
 
   for (int64_t tile = first_tile; tile < n_tiles; tile += tile_stride) {
     const int64_t tok0 = tile * tile_tokens;
@@ -426,7 +443,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
       for (int k = 0; k < 8; ++k) cs[k] = smem[j * HALF + k * CPH + c];
       const int64_t in_row = int64_t(h) * D + c * 8;
       const int64_t a0 = int64_t(row) * row_elems + in_row;
-      const int64_t s0 = int64_t(slot) * row_elems + in_row;
+      const int64_t s0 = cache_slot_base<D>(p, slot) + int64_t(h) * head_stride + c * 8;
       if (row >= 0) {
         for (int l0 = it0; l0 < it1; l0 += kUnroll) {
           u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
@@ -462,6 +479,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     const int row = __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
     if (row >= 0) {
       const int slot = __builtin_amdgcn_readfirstlane(meta[3 * wave + 2]);
+      const int64_t slot_base = cache_slot_base<D>(p, slot);
 
       f32x4 cs[8];
 #pragma unroll
@@ -481,7 +499,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
           const int h = r / CPH;
           lay[u] = l;
           const int64_t in_row = int64_t(h) * D + c * 8;
-          soff[u] = int64_t(slot) * row_elems + in_row;
+          soff[u] = slot_base + int64_t(h) * head_stride + c * 8;
           if (live[u]) {
             const int64_t aoff = int64_t(l) * layer_elems + int64_t(row) * row_elems + in_row;
             ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_arena + aoff));
@@ -788,6 +806,8 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   p.iters_per_split = per;
   p.tpw = tpw;
   p.want_waves = int32_t(want_waves);
+  p.block_size = block_size;
+  p.hnd = d.cache_layout == PRKV_CACHE_HND;
 
   hipError_t e;
   switch (D) {

@@ -47,7 +47,7 @@ class DeviceWorkload:
         self.desc = prkv.desc(sp.num_layers, sp.num_kv_heads, sp.head_dim, w.max_facts,
                               w.capacity_rows, sp.max_position, sp.rope_theta,
                               rope_style=sp.rope_style, key_layout=sp.key_layout,
-                              llama3_scaling=sp.llama3_scaling)
+                              llama3_scaling=sp.llama3_scaling, cache_layout=sp.cache_layout)
         arena_bytes, rope_bytes = prkv.store_required_bytes(self.desc)
         shape = (sp.num_layers, w.capacity_rows, sp.num_kv_heads, sp.head_dim)
         self.store_location = store_location
@@ -66,7 +66,11 @@ class DeviceWorkload:
         self.store = prkv.store_create(self.desc, self.k_arena, self.v_arena, self.rope,
                                        stream=self.stream)
         self._put_all()
-        cshape = (sp.num_layers, w.num_blocks, sp.block_size, sp.num_kv_heads, sp.head_dim)
+        self.hnd = sp.cache_layout == prkv.CACHE_HND
+        if self.hnd:   # [L][block][H][bs][D]
+            cshape = (sp.num_layers, w.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim)
+        else:          # [L][block][bs][H][D]
+            cshape = (sp.num_layers, w.num_blocks, sp.block_size, sp.num_kv_heads, sp.head_dim)
         self.k_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
         self.v_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
         self.reset_cache()
@@ -196,11 +200,34 @@ class DeviceWorkload:
 
     # -- reading back ------------------------------------------------------
     def listed_blocks_host(self, blocks):
-        """K and V cache contents of the given blocks, all layers, as uint16 numpy."""
+        """K and V cache contents of the given blocks, all layers, as uint16
+        numpy [L][n][block_size][H][D] whatever the cache layout."""
         idx = torch.as_tensor(blocks, dtype=torch.long, device=self.device)
-        k = self.k_cache.index_select(1, idx).cpu().numpy().view(np.uint16)
-        v = self.v_cache.index_select(1, idx).cpu().numpy().view(np.uint16)
-        return k, v
+        out = []
+        for cache in (self.k_cache, self.v_cache):
+            sel = cache.index_select(1, idx)
+            if self.hnd:
+                sel = sel.permute(0, 1, 3, 2, 4).contiguous()
+            out.append(sel.cpu().numpy().view(np.uint16))
+        return tuple(out)
+
+    def slot_rows(self, cache, slots):
+        """Rows of the given slots (device int64 tensor), all layers and heads:
+        a device tensor [L][n][H][D] whatever the cache layout."""
+        bs = self.w.spec.block_size
+        if not self.hnd:
+            sp = self.w.spec
+            return cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)[:, slots]
+        # advanced indices around a slice: the result is [n][L][H][D]
+        return cache[:, slots // bs, :, slots % bs].permute(1, 0, 2, 3)
+
+    def set_slot_row(self, cache, layer, slot, value):
+        """Write one slot's [H][D] row of one layer."""
+        bs = self.w.spec.block_size
+        if self.hnd:
+            cache[layer, slot // bs, :, slot % bs] = value
+        else:
+            cache[layer, slot // bs, slot % bs] = value
 
     def count_non_sentinel(self, chunk_elems=1 << 28):
         """Number of cache elements (K and V, all layers) != the sentinel."""

@@ -55,7 +55,7 @@ class StoreDesc(ctypes.Structure):
         ("low_freq_factor", ctypes.c_double),
         ("high_freq_factor", ctypes.c_double),
         ("original_max_position", ctypes.c_int32),
-        ("reserved_", ctypes.c_int32),
+        ("cache_layout", ctypes.c_int32),
     ]
 
 
@@ -184,15 +184,18 @@ def _i32(a):
 ROPE_HALF_SPLIT, ROPE_INTERLEAVED = 0, 1
 SCALING_NONE, SCALING_LLAMA3 = 0, 1
 KEYS_PRE_ROPE, KEYS_CHUNK_LOCAL = 0, 1
+CACHE_NHD, CACHE_HND = 0, 1
 
 
 def desc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows, max_position,
-         rope_theta, rope_style=ROPE_HALF_SPLIT, key_layout=KEYS_PRE_ROPE, llama3_scaling=None):
+         rope_theta, rope_style=ROPE_HALF_SPLIT, key_layout=KEYS_PRE_ROPE, llama3_scaling=None,
+         cache_layout=CACHE_NHD):
     """prkv_store_desc.  llama3_scaling: None or (factor, low_freq_factor,
     high_freq_factor, original_max_position)."""
     d = StoreDesc(num_layers, num_kv_heads, head_dim, max_facts, capacity_rows,
                   max_position, rope_style, float(rope_theta))
     d.key_layout = key_layout
+    d.cache_layout = cache_layout
     if llama3_scaling is not None:
         factor, lo, hi, w = llama3_scaling
         d.rope_scaling = SCALING_LLAMA3

@@ -57,6 +57,7 @@ class Spec:
     rope_style: int = 0       # 0 half-split pairs, 1 interleaved pairs
     llama3_scaling: tuple = None  # (factor, low, high, original max position) or None
     key_layout: int = 0       # 0 pre-RoPE keys, 1 keys rotated at chunk-local positions
+    cache_layout: int = 0     # 0 NHD [block][bs][H][D], 1 HND [block][H][bs][D]
 
     @property
     def row_bytes(self):

@@ -39,6 +39,7 @@ prkv_store_desc random_desc(std::mt19937& rng, bool valid) {
   d.rope_style = u(rng) % 2;
   d.rope_theta = 10000.0;
   d.key_layout = u(rng) % 2;
+  d.cache_layout = u(rng) % 2;
   if (u(rng) % 2) {
     d.rope_scaling = PRKV_SCALING_LLAMA3;
     d.scaling_factor = 8.0;
@@ -55,7 +56,7 @@ prkv_store_desc random_desc(std::mt19937& rng, bool valid) {
       case 4: d.rope_style = 7; break;
       case 5: d.rope_theta = 0.5; break;
       case 6: d.rope_scaling = 1; d.high_freq_factor = 0.5; break;
-      default: d.reserved_ = 1; break;
+      default: d.cache_layout = 2; break;
     }
   }
   return d;

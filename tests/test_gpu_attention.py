@@ -83,20 +83,20 @@ def from_cache(dw, q_bits, q_len, layers):
     """Oracle attention over the GPU cache's own K/V (isolates the kernel)."""
     sp = dw.w.spec
     out = np.zeros((len(layers), sp.n_requests, q_len, q_bits.shape[2], sp.head_dim))
-    kf = dw.k_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
-    vf = dw.v_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
     for r, ids in enumerate(dw.w.retrieved):
         ctx = sum(dw.w.length_of(f) for f in ids)
         bt = dw.w.block_tables[r]
         slots = torch.as_tensor([int(bt[p // sp.block_size]) * sp.block_size + p % sp.block_size
-                                 for p in range(ctx)], device=kf.device)
+                                 for p in range(ctx)], device=dw.device)
+        kr = dw.slot_rows(dw.k_cache, slots)   # [L][ctx][H][D] in either cache layout
+        vr = dw.slot_rows(dw.v_cache, slots)
         pos = np.arange(ctx)
         q_pos = np.arange(ctx - q_len, ctx)
         q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r]), q_pos[:, None], sp.rope_theta,
                             **rope_kwargs(sp))
         for li, l in enumerate(layers):
-            kk = bf16.bf16_bits_to_f64(kf[l, slots].cpu().numpy().view(np.uint16))
-            vv = bf16.bf16_bits_to_f64(vf[l, slots].cpu().numpy().view(np.uint16))
+            kk = bf16.bf16_bits_to_f64(kr[l].cpu().numpy().view(np.uint16))
+            vv = bf16.bf16_bits_to_f64(vr[l].cpu().numpy().view(np.uint16))
             out[li, r] = attention.causal_gqa(q_rot, q_pos, kk, vv, pos,
                                                1.0 / math.sqrt(sp.head_dim))
     return out

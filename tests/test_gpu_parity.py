@@ -215,11 +215,9 @@ def test_tiny_with_attention_equivalence(path):
             img_v.row(0, s)[...] = v
 
     def prior_gpu(dw):
-        flat_k = dw.k_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
-        flat_v = dw.v_cache.view(sp.num_layers, -1, sp.num_kv_heads, sp.head_dim)
         for s, k, v in prior:
-            flat_k[0, s] = torch.from_numpy(k.view(np.int16)).to(flat_k.device)
-            flat_v[0, s] = torch.from_numpy(v.view(np.int16)).to(flat_v.device)
+            dw.set_slot_row(dw.k_cache, 0, s, torch.from_numpy(k.view(np.int16)).to(dw.device))
+            dw.set_slot_row(dw.v_cache, 0, s, torch.from_numpy(v.view(np.int16)).to(dw.device))
 
     dw, rep, (img_k, img_v, gk, gv) = run_full(w, gen_device="cpu", prior_gpu=prior_gpu,
                                                prior_img=prior_img, path=path)
@@ -307,8 +305,6 @@ def _full_size(name, n_sample_tokens, seed, path="host", **variant):
     pos = np.asarray(paged.rotation_positions(w.requests(), w.fact_rows, is_chunk_local(spec)))
     assert np.array_equal(dw.d_map[2].cpu().numpy(), slot)
     L, H, D = spec.num_layers, spec.num_kv_heads, spec.head_dim
-    kflat = dw.k_cache.view(L, -1, H, D)
-    vflat = dw.v_cache.view(L, -1, H, D)
     # V for every token: device gather at the oracle's slots vs regenerated facts
     t0 = 0
     sample = set(np.random.default_rng(seed).choice(len(src), n_sample_tokens, replace=False))
@@ -318,14 +314,14 @@ def _full_size(name, n_sample_tokens, seed, path="host", **variant):
             ln = w.length_of(f)
             k, v = w.fact_kv(f, device="cuda")
             s = torch.as_tensor(slot[t0:t0 + ln], dtype=torch.long, device="cuda")
-            assert torch.equal(vflat[:, s], v), f"V differs for fact {f}"
+            assert torch.equal(dw.slot_rows(dw.v_cache, s), v), f"V differs for fact {f}"
             picks = [t for t in range(ln) if t0 + t in sample]
             if picks:
                 kk = k[:, picks].cpu().numpy().view(np.uint16)          # [L][n][H][D]
                 pp = pos[t0 + np.array(picks)]
                 k_want.append(inject.rotate_k_bits(kk, pp[None, :, None], spec.rope_theta,
                                                    **rope_kwargs(spec)))
-                k_got.append(kflat[:, s[picks]].cpu().numpy().view(np.uint16))
+                k_got.append(dw.slot_rows(dw.k_cache, s[picks]).cpu().numpy().view(np.uint16))
             t0 += ln
     assert t0 == len(src)
     got = np.concatenate(k_got, axis=1)

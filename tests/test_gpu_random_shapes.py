@@ -1,6 +1,7 @@
 """GPU parity on seeded random combinations of store shape and options: layer
 count, KV heads, head_dim, pairing, Llama 3.1 frequency rule, chunk-local
-keys, block size, facts and requests drawn together, so that combinations
+keys, cache layout (NHD or HND), block size, facts and requests drawn
+together, so that combinations
 no hand-written case names (several options on a row narrower than a wave,
 a fused device mapping on a ragged head count...) meet the oracle.  Same bar
 as every parity test: V and untouched slots bit-exact, K within 2 bf16 ulp
@@ -35,7 +36,8 @@ def test_random_shape_and_options(seed):
                         theta=float(rng.choice([1e4, 5e5])), num_blocks=2048)
     options = dict(rope_style=int(rng.integers(0, 2)),
                    llama3_scaling=LLAMA31 if rng.integers(0, 2) else None,
-                   key_layout=int(rng.integers(0, 2)))
+                   key_layout=int(rng.integers(0, 2)),
+                   cache_layout=int(rng.integers(0, 2)))
     w = dataclasses.replace(w, spec=dataclasses.replace(w.spec, **options))
     assert options["rope_style"] in (prkv.ROPE_HALF_SPLIT, prkv.ROPE_INTERLEAVED)
     path = "device" if seed % 2 else "host"

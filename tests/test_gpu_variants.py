@@ -6,10 +6,14 @@ Variants (each a store-descriptor option, the kernels' arithmetic unchanged):
   chunk_local   the store holds keys already rotated at positions 0 .. len-1 of
                 their fact; injection relocates them by R(s), s = the fact's
                 serving start (Theorem 6's axiom R_a^T R_b = R_{b-a})
+  hnd           paged cache blocks laid out [H][block_size][D] instead of
+                [block_size][H][D] (slots and block tables unchanged; the
+                comparison reads the cache back in the logical slot order)
 Same bar as the base path: V and untouched slots bit-exact, K within 2 bf16
 ulp with mean error < 1e-3, the device-built mapping bit-equal to the
 oracle's.  Attention is checked with the interleaved and scaled tables (the
-query is rotated in-kernel with the store's pairing and frequencies).
+query is rotated in-kernel with the store's pairing and frequencies) and over
+an HND cache.
 """
 
 import numpy as np
@@ -18,7 +22,8 @@ import pytest
 from pre_rope_kv_amd import prkv, workloads
 
 import test_gpu_attention as att
-from test_gpu_parity import _full_size, _release_device_memory, run_full  # noqa: F401
+from test_gpu_parity import (EDGE, _full_size, _release_device_memory,  # noqa: F401
+                             custom_workload, run_full)
 
 pytestmark = pytest.mark.gpu
 
@@ -29,6 +34,7 @@ VARIANTS = {
     "chunk_local": dict(key_layout=prkv.KEYS_CHUNK_LOCAL),
     "all_three": dict(rope_style=prkv.ROPE_INTERLEAVED, llama3_scaling=LLAMA31,
                       key_layout=prkv.KEYS_CHUNK_LOCAL),
+    "hnd": dict(cache_layout=prkv.CACHE_HND),
 }
 
 
@@ -53,11 +59,41 @@ def test_variant_llama8b_k50_interleaved_scaled():
     run_full(w, path="device")
 
 
+def test_variant_llama8b_k50_hnd():
+    run_full(variant_workload("llama3_8b_k50", "hnd"), path="device")
+
+
 def test_variant_batch64_full_size_sampled():
     _full_size("llama3_8b_batch64_k50", 256, seed=5, path="device", **VARIANTS["all_three"])
 
 
-@pytest.mark.parametrize("variant", ["interleaved", "llama31"])
+def test_variant_batch64_full_size_sampled_hnd():
+    _full_size("llama3_8b_batch64_k50", 256, seed=6, path="device", **VARIANTS["hnd"])
+
+
+def test_variant_llama70b_full_size_sampled_hnd():
+    # block size 32, fact starts that straddle blocks
+    _full_size("llama3_70b_batch16_k50", 128, seed=7, path="device", **VARIANTS["hnd"])
+
+
+HND_EDGE = ["prefix0_len1", "len256_straddle_bs32", "dup_fact_in_request", "h1_d64", "h1_d16",
+            "h1_d512", "h3_d128", "h2_d1024", "bs1", "250_facts"]
+
+
+@pytest.mark.parametrize("path", ["host", "device"])
+@pytest.mark.parametrize("name", HND_EDGE)
+def test_hnd_edge_case(name, path):
+    _, L, H, D, bs, facts, reqs = next(c for c in EDGE if c[0] == name)
+    nb = 2048 if name == "250_facts" else 512
+    w = custom_workload(name + "_hnd", L, H, D, bs, facts, reqs, theta=5e5, num_blocks=nb)
+    w = workloads.dataclasses.replace(
+        w, spec=workloads.dataclasses.replace(w.spec, **VARIANTS["hnd"]))
+    dw, rep, _ = run_full(w, gen_device="cuda", path=path)
+    assert dw.hnd
+    assert dw.count_non_sentinel() == 2 * L * w.n_tokens * H * D
+
+
+@pytest.mark.parametrize("variant", ["interleaved", "llama31", "hnd"])
 @pytest.mark.parametrize("D", [64, 128])
 def test_variant_attention(variant, D):
     rng = np.random.default_rng(D)
@@ -67,5 +103,19 @@ def test_variant_attention(variant, D):
     w.spec = workloads.dataclasses.replace(w.spec, **VARIANTS[variant])
     q_len, hq = 8, 8
     dw, q_bits, got, layers = att.run_attention(w, q_len, hq, gen="cpu")
+    assert int(dw.status.item()) == 0
+    att.check(dw, q_bits, got, q_len, hq, layers, "cpu")
+
+
+@pytest.mark.parametrize("bs,D,q_len,hq", [(24, 128, 16, 32), (12, 64, 4, 4), (32, 128, 16, 32)])
+def test_hnd_attention_block_sizes(bs, D, q_len, hq):
+    # block sizes that are and are not powers of two, over an HND cache
+    rng = np.random.default_rng(bs * D)
+    lens = [rng.integers(5, 60, size=7), rng.integers(5, 60, size=3)]
+    w = att.context_workload(f"attn_hnd_{bs}_{D}", 2, hq // 4, D, bs, 30,
+                             lens, q_len=q_len, n_req=2, seed=bs + D)
+    w.spec = workloads.dataclasses.replace(w.spec, **VARIANTS["hnd"])
+    dw, q_bits, got, layers = att.run_attention(w, q_len, hq, gen="cpu")
+    assert dw.hnd
     assert int(dw.status.item()) == 0
     att.check(dw, q_bits, got, q_len, hq, layers, "cpu")

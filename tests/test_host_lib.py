@@ -66,7 +66,7 @@ LLAMA31 = (8.0, 1.0, 4.0, 8192)
     dict(key_layout=2), dict(llama3_scaling=(0.5, 1.0, 4.0, 8192)),
     dict(llama3_scaling=(8.0, 4.0, 1.0, 8192)), dict(llama3_scaling=(8.0, 0.0, 4.0, 8192)),
     dict(llama3_scaling=(8.0, 1.0, 4.0, 0)), dict(llama3_scaling=(float("inf"), 1.0, 4.0, 8192)),
-    dict(raw=("rope_scaling", 2)), dict(raw=("reserved_", 1)),
+    dict(raw=("rope_scaling", 2)), dict(raw=("cache_layout", 2)),
 ])
 def test_bad_descriptor(bad):
     raw = bad.pop("raw", None)
