@@ -16,8 +16,11 @@ query is rotated in-kernel with the store's pairing and frequencies) and over
 an HND cache.
 """
 
+import gc
+
 import numpy as np
 import pytest
+import torch
 
 from pre_rope_kv_amd import prkv, workloads
 
@@ -119,3 +122,20 @@ def test_hnd_attention_block_sizes(bs, D, q_len, hq):
     assert dw.hnd
     assert int(dw.status.item()) == 0
     att.check(dw, q_bits, got, q_len, hq, layers, "cpu")
+
+
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k5"])
+def test_hnd_cache_equals_nhd_cache(name):
+    # only addresses differ between the layouts: read back in slot order,
+    # the two caches are bit-identical (K included)
+    got = []
+    for variant in (None, "hnd"):
+        w = workloads.make(name) if variant is None else variant_workload(name, variant)
+        dw, _, _ = run_full(w, gen_device="cpu" if name.startswith("tiny") else "cuda",
+                            path="device")
+        got.append(dw.listed_blocks_host(w.listed_blocks()))
+        del dw
+        gc.collect()
+        torch.cuda.empty_cache()
+    (k0, v0), (k1, v1) = got
+    assert np.array_equal(k0, k1) and np.array_equal(v0, v1)
