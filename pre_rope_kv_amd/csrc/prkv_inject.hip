@@ -420,7 +420,37 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     }
     __syncthreads();
 
-    // 2. Stage each token's cos/sin row in LDS, ordered so that lane c reads
+    // 2. One token per wave: the wave's first layer group is loaded now,
+    //    before the cos/sin staging below, so both loads are in flight
+    //    together (the K/V rows need only the arena row).
+    u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
+    int lay[kUnroll], hd[kUnroll];
+    bool live[kUnroll];
+    const int wrow = MULTI ? -1 : __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
+    auto load_group = [&](int it) {
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) {
+        const int e = (it + u) * kWave + lane;
+        live[u] = (it + u) < it1 && e < total;
+        const int l = e / nc;
+        const int r = e - l * nc;
+        lay[u] = l;
+        hd[u] = r / CPH;
+        if (live[u]) {
+          const int64_t aoff = int64_t(l) * layer_elems + int64_t(wrow) * row_elems +
+                               int64_t(hd[u]) * D + c * 8;
+          ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_arena + aoff));
+          kb[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(p.k_arena + aoff + HALF));
+          va[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v_arena + aoff));
+          vb[u] = __builtin_nontemporal_load(
+              reinterpret_cast<const u32x4*>(p.v_arena + aoff + HALF));
+        }
+      }
+    };
+    if (!MULTI && wrow >= 0 && it0 < it1) load_group(it0);
+
+    // 3. Stage each token's cos/sin row in LDS, ordered so that lane c reads
     //    its 8 pairs at k*CPH + c (pair_slot).
     for (int e = threadIdx.x; e < tile_tokens * HALF; e += kThreads) {
       const int i = e / HALF, j = e - (e / HALF) * HALF;
@@ -430,7 +460,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     }
     __syncthreads();
 
-    // 3a. Rows narrower than a wave (H * D/16 < 64 chunks): the wave covers
+    // 4a. Rows narrower than a wave (H * D/16 < 64 chunks): the wave covers
     //     tpw consecutive tokens of the tile, one layer per iteration, so its
     //     loads and stores cover whole consecutive rows.
     if constexpr (MULTI) {
@@ -474,7 +504,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
         }
       }
     } else {
-    // 3b. Otherwise each wave streams its one token through every layer of
+    // 4b. Otherwise each wave streams its one token through every layer of
     //     its split.
     const int row = __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
     if (row >= 0) {
@@ -486,37 +516,15 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
       for (int k = 0; k < 8; ++k) cs[k] = smem[wave * HALF + k * CPH + c];
 
       for (int it = it0; it < it1; it += kUnroll) {
-        u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
-        int64_t soff[kUnroll];
-        int lay[kUnroll];
-        bool live[kUnroll];
-#pragma unroll
-        for (int u = 0; u < kUnroll; ++u) {
-          const int e = (it + u) * kWave + lane;
-          live[u] = (it + u) < it1 && e < total;
-          const int l = e / nc;
-          const int r = e - l * nc;
-          const int h = r / CPH;
-          lay[u] = l;
-          const int64_t in_row = int64_t(h) * D + c * 8;
-          soff[u] = slot_base + int64_t(h) * head_stride + c * 8;
-          if (live[u]) {
-            const int64_t aoff = int64_t(l) * layer_elems + int64_t(row) * row_elems + in_row;
-            ka[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.k_arena + aoff));
-            kb[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(p.k_arena + aoff + HALF));
-            va[u] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(p.v_arena + aoff));
-            vb[u] = __builtin_nontemporal_load(
-                reinterpret_cast<const u32x4*>(p.v_arena + aoff + HALF));
-          }
-        }
+        if (it != it0) load_group(it);
 #pragma unroll
         for (int u = 0; u < kUnroll; ++u) {
           if (!live[u]) continue;
           if (STYLE == PRKV_ROPE_HALF_SPLIT) rotate8(ka[u], kb[u], cs);
           else rotate8_interleaved(ka[u], kb[u], cs);
-          uint16_t* kd = kc.p[lay[u]] + soff[u];
-          uint16_t* vd = vc.p[lay[u]] + soff[u];
+          const int64_t soff = slot_base + int64_t(hd[u]) * head_stride + c * 8;
+          uint16_t* kd = kc.p[lay[u]] + soff;
+          uint16_t* vd = vc.p[lay[u]] + soff;
           __builtin_nontemporal_store(ka[u], reinterpret_cast<u32x4*>(kd));
           __builtin_nontemporal_store(kb[u], reinterpret_cast<u32x4*>(kd + HALF));
           __builtin_nontemporal_store(va[u], reinterpret_cast<u32x4*>(vd));
