@@ -50,6 +50,8 @@ def parse():
                     help="skip timing the same batch with every request's facts reordered")
     ap.add_argument("--pool-requests", type=int, default=8,
                     help="requests in the sample of the multi-core CPU-oracle baseline (0: skip)")
+    ap.add_argument("--no-other-workloads", action="store_true",
+                    help="skip the step and kernel timings of the other workloads")
     ap.add_argument("--no-attend", action="store_true",
                     help="skip timing the query-prefill attention over the injected cache")
     ap.add_argument("--no-retrieve", action="store_true",
@@ -477,6 +479,62 @@ def k_sweep(args):
                       "sweep": rows}), flush=True)
 
 
+def other_workloads(args, torch, lib, names):
+    """Device step and inject kernel alone on each of `names` (after the main
+    workload's memory is released): tokens/s of the step, algorithmic GB/s of
+    the kernel.  Back-to-back launches, events around args.steps of each."""
+    import gc
+
+    from pre_rope_kv_amd import harness, prkv, workloads
+
+    rows = {}
+    for name in names:
+        spec = workloads.SPECS[name]
+        if args.cache_layout == "hnd":
+            spec = workloads.dataclasses.replace(spec, cache_layout=prkv.CACHE_HND)
+        w0 = workloads.make(spec)
+        nb = harness.fit_num_blocks(spec, 2 * w0.capacity_rows * spec.num_layers *
+                                    spec.row_bytes + (1 << 30))
+        w = w0 if nb == spec.num_blocks else workloads.make(spec, num_blocks=nb)
+        dw = harness.DeviceWorkload(w)
+        dw.setup_device_batch()
+        stream = dw.stream
+
+        def time_fn(fn, a):
+            for _ in range(args.warmup):
+                rc = fn(*a)
+                if rc != 0:
+                    raise prkv.PrkvError(rc, fn.__name__, lib.last_error_string().decode())
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for _ in range(args.steps):
+                fn(*a)
+            e1.record(stream)
+            torch.cuda.synchronize()
+            assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
+            return e0.elapsed_time(e1) / args.steps
+
+        step_ms = time_fn(lib.inject_topk_device, dw.inject_device_args())
+        kernel_ms = time_fn(lib.inject_topk, dw.inject_args())
+        alg = dw.n_tokens * spec.bytes_per_token
+        profiled = w is w0 and args.cache_layout == "nhd"
+        rows[name] = {
+            "tokens": dw.n_tokens, "layers": spec.num_layers, "requests": spec.n_requests,
+            "k": spec.k, "block_size": spec.block_size, "num_blocks": w.num_blocks,
+            "step_ms": step_ms, "tokens_per_s": dw.n_tokens / (step_ms * 1e-3),
+            "kernel_ms": kernel_ms, "hbm_gbps": alg / (kernel_ms * 1e-3) / 1e9,
+            "frac_of_peak": alg / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+            "traffic": read_profile_traffic(name) if profiled else None,
+            "bytes_per_launch": alg,
+        }
+        del dw, w, w0
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+    return rows
+
+
 def main():
     args = parse()
     if args.summarize_profile:
@@ -485,13 +543,14 @@ def main():
         wl = "" if args.workload == DEFAULT_WORKLOAD else f"--workload {args.workload} "
         cmds = [
             f"rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o inject -f csv -- "
-            f"python -u bench.py {wl}--steps 20 --warmup 5 --no-cpu-baseline --no-e2e",
+            f"python -u bench.py {wl}--steps 20 --warmup 5 --no-cpu-baseline --no-e2e "
+            "--no-other-workloads",
             f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
-            "--no-cpu-baseline --no-e2e",
+            "--no-cpu-baseline --no-e2e --no-other-workloads",
             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {write_dir} -o write -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
-            "--no-cpu-baseline --no-e2e",
+            "--no-cpu-baseline --no-e2e --no-other-workloads",
             f"python bench.py --workload {args.workload} --summarize-profile {trace_dir} "
             f"{fetch_dir} {write_dir}",
         ]
@@ -744,6 +803,19 @@ def main():
         if args.pool_requests > 0:
             cpu_pool = cpu_baseline_pool(w, args.pool_requests)
 
+    others = None
+    if not args.no_other_workloads and args.store == "device" and not args.flush:
+        # the main workload's device memory goes first (the 64-request cache
+        # alone takes most of HBM)
+        import gc
+        del dw, kargs, dargs
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        names = [n for n in ("tiny_L1_H2_D64", "llama3_8b_k5", "llama3_8b_k50",
+                             "llama3_8b_batch64_k50", "llama3_70b_batch16_k50") if n != spec.name]
+        others = other_workloads(args, torch, lib, names)
+
     out = {
         "metric": METRIC,
         "value": n_tok * args.steps / (ms_per_step * args.steps * 1e-3),
@@ -795,6 +867,7 @@ def main():
         "graph_replay": graph,
         "retrieval": retrieval,
         "attention": attn,
+        "other_workloads": others,
         "e2e": e2e,
         "setup_s": setup_s,
         "timing": "per-launch events after a 1 GiB MALL flush" if args.flush
