@@ -218,3 +218,65 @@ def test_attention_query_positions_out_of_range_are_reported():
     assert int(dw.status.item()) == 2
     assert np.all(got[:, :2] == 0)
     assert np.array_equal(got[:, 2], ref[:, 2])
+
+
+@pytest.mark.parametrize("name,n_pairs", [("llama3_8b_batch64_k50", 24),
+                                          ("llama3_70b_batch16_k50", 16)])
+def test_attention_full_size_sampled(name, n_pairs):
+    """The launch the bench times: the whole batch injected by the device
+    path into a zeroed cache, then one attend_paged over every request's
+    whole context (16 query tokens = the context's last 16 positions, 4 query
+    heads per KV head, all layers); sampled (layer, request) outputs against
+    the oracle's attention over the same cache contents."""
+    spec = workloads.SPECS[name]
+    w0 = workloads.make(spec)
+    nb = harness.fit_num_blocks(spec, 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes +
+                                (3 << 30))
+    w = w0 if nb == spec.num_blocks else workloads.make(spec, num_blocks=nb)
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    dw.setup_device_batch()
+    dw.k_cache.zero_()
+    dw.v_cache.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    q_len, hq, D, L = 16, 4 * spec.num_kv_heads, spec.head_dim, spec.num_layers
+    ctxs = [int(w.prefix[r]) + sum(w.length_of(f) for f in ids)
+            for r, ids in enumerate(w.retrieved)]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(17)
+    q_bits = torch.randn((spec.n_requests, q_len, hq, D), generator=g) \
+        .to(torch.bfloat16).view(torch.int16)
+    q_start = torch.as_tensor([c - q_len for c in ctxs], dtype=torch.int32, device="cuda")
+    out = torch.full((L, spec.n_requests, q_len, hq, D), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    batch = prkv.attn_batch(spec.n_requests, q_len, hq, dw.d_bt.shape[1], q_bits.cuda(), q_start,
+                            dw.d_bt, dw.d_bt_len, out)
+    dw.status.zero_()
+    prkv.attend_paged(dw.store, batch, dw.k_layers(), dw.v_layers(), spec.block_size,
+                      w.num_blocks, 1.0 / math.sqrt(D), d_status=dw.status)
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    assert bool(torch.isfinite(out).all())
+    rng = np.random.default_rng(len(name))
+    pairs = {(int(rng.integers(0, L)), int(rng.integers(0, spec.n_requests)))
+             for _ in range(n_pairs)}
+    worst = 0.0
+    for l, r in sorted(pairs):
+        ctx = ctxs[r]
+        bt = w.block_tables[r]
+        slots = torch.as_tensor([int(bt[p // spec.block_size]) * spec.block_size +
+                                 p % spec.block_size for p in range(ctx)], device=dw.device)
+        kk = bf16.bf16_bits_to_f64(dw.slot_rows(dw.k_cache, slots)[l].cpu().numpy()
+                                   .view(np.uint16))
+        vv = bf16.bf16_bits_to_f64(dw.slot_rows(dw.v_cache, slots)[l].cpu().numpy()
+                                   .view(np.uint16))
+        q_pos = np.arange(ctx - q_len, ctx)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r].numpy().view(np.uint16)),
+                            q_pos[:, None], spec.rope_theta, **rope_kwargs(spec))
+        want = attention.causal_gqa(q_rot, q_pos, kk, vv, np.arange(ctx), 1.0 / math.sqrt(D))
+        got = out[l, r].cpu().numpy().astype(np.float64)
+        worst = max(worst, float(np.max(np.abs(got - want))))
+    _say(f"{name}: {len(pairs)} (layer, request) pairs, max |gpu - oracle over gpu cache| "
+         f"= {worst:.3g}")
+    assert worst <= TOL_SAME_CACHE
