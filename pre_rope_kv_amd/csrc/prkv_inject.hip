@@ -213,6 +213,8 @@ struct FusedLds {
   int32_t row0[kFuseFacts];
   int32_t req[kFuseFacts];
   int32_t reqptr[kFuseReqs + 1];
+  int32_t start[kFuseReqs];      // per request: prefix length
+  int32_t btlen[kFuseReqs];      // per request: block-table length
   int32_t n_facts;
   int64_t wsum[kWavesPerGroup];
 };
@@ -221,7 +223,14 @@ struct FusedLds {
 __device__ int64_t fused_plan(const DeviceBatch& b, FusedLds& s) {
   const int tid = threadIdx.x, lane = tid % kWave, wave = tid / kWave;
   const bool lead = blockIdx.x == 0;
-  for (int i = tid; i <= b.n_req; i += kThreads) s.reqptr[i] = b.req_fact_ptr[i];
+  // the per-request arrays are staged together, so later steps read LDS
+  for (int i = tid; i <= b.n_req; i += kThreads) {
+    s.reqptr[i] = b.req_fact_ptr[i];
+    if (i < b.n_req) {
+      s.start[i] = b.start_pos[i];
+      s.btlen[i] = b.bt_len[i];
+    }
+  }
   __syncthreads();
   int n_facts = s.reqptr[b.n_req];
   if (n_facts < 0 || n_facts > b.max_facts_batch) {
@@ -271,7 +280,7 @@ __device__ int64_t fused_plan(const DeviceBatch& b, FusedLds& s) {
     int first = s.reqptr[lo];
     if (first < 0 || first > tid) first = tid;
     s.req[tid] = lo;
-    s.pos0[tid] = int64_t(b.start_pos[lo]) + (tok - s.tok[first]);
+    s.pos0[tid] = int64_t(s.start[lo]) + (tok - s.tok[first]);
     if (lead) {
       FactPlan pl;
       pl.tok_start = tok;
@@ -311,7 +320,7 @@ __device__ void fused_map_token(const DeviceBatch& b, const FusedLds& s, int64_t
     bad = 2;
   } else {
     const int64_t bi = ps / b.block_size;
-    const int nb = b.bt_len[r];
+    const int nb = s.btlen[r];
     const int64_t blk =
         bi < nb && bi < b.bt_stride ? int64_t(b.block_tables[int64_t(r) * b.bt_stride + bi]) : -1;
     if (blk < 0 || blk >= b.num_blocks) bad = 4;
