@@ -300,11 +300,18 @@ __device__ int64_t fused_plan(const DeviceBatch& b, FusedLds& s) {
   return n_tokens;
 }
 
-// (arena row, rotation position, slot) of token t < n_tokens, validated as
-// materialize_kernel does; a token that fails gets row -1.  `report`: set
-// the status bits and write the mapping to the workspace.
-__device__ void fused_map_token(const DeviceBatch& b, const FusedLds& s, int64_t t, bool report,
-                                int& row, int& pos, int& slot) {
+// Token t < n_tokens of a fused batch, in two parts so that the block-table
+// load can stay in flight while the tile's K/V rows and cos/sin are loaded.
+// fused_map_token: from the plan in LDS, the arena row, the rotation
+// position, the request, the serving position ps and bad = 2 when ps is out
+// of range; it issues the block-table load and returns the block id (-1:
+// none).  fused_finish: the slot from that block id (bad = 4 when the table
+// is too short or the id out of range) and, with `report`, the status bits
+// and the workspace mapping exactly as materialize_kernel writes them (a
+// token that fails gets row -1, position 0, slot 0).
+__device__ __forceinline__ int64_t fused_map_token(const DeviceBatch& b, const FusedLds& s,
+                                                   int64_t t, int& row, int& pos, int64_t& ps,
+                                                   int& bad) {
   int lo = 0, hi = s.n_facts - 1;  // the fact of t: the last f with tok[f] <= t
   while (lo < hi) {
     const int mid = (lo + hi + 1) / 2;
@@ -312,30 +319,30 @@ __device__ void fused_map_token(const DeviceBatch& b, const FusedLds& s, int64_t
   }
   const int off = int(t - s.tok[lo]);
   const int r = s.req[lo];
-  const int64_t ps = s.pos0[lo] + off;
-  int bad = 0;
+  ps = s.pos0[lo] + off;
   row = s.row0[lo] + off;
-  slot = 0;
-  if (ps < 0 || ps >= b.max_position) {
-    bad = 2;
-  } else {
-    const int64_t bi = ps / b.block_size;
-    const int nb = s.btlen[r];
-    const int64_t blk =
-        bi < nb && bi < b.bt_stride ? int64_t(b.block_tables[int64_t(r) * b.bt_stride + bi]) : -1;
+  bad = (ps < 0 || ps >= b.max_position) ? 2 : 0;
+  pos = bad ? 0 : int32_t(b.chunk_local ? s.pos0[lo] : ps);
+  if (bad) return -1;
+  const int64_t bi = ps / b.block_size;
+  return bi < s.btlen[r] && bi < b.bt_stride
+             ? int64_t(b.block_tables[int64_t(r) * b.bt_stride + bi]) : -1;
+}
+
+__device__ __forceinline__ int fused_finish(const DeviceBatch& b, int64_t t, bool report,
+                                            int row, int pos, int64_t ps, int64_t blk, int bad) {
+  int slot = 0;
+  if (!bad) {
     if (blk < 0 || blk >= b.num_blocks) bad = 4;
     else slot = int32_t(blk * b.block_size + ps % b.block_size);
   }
-  if (bad) {
-    if (report) flag(b.status, bad);
-    row = -1;
-  }
-  pos = bad ? 0 : int32_t(b.chunk_local ? s.pos0[lo] : ps);
   if (report) {
-    b.src_row[t] = row;
-    b.pos[t] = pos;
-    b.slot[t] = slot;
+    if (bad) flag(b.status, bad);
+    b.src_row[t] = bad ? -1 : row;
+    b.pos[t] = bad ? 0 : pos;
+    b.slot[t] = bad ? 0 : slot;
   }
+  return bad ? -1 : slot;
 }
 
 template <int D, int STYLE, bool MULTI, bool FUSED>
@@ -401,14 +408,23 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     const int64_t tok0 = tile * tile_tokens;
     __syncthreads();  // LDS of the previous tile is no longer read
 
-    // 1. Wave-wide gather of the tile's (row, pos, slot); a row of -1 marks a
-    //    token to skip, other out-of-range tokens are reported and skipped.
-    for (int i = threadIdx.x; i < tile_tokens; i += kThreads) {
+    // 1. Wave-wide gather of the tile's (row, pos, slot), thread i for token
+    //    i (tile_tokens <= kThreads); a row of -1 marks a token to skip,
+    //    other out-of-range tokens are reported and skipped.  A fused batch
+    //    leaves the slot for step 3: its block-table load is in flight
+    //    meanwhile (a slot of -1 then marks a token to skip).
+    int f_row = 0, f_pos = 0, f_bad = 0;
+    int64_t f_ps = 0, f_blk = -1;
+    const bool own_token = int(threadIdx.x) < tile_tokens && tok0 + threadIdx.x < n_tokens;
+    if (int(threadIdx.x) < tile_tokens) {
+      const int i = threadIdx.x;
       const int64_t t = tok0 + i;
       int row = -1, pos = 0, slot = 0;
-      if (t < n_tokens) {
+      if (own_token) {
         if constexpr (FUSED) {
-          fused_map_token(fb, *fused, t, split == 0, row, pos, slot);
+          f_blk = fused_map_token(fb, *fused, t, f_row, f_pos, f_ps, f_bad);
+          row = f_bad ? -1 : f_row;
+          pos = f_pos;
         } else {
           row = p.src_row[t];
           pos = p.pos[t];
@@ -417,7 +433,7 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
         const int bad = row == -1 ? 0
                         : ((row < 0 || row >= p.capacity_rows) ? 1 : 0) |
                           ((pos < 0 || pos >= p.max_position) ? 2 : 0) |
-                          ((slot < 0 || slot >= p.num_slots) ? 4 : 0);
+                          ((!FUSED && (slot < 0 || slot >= p.num_slots)) ? 4 : 0);
         if (bad) {
           if (p.status && split == 0) atomicOr(p.status, bad);
           row = -1;
@@ -467,6 +483,13 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
       const f32x4 v = p.rope[int64_t(meta[3 * i + 1]) * HALF + j];
       smem[i * HALF + pair_slot<D, STYLE>(j)] = v;
     }
+    if constexpr (FUSED) {
+      // the slot from the block id loaded in step 1 (only the slot entry is
+      // written here; the loop above reads rows and positions)
+      if (own_token)
+        meta[3 * threadIdx.x + 2] =
+            fused_finish(fb, tok0 + threadIdx.x, split == 0, f_row, f_pos, f_ps, f_blk, f_bad);
+    }
     __syncthreads();
 
     // 4a. Rows narrower than a wave (H * D/16 < 64 chunks): the wave covers
@@ -476,14 +499,14 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
       const int j = wave * tpw + lane / nc;     // the lane's token in the tile
       const int h = (lane % nc) / CPH;
       const int row = meta[3 * j + 0];
-      const int slot = meta[3 * j + 2];
+      const int slot = meta[3 * j + 2];   // -1: a fused token whose block failed
       f32x4 cs[8];
 #pragma unroll
       for (int k = 0; k < 8; ++k) cs[k] = smem[j * HALF + k * CPH + c];
       const int64_t in_row = int64_t(h) * D + c * 8;
       const int64_t a0 = int64_t(row) * row_elems + in_row;
       const int64_t s0 = cache_slot_base<D>(p, slot) + int64_t(h) * head_stride + c * 8;
-      if (row >= 0) {
+      if (row >= 0 && slot >= 0) {
         for (int l0 = it0; l0 < it1; l0 += kUnroll) {
           u32x4 ka[kUnroll], kb[kUnroll], va[kUnroll], vb[kUnroll];
 #pragma unroll
@@ -516,8 +539,8 @@ __global__ __launch_bounds__(kThreads) void inject_kernel(InjectParams p, LayerP
     // 4b. Otherwise each wave streams its one token through every layer of
     //     its split.
     const int row = __builtin_amdgcn_readfirstlane(meta[3 * wave + 0]);
-    if (row >= 0) {
-      const int slot = __builtin_amdgcn_readfirstlane(meta[3 * wave + 2]);
+    const int slot = __builtin_amdgcn_readfirstlane(meta[3 * wave + 2]);
+    if (row >= 0 && slot >= 0) {   // slot -1: a fused token whose block failed
       const int64_t slot_base = cache_slot_base<D>(p, slot);
 
       f32x4 cs[8];
