@@ -12,11 +12,12 @@
 // from those of the other heads) or HND ([block][H][bs][D]: one head's keys
 // of a block are contiguous); only the address of a key's row differs.
 //
-// Work unit: one workgroup per (layer, request, KV head).  Its rows are the
-// q_len query tokens x the `group` query heads sharing that KV head (at most
-// 64 rows, 16 per wave).  Keys stream in tiles of 32 positions through a
-// double-buffered LDS ring: while tile t is computed, tile t+1's K and V rows
-// travel from the paged cache straight into LDS (global_load_lds_dwordx4,
+// Work unit: one workgroup per (layer, request, KV head, row block).  The
+// rows are the q_len query tokens x the `group` query heads sharing that KV
+// head, in blocks of 64 (16 per wave); a row block reads the keys up to its
+// last query token.  Keys stream in tiles of 32 positions through an LDS
+// ring of three tiles: while tile t is computed, tiles t+1 and t+2's K and V
+// rows travel from the paged cache straight into LDS (global_load_lds_dwordx4,
 // no register staging), gathered through the block table (kept in LDS; the
 // slot of every key is computed once, two tiles ahead).  Per tile each wave
 // computes
@@ -84,6 +85,7 @@ struct AttnParams {
   int64_t num_blocks;
   float scale_log2;        // softmax scale * log2(e)
   int32_t n_req, q_len, num_q_heads, num_kv_heads, group, rows;
+  int32_t row_blocks;      // ceil(rows / kMaxRows) workgroups per (layer, request, KV head)
   int32_t bt_stride, block_size, max_position;
   int32_t bs_shift;        // log2(block_size) when it is a power of two, else -1
   int32_t hnd;             // cache layout HND ([block][H][bs][D]) instead of NHD
@@ -137,15 +139,19 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
 
   // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so
   // logical id (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous run
-  // of (layer, request, head) work: the heads of one cache row share an L2.
+  // of (layer, request, head, row block) work: the heads of one cache row,
+  // and the row blocks that read the same keys, share an L2.
   const int nwg = gridDim.x;
   const int bid = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
-  const int g = bid % p.num_kv_heads;
-  const int r = (bid / p.num_kv_heads) % p.n_req;
-  const int layer = bid / (p.num_kv_heads * p.n_req);
+  const int rb = bid % p.row_blocks;
+  const int unit = bid / p.row_blocks;
+  const int g = unit % p.num_kv_heads;
+  const int r = (unit / p.num_kv_heads) % p.n_req;
+  const int layer = unit / (p.num_kv_heads * p.n_req);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int a = lane / 16, c16 = lane % 16;
-  const int row = wave * 16 + c16;
+  // rows (query token, query head of the group) rb * 64 .. rb * 64 + 63
+  const int row = rb * kMaxRows + wave * 16 + c16;
   const bool row_ok = row < p.rows;
   const int qi = row_ok ? row / p.group : 0;
   const int hq = g * p.group + (row_ok ? row % p.group : 0);
@@ -156,7 +162,12 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   if (!req_ok && threadIdx.x == 0 && p.status) atomicOr(p.status, 2);
   const int q0 = req_ok ? q_first : 0;
   const int qpos = q0 + qi;
-  const int ctx = req_ok ? q0 + p.q_len : 0;  // keys [0, ctx)
+  // the row block's first and last query tokens: its keys are [0, ctx), and
+  // tiles that end at or before its first query position need no mask
+  const int qi_first = rb * kMaxRows / p.group;
+  const int qi_last = (min(p.rows, (rb + 1) * kMaxRows) - 1) / p.group;
+  const int q_block0 = q0 + qi_first;
+  const int ctx = req_ok ? q0 + qi_last + 1 : 0;
 
   // The first kThreads block-table entries are loaded now, so that their
   // latency overlaps the query's (the host checks bt_stride >= 1).
@@ -446,7 +457,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     if (t + kStages < ntiles) fill_slots(t + kStages);
     if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
     const int* sl = s_slots[t % kSlotRing];
-    const bool masked = any_missing || base + kTile - 1 > q0;
+    const bool masked = any_missing || base + kTile - 1 > q_block0;
     if (masked) {
       zero_masked(sl, t % kStages);
       __syncthreads();
@@ -506,9 +517,14 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
     return prkv::fail(PRKV_ERR_INVALID_ARG, "num_q_heads %d not a multiple of %d KV heads",
                       b->num_q_heads, d.num_kv_heads);
   const int group = b->num_q_heads / d.num_kv_heads;
-  if (int64_t(b->q_len) * group > kMaxRows)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "q_len * heads per KV head = %lld exceeds %d",
-                      (long long)b->q_len * group, kMaxRows);
+  if (b->q_len > d.max_position)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "q_len %d exceeds max_position %d", b->q_len,
+                      d.max_position);
+  const int64_t rows = int64_t(b->q_len) * group;
+  if (rows > INT32_MAX - kMaxRows)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "q_len * heads per KV head = %lld too large",
+                      (long long)rows);
+  const int64_t row_blocks = (rows + kMaxRows - 1) / kMaxRows;
   if (block_size < 1 || num_blocks < 1 || num_blocks * int64_t(block_size) > INT32_MAX)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "bad cache shape");
   if (!(softmax_scale > 0.f) || !std::isfinite(softmax_scale))
@@ -531,7 +547,7 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
     kc.p[l] = static_cast<const uint16_t*>(k_cache_layers[l]);
     vc.p[l] = static_cast<const uint16_t*>(v_cache_layers[l]);
   }
-  const int64_t grid = int64_t(d.num_layers) * b->n_req * d.num_kv_heads;
+  const int64_t grid = int64_t(d.num_layers) * b->n_req * d.num_kv_heads * row_blocks;
   if (grid > INT32_MAX) return prkv::fail(PRKV_ERR_INVALID_ARG, "grid too large");
   AttnParams p;
   p.q = b->q;
@@ -548,7 +564,8 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
   p.num_q_heads = b->num_q_heads;
   p.num_kv_heads = d.num_kv_heads;
   p.group = group;
-  p.rows = b->q_len * group;
+  p.rows = int32_t(rows);
+  p.row_blocks = int32_t(row_blocks);
   p.bt_stride = b->bt_stride;
   p.block_size = block_size;
   p.bs_shift = (block_size & (block_size - 1)) == 0 ? __builtin_ctz(uint32_t(block_size)) : -1;

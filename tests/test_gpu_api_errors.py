@@ -110,7 +110,7 @@ def test_attend_paged_argument_errors(dw):
                           d_status=dw.status, stream=dw.stream)
 
     assert _code(call, heads=12) == "INVALID_ARG"                 # not a multiple of 8
-    assert _code(call, q_len=17) == "INVALID_ARG"                 # 17 x 4 rows > 64
+    assert _code(call, q_len=w.spec.max_position + 1) == "INVALID_ARG"   # past every position
     assert _code(call, bt_stride=2049) == "INVALID_ARG"
     assert _code(call, scale=0.0) == "INVALID_ARG"
     assert _code(call, scale=float("nan")) == "INVALID_ARG"

@@ -201,6 +201,23 @@ def test_attention_edge_shapes(bs, prefix, lens, q_len, hq, D):
     check(dw, qb, got, q_len, hq, layers, "cpu")
 
 
+@pytest.mark.parametrize("bs,D,H,hq,q_len,lens", [
+    (16, 128, 2, 8, 40, [[30, 12, 41]]),       # 160 rows: three row blocks, the last 32 rows
+    (24, 64, 2, 4, 33, [[9, 50], [17]]),       # 66 rows: a second block of 2 rows, ragged
+    (16, 128, 8, 32, 64, [[35, 22, 48, 20]]),  # Llama-3-8B grouping, a 64-token question
+    (32, 64, 3, 3, 100, [[60, 7]]),            # group 1: 100 rows, two blocks
+])
+def test_attention_long_queries(bs, D, H, hq, q_len, lens):
+    """Queries longer than one workgroup's 64 (query token, query head) rows:
+    the rows are split into blocks, each reading the keys up to its last
+    query token."""
+    w = context_workload(f"attn_long_{bs}_{D}_{H}_{q_len}", 2, H, D, bs, 20, lens, q_len,
+                         n_req=len(lens), seed=q_len)
+    dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu")
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, q_len, hq, layers, "cpu")
+
+
 def test_attention_query_positions_out_of_range_are_reported():
     # request 0 starts past max_position - q_len, request 1 before 0: both are
     # reported (bit 2) and produce 0; request 2 is unaffected
