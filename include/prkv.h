@@ -335,8 +335,8 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
  * q: pre-RoPE, rotated in the kernel with the store's table.  K and V of the
  * cache are bf16; q and the probabilities are carried as bf16 hi + lo pairs
  * into the matrix cores, so the result is accurate to fp32 rounding.
- * Limits: head_dim 64 or 128; bt_stride <= 2048 (the table is staged in
- * LDS); q_len <= max_position.  Rows (query token, query head) are taken 64
+ * Limits: head_dim 64 or 128; q_len <= max_position.  A block table of up
+ * to 2048 entries is staged in LDS, a longer one read from device memory.  Rows (query token, query head) are taken 64
  * at a time per (layer, request, KV head): a query of q_len * (num_q_heads /
  * H) <= 64 rows reads its context once, a longer one once per 64 rows.  Positions whose block is missing
  * from the table are masked and set bit 4 of d_status; a request whose query

@@ -124,9 +124,11 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_addr) {
                : "memory");
 }
 
-template <int D, int STYLE>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(AttnParams p, LayerCPtrs kc,
-                                                          LayerCPtrs vc) {
+// BT_LDS: the request's block table is staged in LDS (bt_stride <= kBtLds);
+// otherwise it is read from device memory.
+template <int D, int STYLE, bool BT_LDS>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(
+    AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
   constexpr int ROWB = D * 2;           // bytes per K or V row
@@ -135,7 +137,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // a ring of tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
   __shared__ __align__(1024) unsigned char s_kv[kStages][2][TILEB];
   __shared__ __align__(16) int s_slots[kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
-  extern __shared__ int s_bt[];         // the request's block table: bt_stride entries
+  extern __shared__ int s_bt[];         // the request's block table (bt_stride <= kBtLds)
 
   // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so
   // logical id (b % 8) * (grid / 8) + b / 8 gives each XCD a contiguous run
@@ -258,15 +260,20 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int64_t row_elems = int64_t(p.num_kv_heads) * D;
   const int ntiles = ctx > 0 ? (ctx + kTile - 1) / kTile : 0;
 
-  // (nb <= bt_stride, the dynamic LDS size; the host checks bt_stride <= kBtLds)
-  if (int(threadIdx.x) < nb) s_bt[threadIdx.x] = bt_first;
-  for (int i = threadIdx.x + kThreads; i < nb; i += kThreads) s_bt[i] = btr[i];
+  // The table is staged in LDS when it fits (nb <= bt_stride <= kBtLds, the
+  // dynamic LDS size); a longer one (contexts beyond kBtLds blocks) is read
+  // from global memory, where the slots are computed kStages tiles ahead.
+  if constexpr (BT_LDS) {
+    if (int(threadIdx.x) < nb) s_bt[threadIdx.x] = bt_first;
+    for (int i = threadIdx.x + kThreads; i < nb; i += kThreads) s_bt[i] = btr[i];
+  }
   __syncthreads();
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
   auto slot_of = [&](int pos) -> int {
     const int bi = p.bs_shift >= 0 ? pos >> p.bs_shift : pos / p.block_size;
     const int off = pos - bi * p.block_size;
-    const int64_t blk = s_bt[bi < nb ? bi : 0];
+    const int bj = bi < nb ? bi : 0;   // nb <= bt_stride and bt_stride >= 1
+    const int64_t blk = BT_LDS ? s_bt[bj] : btr[bj];
     const bool inb = bi < nb && blk >= 0 && blk < p.num_blocks;
     return inb ? int(blk * p.block_size + off) : -2;
   };
@@ -276,7 +283,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   int bad = 0;
   const int nblk = ctx > 0 ? (ctx - 1) / p.block_size + 1 : 0;
   for (int i = threadIdx.x; i < nblk; i += kThreads) {
-    const int64_t blk = i < nb ? s_bt[i] : -1;
+    const int64_t blk = i < nb ? (BT_LDS ? s_bt[i] : btr[i]) : -1;
     bad |= blk < 0 || blk >= p.num_blocks;
   }
   const bool any_missing = __syncthreads_or(bad) != 0;
@@ -477,18 +484,26 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
+template <int D, int STYLE>
+void launch_attend_style(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
+                         int64_t grid, hipStream_t s) {
+  // the block table is the dynamic LDS: a short table leaves room for more
+  // workgroups per CU
+  if (p.bt_stride <= kBtLds)
+    hipLaunchKernelGGL((attend_kernel<D, STYLE, true>), dim3(unsigned(grid)), dim3(kThreads),
+                       size_t(p.bt_stride > 0 ? p.bt_stride : 1) * sizeof(int32_t), s, p, kc, vc);
+  else
+    hipLaunchKernelGGL((attend_kernel<D, STYLE, false>), dim3(unsigned(grid)), dim3(kThreads),
+                       sizeof(int32_t), s, p, kc, vc);
+}
+
 template <int D>
 hipError_t launch_attend(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
                          int64_t grid, int style, hipStream_t s) {
-  // the block table is the dynamic LDS: a short table leaves room for more
-  // workgroups per CU
-  const size_t lds = size_t(p.bt_stride > 0 ? p.bt_stride : 1) * sizeof(int32_t);
   if (style == PRKV_ROPE_INTERLEAVED)
-    hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_INTERLEAVED>), dim3(unsigned(grid)),
-                       dim3(kThreads), lds, s, p, kc, vc);
+    launch_attend_style<D, PRKV_ROPE_INTERLEAVED>(p, kc, vc, grid, s);
   else
-    hipLaunchKernelGGL((attend_kernel<D, PRKV_ROPE_HALF_SPLIT>), dim3(unsigned(grid)),
-                       dim3(kThreads), lds, s, p, kc, vc);
+    launch_attend_style<D, PRKV_ROPE_HALF_SPLIT>(p, kc, vc, grid, s);
   return hipGetLastError();
 }
 
@@ -510,9 +525,6 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
     return prkv::fail(PRKV_ERR_INVALID_ARG, "bad batch sizes");
   if (b->n_req > 0 && b->q_len > 0 && b->bt_stride < 1)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "bt_stride must be >= 1");
-  if (b->bt_stride > kBtLds)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "bt_stride %d exceeds %d block-table entries",
-                      b->bt_stride, kBtLds);
   if (b->num_q_heads % d.num_kv_heads != 0)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "num_q_heads %d not a multiple of %d KV heads",
                       b->num_q_heads, d.num_kv_heads);

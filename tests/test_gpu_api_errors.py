@@ -111,7 +111,6 @@ def test_attend_paged_argument_errors(dw):
 
     assert _code(call, heads=12) == "INVALID_ARG"                 # not a multiple of 8
     assert _code(call, q_len=w.spec.max_position + 1) == "INVALID_ARG"   # past every position
-    assert _code(call, bt_stride=2049) == "INVALID_ARG"
     assert _code(call, scale=0.0) == "INVALID_ARG"
     assert _code(call, scale=float("nan")) == "INVALID_ARG"
     assert _code(call, qp=q.data_ptr() + 8) == "ALIGNMENT"

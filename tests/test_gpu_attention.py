@@ -218,6 +218,18 @@ def test_attention_long_queries(bs, D, H, hq, q_len, lens):
     check(dw, qb, got, q_len, hq, layers, "cpu")
 
 
+@pytest.mark.parametrize("bs,prefix,lens", [(1, 2000, [[40, 30]]), (2, 4100, [[57, 9]])])
+def test_attention_block_table_beyond_lds(bs, prefix, lens):
+    """Block tables longer than the 2048 entries staged in LDS are read from
+    device memory (contexts of ~2,080 and ~4,170 positions at block sizes 1
+    and 2: 2,078 and 2,087 table entries)."""
+    w = context_workload(f"attn_longbt_{bs}", 2, 2, 64, bs, prefix, lens, 8, seed=bs)
+    dw, qb, got, layers = run_attention(w, 8, 8, gen="cpu")
+    assert dw.bt.shape[1] > 2048
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, 8, 8, layers, "cpu")
+
+
 def test_attention_query_positions_out_of_range_are_reported():
     # request 0 starts past max_position - q_len, request 1 before 0: both are
     # reported (bit 2) and produce 0; request 2 is unaffected
