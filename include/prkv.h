@@ -340,7 +340,8 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
  * at a time per (layer, request, KV head): a query of q_len * (num_q_heads /
  * H) <= 64 rows reads its context once, a longer one once per 64 rows.  Positions whose block is missing
  * from the table are masked and set bit 4 of d_status; a request whose query
- * positions do not lie in [0, max_position) sets bit 2 and gets output 0.
+ * positions do not lie in [0, max_position) sets bit 2 and gets output 0;
+ * a q_lens value outside [0, q_len] sets bit 8 and is clamped.
  * One kernel launch on `stream`, asynchronous. */
 typedef struct prkv_attn_batch {
   int32_t n_req;
@@ -352,6 +353,9 @@ typedef struct prkv_attn_batch {
   const int32_t* block_tables; /* device [n_req][bt_stride] */
   const int32_t* bt_len;       /* device [n_req] */
   float* out;                  /* device [L][n_req][q_len][num_q_heads][D] */
+  const int32_t* q_lens;       /* device [n_req] or NULL: request r's query is its
+                                  first q_lens[r] <= q_len tokens (positions
+                                  q_start[r] ..); the rows past it get output 0 */
 } prkv_attn_batch;
 
 int attend_paged(const prkv_store* st, const prkv_attn_batch* batch,

@@ -77,6 +77,7 @@ struct LayerCPtrs {
 struct AttnParams {
   const uint16_t* q;       // [n_req][q_len][Hq][D] pre-RoPE bf16
   const int32_t* q_start;  // [n_req]
+  const int32_t* q_lens;   // [n_req] query tokens per request (<= q_len), or null: all q_len
   const int32_t* bt;       // [n_req][bt_stride]
   const int32_t* bt_len;   // [n_req]
   const f32x4* rope;       // [max_position][D/2]
@@ -152,24 +153,37 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int layer = unit / (p.num_kv_heads * p.n_req);
   const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
   const int a = lane / 16, c16 = lane % 16;
-  // rows (query token, query head of the group) rb * 64 .. rb * 64 + 63
+  // This request's query tokens: q_lens[r] (a value outside [0, q_len] is
+  // reported, status bit 8, and clamped), else q_len.
+  int qlen_r = p.q_len;
+  if (p.q_lens) {
+    const int v = p.q_lens[r];
+    if ((v < 0 || v > p.q_len) && threadIdx.x == 0 && p.status) atomicOr(p.status, 8);
+    qlen_r = v < 0 ? 0 : (v > p.q_len ? p.q_len : v);
+  }
+  const int rows_r = qlen_r * p.group;
+  // rows (query token, query head of the group) rb * 64 .. rb * 64 + 63;
+  // rows past this request's query (but inside q_len) get output 0
   const int row = rb * kMaxRows + wave * 16 + c16;
-  const bool row_ok = row < p.rows;
-  const int qi = row_ok ? row / p.group : 0;
-  const int hq = g * p.group + (row_ok ? row % p.group : 0);
+  const bool row_ok = row < rows_r;
+  const bool row_out = row < p.rows;
+  const int qi = row_out ? row / p.group : 0;
+  const int hq = g * p.group + (row_out ? row % p.group : 0);
   // The query's positions must lie in [0, max_position); a request whose
   // do not is reported (status bit 2) and attends to nothing (output 0).
   const int q_first = p.q_start[r];
-  const bool req_ok = q_first >= 0 && q_first <= p.max_position - p.q_len;
+  const bool req_ok = q_first >= 0 && q_first <= p.max_position - qlen_r;
   if (!req_ok && threadIdx.x == 0 && p.status) atomicOr(p.status, 2);
   const int q0 = req_ok ? q_first : 0;
   const int qpos = q0 + qi;
   // the row block's first and last query tokens: its keys are [0, ctx), and
-  // tiles that end at or before its first query position need no mask
+  // tiles that end at or before its first query position need no mask; a
+  // block with no row of this request reads nothing
   const int qi_first = rb * kMaxRows / p.group;
-  const int qi_last = (min(p.rows, (rb + 1) * kMaxRows) - 1) / p.group;
+  const bool block_live = req_ok && rows_r > rb * kMaxRows;
+  const int qi_last = block_live ? (min(rows_r, (rb + 1) * kMaxRows) - 1) / p.group : 0;
   const int q_block0 = q0 + qi_first;
-  const int ctx = req_ok ? q0 + qi_last + 1 : 0;
+  const int ctx = block_live ? q0 + qi_last + 1 : 0;
 
   // The first kThreads block-table entries are loaded now, so that their
   // latency overlaps the query's (the host checks bt_stride >= 1).
@@ -475,12 +489,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // normalise and write O[layer][r][qi][hq][d], d = 16mt + 4a + i
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
-  if (row_ok) {
-    const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (row_out) {
+    const float inv = row_ok && l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* orow = p.out + (((int64_t(layer) * p.n_req + r) * p.q_len + qi) * p.num_q_heads + hq) * D;
 #pragma unroll
     for (int mt = 0; mt < MT; ++mt)
-      *reinterpret_cast<f32x4*>(orow + 16 * mt + 4 * a) = o[mt] * inv;
+      *reinterpret_cast<f32x4*>(orow + 16 * mt + 4 * a) =
+          row_ok ? o[mt] * inv : f32x4{0.f, 0.f, 0.f, 0.f};
   }
 }
 
@@ -547,7 +562,8 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
     return prkv::fail(PRKV_ERR_INVALID_ARG, "NULL pointer argument");
   if ((reinterpret_cast<uintptr_t>(b->q) | reinterpret_cast<uintptr_t>(b->out)) & 15u ||
       (reinterpret_cast<uintptr_t>(b->q_start) | reinterpret_cast<uintptr_t>(b->block_tables) |
-       reinterpret_cast<uintptr_t>(b->bt_len) | reinterpret_cast<uintptr_t>(d_status)) & 3u)
+       reinterpret_cast<uintptr_t>(b->bt_len) | reinterpret_cast<uintptr_t>(b->q_lens) |
+       reinterpret_cast<uintptr_t>(d_status)) & 3u)
     return prkv::fail(PRKV_ERR_ALIGNMENT, "q/out 16-byte, int32 arrays 4-byte aligned");
   LayerCPtrs kc{}, vc{};
   for (int l = 0; l < d.num_layers; ++l) {
@@ -564,6 +580,7 @@ int attend_paged(const prkv_store* st, const prkv_attn_batch* b, void* const* k_
   AttnParams p;
   p.q = b->q;
   p.q_start = b->q_start;
+  p.q_lens = b->q_lens;
   p.bt = b->block_tables;
   p.bt_len = b->bt_len;
   p.rope = static_cast<const f32x4*>(st->rope);

@@ -87,6 +87,7 @@ class AttnBatch(ctypes.Structure):
         ("block_tables", ctypes.c_void_p),
         ("bt_len", ctypes.c_void_p),
         ("out", ctypes.c_void_p),
+        ("q_lens", ctypes.c_void_p),
     ]
 
 
@@ -374,10 +375,12 @@ def retrieve_topk(d_fact_emb, n_stores, facts_per_store, dim, d_query_emb, d_req
            "retrieve_topk")
 
 
-def attn_batch(n_req, q_len, num_q_heads, bt_stride, q, q_start, block_tables, bt_len, out):
-    """prkv_attn_batch over device tensors (raw pointers: keep the tensors alive)."""
+def attn_batch(n_req, q_len, num_q_heads, bt_stride, q, q_start, block_tables, bt_len, out,
+               q_lens=None):
+    """prkv_attn_batch over device tensors (raw pointers: keep the tensors alive).
+    q_lens: optional device int32 [n_req], each request's own query length."""
     return AttnBatch(int(n_req), int(q_len), int(num_q_heads), int(bt_stride), _ptr(q),
-                     _ptr(q_start), _ptr(block_tables), _ptr(bt_len), _ptr(out))
+                     _ptr(q_start), _ptr(block_tables), _ptr(bt_len), _ptr(out), _ptr(q_lens))
 
 
 def attend_paged(st, batch, k_cache_layers, v_cache_layers, block_size, num_blocks,

@@ -35,12 +35,14 @@ TOL_IN_PLACE = 3e-3
 
 
 def context_workload(name, L, H, D, bs, prefix, fact_lens, q_len, n_req=1, seed=0):
-    """Request r: [prefix fact, its facts..., query fact], start position 0."""
+    """Request r: [prefix fact, its facts..., query fact], start position 0.
+    q_len: the query fact's length, or a list of them per request (0: none)."""
     rng = np.random.default_rng(seed)
     facts, reqs, fid = {}, [], 0
     for r in range(n_req):
         ids = []
-        for ln in [prefix] + [int(x) for x in fact_lens[r]] + [q_len]:
+        ql = q_len[r] if isinstance(q_len, (list, tuple)) else q_len
+        for ln in [prefix] + [int(x) for x in fact_lens[r]] + ([ql] if ql > 0 else []):
             facts[fid] = ln
             ids.append(fid)
             fid += 1
@@ -228,6 +230,71 @@ def test_attention_block_table_beyond_lds(bs, prefix, lens):
     assert dw.bt.shape[1] > 2048
     assert int(dw.status.item()) == 0
     check(dw, qb, got, 8, 8, layers, "cpu")
+
+
+def test_attention_ragged_query_lengths():
+    """Per-request query lengths (q_lens) inside a padded q_len: each
+    request's own rows against the oracle over the same cache, the padding
+    rows exactly 0; a q_lens value out of range sets bit 8, is clamped, and
+    leaves the other requests' outputs bit for bit unchanged."""
+    qls = [16, 5, 0, 9, 1]
+    rng = np.random.default_rng(77)
+    lens = [rng.integers(5, 50, size=int(rng.integers(1, 5))) for _ in qls]
+    L, H, D, bs, Q, hq = 2, 2, 128, 16, max(qls), 8
+    w = context_workload("attn_ragged", L, H, D, bs, 20, lens, qls, n_req=len(qls), seed=77)
+    dw = harness.DeviceWorkload(w, gen_device="cpu")
+    dw.inject()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    ctxs = [sum(w.length_of(f) for f in ids) for ids in w.retrieved]
+    g = torch.Generator(device="cpu")
+    g.manual_seed(78)
+    q_bits = torch.randn((len(qls), Q, hq, D), generator=g).to(torch.bfloat16).view(torch.int16)
+    q_start = torch.as_tensor([c - ql for c, ql in zip(ctxs, qls)], dtype=torch.int32,
+                              device="cuda")
+    bt = torch.from_numpy(np.ascontiguousarray(dw.bt)).cuda()
+    bt_len = torch.from_numpy(dw.bt_len).cuda()
+    q = q_bits.cuda()
+
+    def run(q_lens):
+        out = torch.full((L, len(qls), Q, hq, D), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        d_ql = torch.as_tensor(q_lens, dtype=torch.int32, device="cuda")
+        ab = prkv.attn_batch(len(qls), Q, hq, bt.shape[1], q, q_start, bt, bt_len, out,
+                             q_lens=d_ql)
+        dw.status.zero_()
+        prkv.attend_paged(dw.store, ab, dw.k_layers(), dw.v_layers(), bs, w.num_blocks,
+                          1.0 / math.sqrt(D), d_status=dw.status)
+        torch.cuda.synchronize()
+        return out.cpu().numpy().astype(np.float64), int(dw.status.item())
+
+    got, st = run(qls)
+    assert st == 0
+    worst = 0.0
+    for r, (ql, ctx) in enumerate(zip(qls, ctxs)):
+        assert np.all(got[:, r, ql:] == 0), r
+        if ql == 0:
+            continue
+        b = w.block_tables[r]
+        slots = torch.as_tensor([int(b[p // bs]) * bs + p % bs for p in range(ctx)],
+                                device=dw.device)
+        kr = dw.slot_rows(dw.k_cache, slots)
+        vr = dw.slot_rows(dw.v_cache, slots)
+        q_pos = np.arange(ctx - ql, ctx)
+        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r, :ql].numpy().view(np.uint16)),
+                            q_pos[:, None], 5e5)
+        for l in range(L):
+            want = attention.causal_gqa(q_rot, q_pos,
+                                        bf16.bf16_bits_to_f64(kr[l].cpu().numpy().view(np.uint16)),
+                                        bf16.bf16_bits_to_f64(vr[l].cpu().numpy().view(np.uint16)),
+                                        np.arange(ctx), 1.0 / math.sqrt(D))
+            worst = max(worst, float(np.max(np.abs(got[l, r, :ql] - want))))
+    _say(f"ragged queries: max |gpu - oracle over gpu cache| = {worst:.3g}")
+    assert worst <= TOL_SAME_CACHE
+    bad, st = run([-1] + qls[1:])
+    assert st == 8
+    assert np.all(bad[:, 0] == 0)
+    assert np.array_equal(bad[:, 1:], got[:, 1:])
 
 
 def test_attention_query_positions_out_of_range_are_reported():
