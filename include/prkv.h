@@ -304,7 +304,7 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
  * the facts found -- exact search stands in for the approximate index.
  * d_fact_emb: device bf16 [n_stores][facts_per_store][dim]; d_query_emb:
  * device bf16 [n_req][dim]; d_req_store: device int32 [n_req], the store each
- * request searches.  dim: multiple of 512 in [512, 4096]; 1 <= k <= 64 and
+ * request searches.  dim: multiple of 8 in [8, 4096]; 1 <= k <= 64 and
  * k <= facts_per_store.  Scores are inner products of the bf16 values
  * accumulated in float64 (products are exact).  Output d_fact_ids: device
  * int32 [n_req][k], global ids store * facts_per_store + fact, best first

@@ -12,7 +12,8 @@
 //
 // score_kernel: one wave per group of facts of one request.  The query is
 // read once per wave; lane l owns elements [8l + 512j, 8l + 512j + 8) of the
-// embedding, so every 16-byte load of a fact row is coalesced.  Products of
+// embedding (lanes past the width take zeros in the last, partial chunk), so
+// every 16-byte load of a fact row is coalesced.  Products of
 // two bf16 values are exact; they are accumulated in float64 and reduced
 // across the wave with a butterfly, so a score differs from the exact inner
 // product by ~1e-16 relative.  HBM bound (the embeddings are read once);
@@ -57,7 +58,7 @@ __device__ __forceinline__ double bf16_hi(unsigned w) {
   return double(__uint_as_float(w & 0xffff0000u));
 }
 
-template <int CHUNKS>  // dim / 512
+template <int CHUNKS>  // ceil(dim / 512); dim is a multiple of 8
 __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams p) {
   const int gw = blockIdx.x * kScoreWaves + threadIdx.x / kWave;
   const int lane = threadIdx.x % kWave;
@@ -69,10 +70,16 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
     if (lane == 0 && f0 == 0 && p.status) atomicOr(p.status, 64);
     return;
   }
+  // The last 512-element chunk may be partial: a lane whose 8 elements lie
+  // past dim takes zeros (dim is a multiple of 8, so a lane's piece is
+  // wholly inside or wholly outside).
+  const bool tail_in = lane * 8 + 512 * (CHUNKS - 1) < p.dim;
+  const u32x4 zero = {0u, 0u, 0u, 0u};
   u32x4 q[CHUNKS];
   const uint16_t* qrow = p.query_emb + int64_t(r) * p.dim + lane * 8;
 #pragma unroll
-  for (int j = 0; j < CHUNKS; ++j) q[j] = *reinterpret_cast<const u32x4*>(qrow + 512 * j);
+  for (int j = 0; j < CHUNKS; ++j)
+    q[j] = (j < CHUNKS - 1 || tail_in) ? *reinterpret_cast<const u32x4*>(qrow + 512 * j) : zero;
   const uint16_t* base = p.fact_emb + (int64_t(s) * p.facts_per_store) * p.dim + lane * 8;
   const int f1 = min(f0 + kFactsPerWave, p.facts_per_store);
   for (int f = f0; f < f1; ++f) {
@@ -80,7 +87,9 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
     u32x4 e[CHUNKS];
 #pragma unroll
     for (int j = 0; j < CHUNKS; ++j)
-      e[j] = __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 512 * j));
+      e[j] = (j < CHUNKS - 1 || tail_in)
+                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 512 * j))
+                 : zero;
     double acc = 0.0;
 #pragma unroll
     for (int j = 0; j < CHUNKS; ++j) {
@@ -251,9 +260,8 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
                       n_stores, facts_per_store);
   if (k < 1 || k > kMaxK || k > facts_per_store)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "k %d not in [1, min(64, facts_per_store)]", k);
-  if (dim < 512 || dim % 512 != 0 || dim > 4096)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "dim %d must be a multiple of 512 in [512, 4096]",
-                      dim);
+  if (dim < 8 || dim % 8 != 0 || dim > 4096)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "dim %d must be a multiple of 8 in [8, 4096]", dim);
   if (int64_t(n_stores) * facts_per_store > INT32_MAX)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "n_stores * facts_per_store exceeds 2^31-1");
   if (n_req == 0) return PRKV_OK;
@@ -284,7 +292,7 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
     return prkv::fail(PRKV_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
   hipError_t e;
-  switch (dim / 512) {
+  switch ((dim + 511) / 512) {
     case 1: e = launch_scores<1>(sp, s); break;
     case 2: e = launch_scores<2>(sp, s); break;
     case 3: e = launch_scores<3>(sp, s); break;

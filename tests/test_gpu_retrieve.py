@@ -81,7 +81,11 @@ def test_retrieve_matches_oracle(name):
 
 
 @pytest.mark.parametrize("F,k,dim", [(1, 1, 512), (1003, 64, 512), (777, 7, 4096),
-                                     (64, 64, 1024), (5000, 50, 2560)])
+                                     (64, 64, 1024), (5000, 50, 2560),
+                                     # widths that are not multiples of 512: a partial
+                                     # last chunk (384, 768, 1000, 8) or a single one
+                                     (2000, 50, 384), (1500, 20, 768), (300, 64, 1000),
+                                     (100, 10, 8), (257, 5, 4088)])
 def test_retrieve_shapes(F, k, dim):
     g = torch.Generator(device="cuda")
     g.manual_seed(F * 131 + k * 7 + dim)

@@ -325,7 +325,8 @@ def test_inject_device_rejects_metadata_store_and_bad_batches():
 
 @pytest.mark.parametrize("kw,name", [
     (dict(k=0), "INVALID_ARG"), (dict(k=65), "INVALID_ARG"), (dict(k=101), "INVALID_ARG"),
-    (dict(dim=1000), "INVALID_ARG"), (dict(dim=4608), "INVALID_ARG"),
+    (dict(dim=1004), "INVALID_ARG"), (dict(dim=0), "INVALID_ARG"), (dict(dim=4104), "INVALID_ARG"),
+    (dict(dim=4608), "INVALID_ARG"),
     (dict(n_stores=0), "INVALID_ARG"), (dict(fact_emb=None), "INVALID_ARG"),
     (dict(fact_emb=4104), "ALIGNMENT"), (dict(ws_bytes=8), "BUFFER_TOO_SMALL"),
 ])
