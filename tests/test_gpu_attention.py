@@ -34,7 +34,7 @@ TOL_SAME_CACHE = 2e-4
 TOL_IN_PLACE = 3e-3
 
 
-def context_workload(name, L, H, D, bs, prefix, fact_lens, q_len, n_req=1, seed=0):
+def context_workload(name, L, H, D, bs, prefix, fact_lens, q_len, n_req=1, seed=0, theta=5e5):
     """Request r: [prefix fact, its facts..., query fact], start position 0.
     q_len: the query fact's length, or a list of them per request (0: none)."""
     rng = np.random.default_rng(seed)
@@ -50,7 +50,7 @@ def context_workload(name, L, H, D, bs, prefix, fact_lens, q_len, n_req=1, seed=
     # put order shuffled so rows are scattered in the arena
     order = list(facts)
     rng.shuffle(order)
-    w = custom_workload(name, L, H, D, bs, {f: facts[f] for f in order}, reqs, theta=5e5,
+    w = custom_workload(name, L, H, D, bs, {f: facts[f] for f in order}, reqs, theta=theta,
                         num_blocks=max(512, 4 * sum(facts.values()) // bs))
     return w
 
@@ -230,6 +230,23 @@ def test_attention_block_table_beyond_lds(bs, prefix, lens):
     assert dw.bt.shape[1] > 2048
     assert int(dw.status.item()) == 0
     check(dw, qb, got, 8, 8, layers, "cpu")
+
+
+@pytest.mark.parametrize("H,hq,q_len,theta", [
+    (4, 28, 12, 1e6),   # Qwen2.5-7B grouping (7 query heads per KV head): 84 rows, the
+                        # 64-row block boundary falls inside query token 9's heads
+    (8, 32, 16, 1e6),   # Mistral-7B grouping and RoPE base
+])
+def test_attention_evaluated_model_shapes(H, hq, q_len, theta):
+    """Query prefill in the KV shapes of the other models the InferScale page
+    evaluates (Qwen2.5-7B, Mistral-7B; D 128)."""
+    rng = np.random.default_rng(H * 100 + hq)
+    lens = [rng.integers(20, 61, size=6), rng.integers(20, 61, size=3)]
+    w = context_workload(f"attn_models_{H}_{hq}", 2, H, 128, 16, 64, lens, q_len, n_req=2,
+                         seed=hq, theta=theta)
+    dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu")
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, q_len, hq, layers, "cpu")
 
 
 def test_attention_ragged_query_lengths():

@@ -394,6 +394,22 @@ def test_edge_case(case, path):
     assert dw.count_non_sentinel() == expect
 
 
+@pytest.mark.parametrize("path", ["host", "device"])
+@pytest.mark.parametrize("name,L,H,theta", [("qwen25_7b_kv", 28, 4, 1e6),
+                                            ("mistral_7b_kv", 32, 8, 1e6)])
+def test_evaluated_model_kv_shapes(name, L, H, theta, path):
+    """The KV shapes of the other models the InferScale page evaluates
+    (Qwen2.5-7B: 28 layers, 4 KV heads; Mistral-7B: 32 layers, 8 KV heads;
+    D 128, RoPE base 1e6), 12 facts of 20-60 tokens after a 64-token prefix,
+    full compare against the oracle."""
+    rng = np.random.default_rng(L * 10 + H)
+    facts = {f: int(rng.integers(20, 61)) for f in range(40)}
+    ids = [int(x) for x in rng.choice(40, size=12, replace=False)]
+    w = custom_workload(name, L, H, 128, 16, facts, [(ids, 64)], theta=theta, num_blocks=1024)
+    dw, rep, _ = run_full(w, gen_device="cuda", path=path)
+    assert dw.count_non_sentinel() == 2 * L * w.n_tokens * H * 128
+
+
 def test_zero_tokens_is_noop():
     w = custom_workload("zero", 2, 8, 128, 16, {0: 5}, [([0], 3)])
     dw = harness.DeviceWorkload(w)
