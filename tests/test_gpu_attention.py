@@ -333,15 +333,17 @@ def test_attention_query_positions_out_of_range_are_reported():
     assert np.array_equal(got[:, 2], ref[:, 2])
 
 
-@pytest.mark.parametrize("name,n_pairs", [("llama3_8b_batch64_k50", 24),
-                                          ("llama3_70b_batch16_k50", 16)])
-def test_attention_full_size_sampled(name, n_pairs):
+@pytest.mark.parametrize("name,n_pairs,layout", [("llama3_8b_batch64_k50", 24, 0),
+                                                 ("llama3_70b_batch16_k50", 16, 0),
+                                                 ("llama3_8b_batch64_k50", 12, 1)])
+def test_attention_full_size_sampled(name, n_pairs, layout):
     """The launch the bench times: the whole batch injected by the device
     path into a zeroed cache, then one attend_paged over every request's
     whole context (16 query tokens = the context's last 16 positions, 4 query
     heads per KV head, all layers); sampled (layer, request) outputs against
-    the oracle's attention over the same cache contents."""
-    spec = workloads.SPECS[name]
+    the oracle's attention over the same cache contents.  layout 1: the HND
+    cache layout."""
+    spec = workloads.dataclasses.replace(workloads.SPECS[name], cache_layout=layout)
     w0 = workloads.make(spec)
     nb = harness.fit_num_blocks(spec, 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes +
                                 (3 << 30))
