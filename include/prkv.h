@@ -336,12 +336,14 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
  * cache are bf16; q and the probabilities are carried as bf16 hi + lo pairs
  * into the matrix cores, so the result is accurate to fp32 rounding.
  * Limits: head_dim 64 or 128; q_len <= max_position.  A block table of up
- * to 2048 entries is staged in LDS, a longer one read from device memory.  Rows (query token, query head) are taken 64
- * at a time per (layer, request, KV head): a query of q_len * (num_q_heads /
- * H) <= 64 rows reads its context once, a longer one once per 64 rows.  Positions whose block is missing
- * from the table are masked and set bit 4 of d_status; a request whose query
- * positions do not lie in [0, max_position) sets bit 2 and gets output 0;
- * a q_lens value outside [0, q_len] sets bit 8 and is clamped.
+ * to 2048 entries is staged in LDS, a longer one read from device memory.
+ * Rows (query token, query head) are taken 64 at a time per (layer,
+ * request, KV head): a query of q_len * (num_q_heads / H) <= 64 rows reads
+ * its context once, a longer one once per 64 rows.
+ * Status (d_status, optional): positions whose block is missing from the
+ * table are masked and set bit 4; a request whose query positions do not
+ * lie in [0, max_position) sets bit 2 and gets output 0; a q_lens value
+ * outside [0, q_len] sets bit 8 and is clamped.
  * One kernel launch on `stream`, asynchronous. */
 typedef struct prkv_attn_batch {
   int32_t n_req;
