@@ -82,26 +82,35 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
     q[j] = (j < CHUNKS - 1 || tail_in) ? *reinterpret_cast<const u32x4*>(qrow + 512 * j) : zero;
   const uint16_t* base = p.fact_emb + (int64_t(s) * p.facts_per_store) * p.dim + lane * 8;
   const int f1 = min(f0 + kFactsPerWave, p.facts_per_store);
-  for (int f = f0; f < f1; ++f) {
-    const uint16_t* row = base + int64_t(f) * p.dim;
-    u32x4 e[CHUNKS];
+  // G facts' rows are loaded together before any is reduced, so G rows per
+  // wave are in flight (G * CHUNKS * 4 VGPRs)
+  constexpr int G = CHUNKS <= 2 ? 8 : (CHUNKS <= 4 ? 4 : 2);
+  for (int g0 = f0; g0 < f1; g0 += G) {
+    u32x4 e[G][CHUNKS];
 #pragma unroll
-    for (int j = 0; j < CHUNKS; ++j)
-      e[j] = (j < CHUNKS - 1 || tail_in)
-                 ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 512 * j))
-                 : zero;
-    double acc = 0.0;
+    for (int i = 0; i < G; ++i) {
+      const uint16_t* row = base + int64_t(g0 + i < f1 ? g0 + i : f0) * p.dim;
 #pragma unroll
-    for (int j = 0; j < CHUNKS; ++j) {
-#pragma unroll
-      for (int d = 0; d < 4; ++d) {
-        acc = __builtin_fma(bf16_lo(q[j][d]), bf16_lo(e[j][d]), acc);
-        acc = __builtin_fma(bf16_hi(q[j][d]), bf16_hi(e[j][d]), acc);
-      }
+      for (int j = 0; j < CHUNKS; ++j)
+        e[i][j] = (j < CHUNKS - 1 || tail_in)
+                      ? __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(row + 512 * j))
+                      : zero;
     }
 #pragma unroll
-    for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
-    if (lane == 0) p.scores[int64_t(r) * p.facts_per_store + f] = acc;
+    for (int i = 0; i < G; ++i) {
+      double acc = 0.0;
+#pragma unroll
+      for (int j = 0; j < CHUNKS; ++j) {
+#pragma unroll
+        for (int d = 0; d < 4; ++d) {
+          acc = __builtin_fma(bf16_lo(q[j][d]), bf16_lo(e[i][j][d]), acc);
+          acc = __builtin_fma(bf16_hi(q[j][d]), bf16_hi(e[i][j][d]), acc);
+        }
+      }
+#pragma unroll
+      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+      if (lane == 0 && g0 + i < f1) p.scores[int64_t(r) * p.facts_per_store + g0 + i] = acc;
+    }
   }
 }
 
