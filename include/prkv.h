@@ -310,8 +310,10 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
  * int32 [n_req][k], global ids store * facts_per_store + fact, best first
  * (higher score, then smaller id); d_scores: optional device double
  * [n_req][k].  A request with an out-of-range store gets ids -1 and sets
- * bit 64 in d_status.  d_workspace: device, retrieve_workspace_bytes,
- * 8-byte aligned.  Two kernels on `stream`, asynchronous.  The ids can be
+ * bit 64 in d_status.  d_workspace: device, retrieve_workspace_bytes
+ * (scores, plus partial top-64 lists when few requests have many facts),
+ * 8-byte aligned.  Two kernels on `stream` (scores, top-k), three when the
+ * top-k of a request is split over several workgroups; asynchronous.  The ids can be
  * passed straight to inject_topk_device (req_fact_ptr[r] = r * k). */
 int retrieve_workspace_bytes(int32_t n_req, int32_t facts_per_store, size_t* bytes);
 int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_store,

@@ -19,15 +19,19 @@
 // product by ~1e-16 relative.  HBM bound (the embeddings are read once);
 // no MFMA: one query per store is a matrix-vector product.
 //
-// topk_kernel: one 1024-lane workgroup per request.  Each wave streams
-// 64-score chunks, sorts a chunk with an in-register bitonic network and
-// merges it into its running top-64 (elementwise best of the list and the
-// reversed chunk, then a bitonic merge); the 16 wave lists are merged in LDS
-// as a tree (4 rounds).
+// topk_kernel: 1024-lane workgroups, one per request, or up to 16 per
+// request when few requests have many facts (each takes a slice of the
+// scores).  Each wave streams 64-score chunks, sorts a chunk with an
+// in-register bitonic network and merges it into its running top-64
+// (elementwise best of the list and the reversed chunk, then a bitonic
+// merge); the 16 wave lists are merged in LDS as a tree (4 rounds).  With
+// several slices, topk_merge_kernel merges their top-64 lists the same way
+// (k <= 64, so the request's best k are among them).
 // Order: higher score first, then smaller fact id, so ties are deterministic.
 
 #include <hip/hip_runtime.h>
 
+#include <algorithm>
 #include <cstdint>
 
 #include "prkv_internal.h"
@@ -41,6 +45,7 @@ constexpr int kScoreWaves = 4;
 constexpr int kFactsPerWave = 8;
 constexpr int kTopkThreads = 1024;
 constexpr int kMaxK = 64;
+constexpr int kMaxList = 64;   // candidates per partial list (one per lane)
 
 struct ScoreParams {
   const uint16_t* fact_emb;   // [n_stores][F][dim]
@@ -185,37 +190,47 @@ struct TopkParams {
   const int32_t* req_store;
   int32_t* fact_ids;     // [n_req][k]
   double* out_scores;    // [n_req][k], optional
+  uint64_t* part_key;    // [n_req][parts][64] partial lists (parts > 1), workspace
+  int32_t* part_id;
   int32_t n_req, n_stores, facts_per_store, k;
+  int32_t parts;         // workgroups per request in the first pass
 };
 
-__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
-  __shared__ uint64_t s_key[kTopkThreads];
-  __shared__ int32_t s_id[kTopkThreads];
-  const int r = blockIdx.x;
-  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
-  const int nw = kTopkThreads / kWave;
-  const int s = p.req_store[r];
-  const bool ok = s >= 0 && s < p.n_stores;
-  const double* sc = p.scores + int64_t(r) * p.facts_per_store;
-  const Cand worst = {0, INT32_MAX};
-  Cand best = worst;
-  const int F = ok ? p.facts_per_store : 0;
-  for (int c0 = wave * kWave; c0 < F; c0 += nw * kWave) {
-    const int f = c0 + lane;
-    Cand v = worst;
-    if (f < F) {
-      v.key = order_key(sc[f]);
-      v.id = f;
-    }
-    v = sort64(v, lane);
-    best = merge64(best, v, lane);
+// Score slices per request for the first top-k pass: enough workgroups to
+// spread a few large requests over the chip (up to 16, at least 1024 scores
+// each); one when the requests alone fill it.
+inline int topk_parts(int64_t n_req, int64_t facts_per_store) {
+  if (n_req <= 0) return 1;
+  int parts = int(std::min<int64_t>(16, (256 + n_req - 1) / n_req));
+  while (parts > 1 && facts_per_store / parts < 1024) parts /= 2;
+  return parts < 1 ? 1 : parts;
+}
+
+// Byte offsets of the parts of the retrieval workspace: scores at 0, then
+// the partial keys and ids (256-byte aligned), and the total.
+struct RetrieveWs {
+  size_t keys, ids, total;
+  RetrieveWs(int64_t n_req, int64_t facts_per_store) {
+    auto up = [](size_t v) { return (v + 255u) / 256u * 256u; };
+    const size_t scores = size_t(n_req) * size_t(facts_per_store) * sizeof(double);
+    const int parts = topk_parts(n_req, facts_per_store);
+    const size_t n = parts > 1 ? size_t(n_req) * size_t(parts) * kMaxList : 0;
+    keys = up(scores);
+    ids = keys + up(n * sizeof(uint64_t));
+    total = parts > 1 ? ids + n * sizeof(int32_t) : scores;
   }
+};
+
+// The waves' sorted lists (one Cand per lane) merged in LDS as a tree; wave 0
+// returns the best 64 of the workgroup, best first.  In each round wave
+// w < half merges in the list of wave w + half (it writes only its own slots,
+// which no wave reads in that round).
+__device__ Cand block_merge(Cand best, uint64_t* s_key, int32_t* s_id) {
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  constexpr int nw = kTopkThreads / kWave;
   s_key[threadIdx.x] = best.key;
   s_id[threadIdx.x] = best.id;
   __syncthreads();
-  // tree merge of the wave lists: in each round wave w < half merges in the
-  // list of wave w + half (it writes only its own slots, which no wave reads
-  // in that round)
   for (int half = nw / 2; half >= 1; half /= 2) {
     if (wave < half) {
       const Cand mine = {s_key[threadIdx.x], s_id[threadIdx.x]};
@@ -226,15 +241,72 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
     }
     __syncthreads();
   }
-  if (wave == 0) {
-    const Cand acc = {s_key[lane], s_id[lane]};
-    if (lane < p.k) {
-      const int64_t o = int64_t(r) * p.k + lane;
-      const bool real = ok && acc.id != INT32_MAX;
-      p.fact_ids[o] = real ? s * p.facts_per_store + acc.id : -1;
-      if (p.out_scores) p.out_scores[o] = real ? key_value(acc.key) : 0.0;
-    }
+  return Cand{s_key[lane], s_id[lane]};
+}
+
+// Lane i < k of wave 0 writes the request's i-th best fact (global id) and
+// score.
+__device__ void write_topk(const TopkParams& p, int r, int s, bool ok, const Cand& acc) {
+  const int lane = threadIdx.x % kWave;
+  if (threadIdx.x < kWave && lane < p.k) {
+    const int64_t o = int64_t(r) * p.k + lane;
+    const bool real = ok && acc.id != INT32_MAX;
+    p.fact_ids[o] = real ? s * p.facts_per_store + acc.id : -1;
+    if (p.out_scores) p.out_scores[o] = real ? key_value(acc.key) : 0.0;
   }
+}
+
+// First pass: workgroup (r, part) keeps the best 64 of its slice of request
+// r's scores; with one part it writes the result, otherwise its list.
+__global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
+  __shared__ uint64_t s_key[kTopkThreads];
+  __shared__ int32_t s_id[kTopkThreads];
+  const int r = blockIdx.x / p.parts, part = blockIdx.x % p.parts;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int nw = kTopkThreads / kWave;
+  const int s = p.req_store[r];
+  const bool ok = s >= 0 && s < p.n_stores;
+  const double* sc = p.scores + int64_t(r) * p.facts_per_store;
+  const Cand worst = {0, INT32_MAX};
+  Cand best = worst;
+  const int F = ok ? p.facts_per_store : 0;
+  const int lo = int(int64_t(F) * part / p.parts), hi = int(int64_t(F) * (part + 1) / p.parts);
+  for (int c0 = lo + wave * kWave; c0 < hi; c0 += nw * kWave) {
+    const int f = c0 + lane;
+    Cand v = worst;
+    if (f < hi) {
+      v.key = order_key(sc[f]);
+      v.id = f;
+    }
+    v = sort64(v, lane);
+    best = merge64(best, v, lane);
+  }
+  const Cand acc = block_merge(best, s_key, s_id);
+  if (p.parts == 1) {
+    write_topk(p, r, s, ok, acc);
+  } else if (threadIdx.x < kWave) {
+    const int64_t o = (int64_t(r) * p.parts + part) * kMaxList + lane;
+    p.part_key[o] = acc.key;
+    p.part_id[o] = acc.id;
+  }
+}
+
+// Second pass (parts > 1): one workgroup per request; wave w < parts loads
+// list w (sorted best first) and the lists are merged as in the first pass.
+__global__ __launch_bounds__(kTopkThreads) void topk_merge_kernel(TopkParams p) {
+  __shared__ uint64_t s_key[kTopkThreads];
+  __shared__ int32_t s_id[kTopkThreads];
+  const int r = blockIdx.x;
+  const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
+  const int s = p.req_store[r];
+  const bool ok = s >= 0 && s < p.n_stores;
+  Cand best = {0, INT32_MAX};
+  if (wave < p.parts) {
+    const int64_t o = (int64_t(r) * p.parts + wave) * kMaxList + lane;
+    best.key = p.part_key[o];
+    best.id = p.part_id[o];
+  }
+  write_topk(p, r, s, ok, block_merge(best, s_key, s_id));
 }
 
 template <int CHUNKS>
@@ -255,7 +327,7 @@ int retrieve_workspace_bytes(int32_t n_req, int32_t facts_per_store, size_t* byt
   if (!bytes) return prkv::fail(PRKV_ERR_INVALID_ARG, "bytes is NULL");
   if (n_req < 0 || facts_per_store < 0)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "negative size");
-  *bytes = size_t(n_req) * size_t(facts_per_store) * sizeof(double);
+  *bytes = RetrieveWs(n_req, facts_per_store).total;
   return PRKV_OK;
 }
 
@@ -282,7 +354,8 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
       (reinterpret_cast<uintptr_t>(d_req_store) | reinterpret_cast<uintptr_t>(d_fact_ids) |
        reinterpret_cast<uintptr_t>(d_status)) & 3u)
     return prkv::fail(PRKV_ERR_ALIGNMENT, "workspace/scores 8-byte, int32 arrays 4-byte aligned");
-  const size_t need = size_t(n_req) * size_t(facts_per_store) * sizeof(double);
+  const RetrieveWs wl(n_req, facts_per_store);
+  const size_t need = wl.total;
   if (workspace_bytes < need)
     return prkv::fail(PRKV_ERR_BUFFER_TOO_SMALL, "workspace needs %zu bytes, got %zu", need,
                       workspace_bytes);
@@ -323,7 +396,15 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
   tp.n_stores = n_stores;
   tp.facts_per_store = facts_per_store;
   tp.k = k;
-  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(n_req)), dim3(kTopkThreads), 0, s, tp);
+  tp.parts = topk_parts(n_req, facts_per_store);
+  if (int64_t(n_req) * tp.parts > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "top-k grid too large");
+  tp.part_key = reinterpret_cast<uint64_t*>(static_cast<char*>(d_workspace) + wl.keys);
+  tp.part_id = reinterpret_cast<int32_t*>(static_cast<char*>(d_workspace) + wl.ids);
+  hipLaunchKernelGGL(topk_kernel, dim3(unsigned(int64_t(n_req) * tp.parts)), dim3(kTopkThreads), 0,
+                     s, tp);
+  if (tp.parts > 1)
+    hipLaunchKernelGGL(topk_merge_kernel, dim3(unsigned(n_req)), dim3(kTopkThreads), 0, s, tp);
   e = hipGetLastError();
   if (e != hipSuccess) return prkv::fail(PRKV_ERR_HIP, "top-k launch: %s", hipGetErrorString(e));
   return PRKV_OK;

@@ -101,23 +101,28 @@ def test_retrieve_shapes(F, k, dim):
                          q.cpu().numpy().view(np.uint16), req_store, F, k, ids, sc)
 
 
-def test_retrieve_exact_ties_order_by_id():
-    """Duplicate embeddings score identically: the smaller fact id ranks first."""
-    F, dim, k = 300, 512, 20
+@pytest.mark.parametrize("F", [300, 16384])
+def test_retrieve_exact_ties_order_by_id(F):
+    """Duplicate embeddings score identically: the smaller fact id ranks first
+    (F = 16384: one request's scores are split over 16 top-k workgroups, and
+    the duplicates fall in different slices)."""
+    dim, k = 512, 20
     g = torch.Generator(device="cuda")
     g.manual_seed(5)
     base = (torch.randn((F, dim), generator=g, device="cuda") / dim ** 0.5).to(torch.bfloat16)
-    base[150:] = base[:150]          # fact f and f+150 are identical
-    q = base[10:11].clone()          # query equals fact 10 (and 160)
+    h = F // 2
+    base[h:2 * h] = base[:h]         # fact f and f + F/2 are identical
+    q = base[10:11].clone()          # query equals fact 10 (and 10 + F/2)
     emb = base.view(torch.int16).contiguous()
     ids, sc, st = run_retrieve(emb, q.view(torch.int16), np.array([0], np.int32), F, k, dim, 1)
-    assert ids[0][0] == 10 and ids[0][1] == 160
+    assert ids[0][0] == 10 and ids[0][1] == 10 + h
     check_against_oracle(emb.cpu().numpy().view(np.uint16)[None], q.view(torch.int16).cpu()
                          .numpy().view(np.uint16), [0], F, k, ids, sc)
 
 
-def test_retrieve_bad_store_reports():
-    F, dim, k = 50, 512, 5
+@pytest.mark.parametrize("F", [50, 8192])
+def test_retrieve_bad_store_reports(F):
+    dim, k = 512, 5
     emb = torch.zeros((F, dim), dtype=torch.int16, device="cuda")
     q = torch.zeros((2, dim), dtype=torch.int16, device="cuda")
     ids, sc, st = run_retrieve(emb, q, np.array([0, 3], np.int32), F, k, dim, 1)

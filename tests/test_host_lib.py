@@ -343,6 +343,12 @@ def test_retrieve_argument_errors(kw, name):
 
 def test_retrieve_workspace_bytes():
     assert prkv.retrieve_workspace_bytes(64, 2000) == 64 * 2000 * 8
+    # few requests with many facts: 16 score slices each, partial top-64
+    # lists (8-byte keys, then 4-byte ids, 256-byte aligned) after the scores
+    scores = 16 * 20000 * 8
+    n = 16 * 16 * 64
+    assert prkv.retrieve_workspace_bytes(16, 20000) == scores + n * 8 + n * 4
+    assert prkv.retrieve_workspace_bytes(1, 1023) == 1023 * 8   # slices need >= 1024 scores
 
 
 def test_missing_library_fails_loudly(monkeypatch, tmp_path):
