@@ -206,6 +206,9 @@ constexpr int kFuseReqs = kThreads;
 // than the two extra launches (measured on MI355X: fused 4 % faster at 50
 // facts / 1.9k tokens, 0.5-2 % slower from 100 facts / 3.8k tokens up).
 constexpr int64_t kFuseTokens = 4096;
+// Up to this many expected tokens the fused grid is capped at one round of
+// resident workgroups (launch_inject).
+constexpr int64_t kFuseCapTokens = 1024;
 
 struct FusedLds {
   int64_t pos0[kFuseFacts];      // serving position of the fact's first token
@@ -821,6 +824,15 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
     const int64_t spread =
         std::min<int64_t>(want_waves / kWavesPerGroup * 2, tiles_bound * iters);
     if (grid < spread) grid = spread;
+  }
+  // A fused launch's workgroups each rebuild the batch plan before they know
+  // whether a tile is left for them, so a small batch gets at most one
+  // residency round of them (four per CU); its tiles are then walked by the
+  // grid stride (same-process A/B: k = 5 -8 %, k = 10 -1.4 %, k = 20 -2.9 %;
+  // at k = 50, 2k tokens, +1 %, so larger batches keep the wider grid).
+  if (fused && expect_tokens >= 0 && expect_tokens <= kFuseCapTokens) {
+    const int64_t cap = int64_t(compute_units()) * 4;
+    if (grid > cap) grid = cap;
   }
   size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
   if (fused)  // the plan follows the metadata at the next 16-byte boundary
