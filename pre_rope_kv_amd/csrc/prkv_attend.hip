@@ -49,6 +49,7 @@
 
 #include <hip/hip_runtime.h>
 
+#include <atomic>
 #include <cmath>
 #include <cstdint>
 
@@ -127,17 +128,23 @@ __device__ __forceinline__ void load_lds16(const void* src, uint32_t lds_addr) {
 
 // BT_LDS: the request's block table is staged in LDS (bt_stride <= kBtLds);
 // otherwise it is read from device memory.
-template <int D, int STYLE, bool BT_LDS>
-__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) void attend_kernel(
-    AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
+// KG: key groups.  With KG > 1 (a grid too small to fill the chip, e.g. one
+// request) the workgroup has KG groups of 4 waves with the same rows; group
+// g takes key tiles g, g + KG, ... through its own LDS ring, and the groups'
+// (max, sum, O) are merged in LDS at the end, so a CU has KG times as many
+// tiles in flight for the one workgroup it holds.
+template <int D, int STYLE, bool BT_LDS, int KG>
+__global__ __launch_bounds__(kThreads * KG) __attribute__((amdgpu_waves_per_eu(3))) void
+attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
+  constexpr int NT = kThreads * KG;      // threads of the workgroup
   constexpr int KB = D / 32;            // 32-wide k-blocks of Q K^T
   constexpr int MT = D / 16;            // 16-dim tiles of O^T
   constexpr int ROWB = D * 2;           // bytes per K or V row
   constexpr int DC = D / 8;             // 16-byte chunks per row
   constexpr int TILEB = kTile * ROWB;   // bytes per K or V tile
   // a ring of tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
-  __shared__ __align__(1024) unsigned char s_kv[kStages][2][TILEB];
-  __shared__ __align__(16) int s_slots[kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
+  __shared__ __align__(1024) unsigned char s_kv[KG][kStages][2][TILEB];
+  __shared__ __align__(16) int s_slots[KG][kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
   extern __shared__ int s_bt[];         // the request's block table (bt_stride <= kBtLds)
 
   // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so
@@ -151,7 +158,10 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   const int g = unit % p.num_kv_heads;
   const int r = (unit / p.num_kv_heads) % p.n_req;
   const int layer = unit / (p.num_kv_heads * p.n_req);
-  const int wave = threadIdx.x / kWave, lane = threadIdx.x % kWave;
+  const int lane = threadIdx.x % kWave;
+  const int kg = int(threadIdx.x) / kThreads;     // key group
+  const int lt = int(threadIdx.x) % kThreads;     // thread within the group
+  const int wave = lt / kWave;                    // wave within the group
   const int a = lane / 16, c16 = lane % 16;
   // This request's query tokens: q_lens[r] (a value outside [0, q_len] is
   // reported, status bit 8, and clamped), else q_len.
@@ -279,7 +289,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // from global memory, where the slots are computed kStages tiles ahead.
   if constexpr (BT_LDS) {
     if (int(threadIdx.x) < nb) s_bt[threadIdx.x] = bt_first;
-    for (int i = threadIdx.x + kThreads; i < nb; i += kThreads) s_bt[i] = btr[i];
+    for (int i = threadIdx.x + NT; i < nb; i += NT) s_bt[i] = btr[i];
   }
   __syncthreads();
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
@@ -296,7 +306,7 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   // no mask at all (every key is visible to every row).
   int bad = 0;
   const int nblk = ctx > 0 ? (ctx - 1) / p.block_size + 1 : 0;
-  for (int i = threadIdx.x; i < nblk; i += kThreads) {
+  for (int i = threadIdx.x; i < nblk; i += NT) {
     const int64_t blk = i < nb ? (BT_LDS ? s_bt[i] : btr[i]) : -1;
     bad |= blk < 0 || blk >= p.num_blocks;
   }
@@ -314,12 +324,13 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   auto swk = [](int k) { return D == 128 ? k % 16 : (k / 2) % 8; };
   auto swv = [](int k) { return D == 128 ? 2 * (k % 8) : 2 * ((k / 2) % 4); };
 
-  // The slots of a tile, one per key, by the first kTile lanes kStages tiles
-  // ahead, in a ring of kSlotRing buffers.
-  auto fill_slots = [&](int t) {
-    if (threadIdx.x < kTile) {
-      const int pos = t * kTile + threadIdx.x;
-      s_slots[t % kSlotRing][threadIdx.x] = pos < ctx ? slot_of(pos) : -1;
+  // Group kg's i-th tile is key tile i * KG + kg; group-local index i runs
+  // its ring.  The slots of a tile, one per key, by the group's first kTile
+  // lanes kStages tiles ahead, in a ring of kSlotRing buffers.
+  auto fill_slots = [&](int i) {
+    if (lt < kTile) {
+      const int pos = (i * KG + kg) * kTile + lt;
+      s_slots[kg][i % kSlotRing][lt] = pos < ctx ? slot_of(pos) : -1;
     }
   };
   // Issue the direct loads of tile t into ring buffer t % kStages.
@@ -331,10 +342,11 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   constexpr int NI = kTile * DC / 64 / 4;       // instructions per wave per tile, for K and for V
   constexpr unsigned LPT = 2 * NI;              // loads per wave per tile
   static_assert(NI >= 1 && kTile * DC % 256 == 0, "a tile must split over the 4 waves");
-  const uint32_t kv_lds = uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(&s_kv[0][0][0])));
-  auto issue = [&](int t) {
-    const int* sl = s_slots[t % kSlotRing];
-    const uint32_t kd = kv_lds + uint32_t(t % kStages) * (2 * TILEB);
+  const uint32_t kv_lds =
+      uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(&s_kv[kg][0][0][0])));
+  auto issue = [&](int ti) {
+    const int* sl = s_slots[kg][ti % kSlotRing];
+    const uint32_t kd = kv_lds + uint32_t(ti % kStages) * (2 * TILEB);
     const uint32_t vd = kd + TILEB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
@@ -355,14 +367,14 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
       load_lds16(vl + off + 8 * (pk ^ swv(k)), vd + n * 1024);
     }
   };
-  // Zero the K and V rows of masked keys of the tile in buffer `buf`.
+  // Zero the K and V rows of masked keys of the group's tile in buffer `buf`.
   auto zero_masked = [&](const int* sl, int buf) {
     const u32x4 zero = {0u, 0u, 0u, 0u};
-    for (int e = threadIdx.x; e < kTile * DC; e += kThreads) {
+    for (int e = lt; e < kTile * DC; e += kThreads) {
       const int k = e / DC;
       if (sl[k] < 0) {
-        *reinterpret_cast<u32x4*>(s_kv[buf][0] + k * ROWB + 16 * (e % DC)) = zero;
-        *reinterpret_cast<u32x4*>(s_kv[buf][1] + k * ROWB + 16 * (e % DC)) = zero;
+        *reinterpret_cast<u32x4*>(s_kv[kg][buf][0] + k * ROWB + 16 * (e % DC)) = zero;
+        *reinterpret_cast<u32x4*>(s_kv[kg][buf][1] + k * ROWB + 16 * (e % DC)) = zero;
       }
     }
   };
@@ -458,37 +470,115 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
     }
   };
 
-  // Pipeline: tiles t+1 .. t+kStages-1 stream into the ring while tile t is
-  // computed; slots run kStages tiles ahead.
-  if (ntiles > 0) {
-    for (int u = 0; u < kStages && u < ntiles; ++u) fill_slots(u);
-    __syncthreads();
-    for (int u = 0; u < kStages - 1 && u < ntiles; ++u) issue(u);
-  }
-  for (int t = 0; t < ntiles; ++t) {
-    const int base = t * kTile;
-    // this wave's loads of tile t have landed (later tiles may still fly)
-    const int later = min(kStages - 2, ntiles - 1 - t);
-    static_assert(kStages <= 4, "extend the waits below");
-    if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
-    else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
-    else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
-    __syncthreads();                 // ... and every wave's; tile t-1 is consumed
-    __asm__ volatile("" ::: "memory");
-    if (t + kStages < ntiles) fill_slots(t + kStages);
-    if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-    const int* sl = s_slots[t % kSlotRing];
-    const bool masked = any_missing || base + kTile - 1 > q_block0;
-    if (masked) {
-      zero_masked(sl, t % kStages);
+  if constexpr (KG == 1) {
+    // Pipeline: tiles t+1 .. t+kStages-1 stream into the ring while tile t
+    // is computed; slots run kStages tiles ahead.
+    if (ntiles > 0) {
+      for (int u = 0; u < kStages && u < ntiles; ++u) fill_slots(u);
       __syncthreads();
+      for (int u = 0; u < kStages - 1 && u < ntiles; ++u) issue(u);
     }
-    compute(s_kv[t % kStages][0], s_kv[t % kStages][1], base, sl, masked);
+    for (int t = 0; t < ntiles; ++t) {
+      const int base = t * kTile;
+      // this wave's loads of tile t have landed (later tiles may still fly)
+      const int later = min(kStages - 2, ntiles - 1 - t);
+      static_assert(kStages <= 4, "extend the waits below");
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();                 // ... and every wave's; tile t-1 is consumed
+      __asm__ volatile("" ::: "memory");
+      if (t + kStages < ntiles) fill_slots(t + kStages);
+      if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+      const int* sl = s_slots[0][t % kSlotRing];
+      const bool masked = any_missing || base + kTile - 1 > q_block0;
+      if (masked) {
+        zero_masked(sl, t % kStages);
+        __syncthreads();
+      }
+      compute(s_kv[0][t % kStages][0], s_kv[0][t % kStages][1], base, sl, masked);
+    }
+  } else {
+    // Pipeline (per key group, on its own tiles): tiles i+1 .. i+kStages-1
+    // stream into the group's ring while tile i is computed; slots run kStages
+    // tiles ahead.  Every group runs n_iter iterations so that the barriers
+    // match; a group whose tiles have run out only takes part in them.
+    const int n_mine = ntiles > kg ? (ntiles - kg + KG - 1) / KG : 0;   // this group's tiles
+    const int n_iter = (ntiles + KG - 1) / KG;
+    if (n_iter > 0) {
+      for (int u = 0; u < kStages && u < n_mine; ++u) fill_slots(u);
+      __syncthreads();
+      for (int u = 0; u < kStages - 1 && u < n_mine; ++u) issue(u);
+    }
+    for (int i = 0; i < n_iter; ++i) {
+      const int base = (i * KG + kg) * kTile;
+      const bool mine = i < n_mine;
+      // this wave's loads of tile i have landed (later tiles may still fly)
+      const int later = mine ? min(kStages - 2, n_mine - 1 - i) : 0;
+      static_assert(kStages <= 4, "extend the waits below");
+      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
+      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
+      __syncthreads();                 // ... and every wave's; tile i-1 is consumed
+      __asm__ volatile("" ::: "memory");
+      if (i + kStages < n_mine) fill_slots(i + kStages);
+      if (i + kStages - 1 < n_mine) issue(i + kStages - 1);
+      const int* sl = s_slots[kg][i % kSlotRing];
+      // Zeroing masked rows is decided for the whole workgroup (the barrier
+      // after it must be reached by every wave): by the iteration's last tile.
+      const bool any_masked = any_missing || (i + 1) * KG * kTile - 1 > q_block0;
+      if (any_masked) {
+        if (mine) zero_masked(sl, i % kStages);
+        __syncthreads();
+      }
+      const bool masked = any_missing || base + kTile - 1 > q_block0;
+      if (mine) compute(s_kv[kg][i % kStages][0], s_kv[kg][i % kStages][1], base, sl, masked);
+    }
+
   }
 
   // normalise and write O[layer][r][qi][hq][d], d = 16mt + 4a + i
   float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
   l_tot += __shfl_xor(l_tot, 32, kWave);
+  if constexpr (KG > 1) {
+    // Groups 1.. hand (max, sum, O) to group 0 through LDS (the rings are
+    // free: every group has waited for and consumed its last tile), and
+    // group 0 rescales all to the largest reference and adds them up.
+    constexpr int NF = 2 + 4 * MT;                 // floats per thread
+    static_assert(sizeof(s_kv) >= size_t(KG - 1) * NF * kThreads * sizeof(float),
+                  "merge scratch must fit in the rings");
+    float* scratch = reinterpret_cast<float*>(&s_kv[0][0][0][0]);
+    __syncthreads();
+    if (kg > 0) {
+      float* my = scratch + size_t(kg - 1) * NF * kThreads;
+      my[lt] = m_run;
+      my[kThreads + lt] = l_tot;
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) my[(2 + 4 * mt + e) * kThreads + lt] = o[mt][e];
+    }
+    __syncthreads();
+    if (kg > 0) return;
+    float m_all = m_run;
+#pragma unroll
+    for (int g2 = 1; g2 < KG; ++g2)
+      m_all = fmaxf(m_all, scratch[size_t(g2 - 1) * NF * kThreads + lt]);
+    const float w0 = m_all == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(m_run - m_all);
+    l_tot *= w0;
+#pragma unroll
+    for (int mt = 0; mt < MT; ++mt) o[mt] *= w0;
+#pragma unroll
+    for (int g2 = 1; g2 < KG; ++g2) {
+      const float* other = scratch + size_t(g2 - 1) * NF * kThreads;
+      const float wg = m_all == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(other[lt] - m_all);
+      l_tot += wg * other[kThreads + lt];
+#pragma unroll
+      for (int mt = 0; mt < MT; ++mt)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) o[mt][e] += wg * other[(2 + 4 * mt + e) * kThreads + lt];
+    }
+  }
   if (row_out) {
     const float inv = row_ok && l_tot > 0.f ? 1.f / l_tot : 0.f;
     float* orow = p.out + (((int64_t(layer) * p.n_req + r) * p.q_len + qi) * p.num_q_heads + hq) * D;
@@ -499,17 +589,47 @@ __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(3))) v
   }
 }
 
-template <int D, int STYLE>
-void launch_attend_style(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
-                         int64_t grid, hipStream_t s) {
+template <int D, int STYLE, int KG>
+void launch_attend_kg(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
+                      int64_t grid, hipStream_t s) {
   // the block table is the dynamic LDS: a short table leaves room for more
   // workgroups per CU
   if (p.bt_stride <= kBtLds)
-    hipLaunchKernelGGL((attend_kernel<D, STYLE, true>), dim3(unsigned(grid)), dim3(kThreads),
+    hipLaunchKernelGGL((attend_kernel<D, STYLE, true, KG>), dim3(unsigned(grid)),
+                       dim3(kThreads * KG),
                        size_t(p.bt_stride > 0 ? p.bt_stride : 1) * sizeof(int32_t), s, p, kc, vc);
   else
-    hipLaunchKernelGGL((attend_kernel<D, STYLE, false>), dim3(unsigned(grid)), dim3(kThreads),
-                       sizeof(int32_t), s, p, kc, vc);
+    hipLaunchKernelGGL((attend_kernel<D, STYLE, false, KG>), dim3(unsigned(grid)),
+                       dim3(kThreads * KG), sizeof(int32_t), s, p, kc, vc);
+}
+
+// Compute units of the current device (cached per device; 256 if unknown).
+int attend_compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+template <int D, int STYLE>
+void launch_attend_style(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
+                         int64_t grid, hipStream_t s) {
+  // A grid of at most one workgroup per CU (e.g. one request: L x H
+  // workgroups) leaves each CU one workgroup's tiles in flight: there, three
+  // key groups per workgroup (12 waves, three LDS rings) triple them.
+  if (grid <= attend_compute_units())
+    launch_attend_kg<D, STYLE, 3>(p, kc, vc, grid, s);
+  else
+    launch_attend_kg<D, STYLE, 1>(p, kc, vc, grid, s);
 }
 
 template <int D>
