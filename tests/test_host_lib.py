@@ -404,3 +404,80 @@ def test_duplicate_slot_reports_the_first_one(start0, start1, first_dup):
     # every bit set before the failure was cleared: the same blocks map cleanly now
     src, pos, slot = prkv.build_slot_mapping(st, [0, 1], [1], [start1], bt[1:], [2], 100, 8)
     assert slot.tolist() == [200 + q if q < 100 else 500 + q - 100 for q in range(start1, start1 + 90)]
+
+
+def test_build_slot_mapping_concurrent_calls_on_one_store():
+    """build_slot_mapping is documented safe to call concurrently on one store:
+    eight threads (ctypes releases the GIL during the call) map different
+    batches at once, some invalid; every valid result equals the same call
+    made alone, and every invalid one fails with its own error message
+    (last_error_string is per thread)."""
+    import threading
+
+    d = _desc(max_facts=400, capacity_rows=400 * 60, max_position=16384)
+    st = prkv.store_create(d)
+    rng = np.random.default_rng(11)
+    lengths = {}
+    for f in range(400):
+        lengths[f] = int(rng.integers(1, 60))
+        prkv.store_put_fact(st, f, lengths[f])
+
+    def batch(seed):
+        r = np.random.default_rng(seed)
+        n_req = int(r.integers(1, 6))
+        ptr, ids, start, tables, bt_len = [0], [], [], [], []
+        free = r.permutation(20000)
+        used = 0
+        for _ in range(n_req):
+            k = int(r.integers(1, 30))
+            fid = [int(x) for x in r.choice(400, size=k, replace=False)]
+            pre = int(r.integers(0, 200))
+            need = -(-(pre + sum(lengths[f] for f in fid)) // 16)
+            ids += fid
+            ptr.append(len(ids))
+            start.append(pre)
+            tables.append(free[used:used + need])
+            bt_len.append(need)
+            used += need
+        stride = max(bt_len)
+        bt = np.zeros((n_req, stride), np.int32)
+        for i, t in enumerate(tables):
+            bt[i, :len(t)] = t
+        bad = seed % 3 == 0
+        if bad:
+            ids[0] = 399 + 1000     # an id never stored
+        return (ptr, ids, start, bt, bt_len), bad
+
+    cases = [batch(s) for s in range(48)]
+    expected = []
+    for args, bad in cases:
+        if bad:
+            expected.append(None)
+        else:
+            expected.append(prkv.build_slot_mapping(st, *args, 16, 20000))
+
+    results = [None] * len(cases)
+
+    def worker(w):
+        for i in range(w, len(cases), 8):
+            args, bad = cases[i]
+            for _ in range(5):
+                try:
+                    got = prkv.build_slot_mapping(st, *args, 16, 20000)
+                    results[i] = ("ok", got)
+                except prkv.PrkvError as e:
+                    results[i] = ("err", e.name, str(e))
+
+    threads = [threading.Thread(target=worker, args=(w,)) for w in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    for i, ((args, bad), want) in enumerate(zip(cases, expected)):
+        if bad:
+            assert results[i][0] == "err" and results[i][1] == "UNKNOWN_FACT", i
+            assert "1399" in results[i][2], results[i][2]
+        else:
+            assert results[i][0] == "ok", results[i]
+            for g, e in zip(results[i][1], want):
+                assert np.array_equal(g, e), i
