@@ -20,7 +20,7 @@ from oracle import paged
 from pre_rope_kv_amd import harness, prkv, workloads
 
 from test_gpu_parity import (_release_device_memory, compare, custom_workload,  # noqa: F401
-                             oracle_images, written_mask)
+                             oracle_images, run_full, written_mask)
 
 pytestmark = pytest.mark.gpu
 
@@ -297,3 +297,60 @@ def test_random_small_batches_both_mappings(seed):
         _check(dw1, w)
     else:
         assert s1 != 0
+
+
+def test_two_streams_inject_concurrently():
+    """Two batches (the two halves of a batch's requests) injected at once on
+    two HIP streams, host-mapped through inject_topk and device-mapped
+    through inject_topk_device with separate workspaces: the cache equals one
+    launch of the whole batch, bit for bit, and matches the oracle."""
+    rng = np.random.default_rng(21)
+    facts = {f: int(rng.integers(5, 60)) for f in range(60)}
+    reqs = [([int(x) for x in rng.choice(60, size=int(rng.integers(3, 12)), replace=False)],
+             int(rng.integers(0, 100))) for _ in range(6)]
+    w = custom_workload("two_streams", 4, 8, 128, 16, facts, reqs, theta=5e5, num_blocks=1024)
+    dw, rep, (img_k, img_v, want_k, want_v) = run_full(w, path="host")
+    blocks = w.listed_blocks()
+    s1, s2 = torch.cuda.Stream(), torch.cuda.Stream()
+    n0 = sum(w.length_of(f) for ids, _ in reqs[:3] for f in ids)
+    n = dw.n_tokens
+    src, pos, slot = dw.d_map
+
+    # host-mapped: tokens of requests 0-2 on one stream, 3-5 on the other
+    dw.reset_cache()
+    torch.cuda.synchronize()
+    prkv.inject_topk(dw.store, n0, src[:n0], pos[:n0], slot[:n0], dw.k_layers(), dw.v_layers(),
+                     16, w.num_blocks, d_status=dw.status, stream=s1)
+    prkv.inject_topk(dw.store, n - n0, src[n0:], pos[n0:], slot[n0:], dw.k_layers(),
+                     dw.v_layers(), 16, w.num_blocks, d_status=dw.status, stream=s2)
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    got_k, got_v = dw.listed_blocks_host(blocks)
+    assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
+
+    # device-mapped: each half its own device batch and workspace
+    halves = []
+    for r0 in (0, 3):
+        part = reqs[r0:r0 + 3]
+        sub = custom_workload("two_streams", 4, 8, 128, 16, facts, part, theta=5e5,
+                              num_blocks=1024)
+        req_ptr, ids, start, _, _ = sub.csr()
+        bt = np.ascontiguousarray(dw.bt[r0:r0 + 3])
+        btl = np.ascontiguousarray(dw.bt_len[r0:r0 + 3])
+        d = [torch.from_numpy(np.ascontiguousarray(a)).cuda()
+             for a in (req_ptr, ids, start, bt, btl)]
+        max_tok = len(ids) * 60
+        ws_b = prkv.inject_device_workspace_bytes(len(ids), max_tok)
+        ws = torch.zeros(ws_b, dtype=torch.uint8, device="cuda")
+        b = prkv.device_batch(3, bt.shape[1], len(ids), max_tok, *d)
+        halves.append((b, ws, ws_b, d))
+    dw.setup_device_batch()
+    dw.reset_cache()
+    torch.cuda.synchronize()
+    for (b, ws, ws_b, _), s in zip(halves, (s1, s2)):
+        prkv.inject_topk_device(dw.store, dw.fact_table, b, dw.k_layers(), dw.v_layers(), 16,
+                                w.num_blocks, ws, ws_b, d_status=dw.status, stream=s)
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    got_k, got_v = dw.listed_blocks_host(blocks)
+    assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
