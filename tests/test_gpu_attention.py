@@ -314,6 +314,20 @@ def test_attention_ragged_query_lengths():
     assert np.array_equal(bad[:, 1:], got[:, 1:])
 
 
+@pytest.mark.parametrize("D,H,hq,q_len", [(64, 8, 32, 16), (128, 8, 32, 7)])
+def test_attention_one_key_group_grids(D, H, hq, q_len):
+    """Grids of more than one workgroup per CU (here 2 layers x 20 requests x
+    8 KV heads = 320) take the one-key-group kernel; small grids, as in most
+    tests here, take three key groups."""
+    rng = np.random.default_rng(D + q_len)
+    lens = [rng.integers(3, 40, size=int(rng.integers(1, 4))) for _ in range(20)]
+    w = context_workload(f"attn_kg1_{D}_{q_len}", 2, H, D, 16, 9, lens, q_len, n_req=20,
+                         seed=D + q_len)
+    dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu")
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, q_len, hq, layers, "cpu")
+
+
 def test_attention_query_positions_out_of_range_are_reported():
     # request 0 starts past max_position - q_len, request 1 before 0: both are
     # reported (bit 2) and produce 0; request 2 is unaffected
