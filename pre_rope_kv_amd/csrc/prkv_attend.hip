@@ -215,12 +215,13 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
         x[kb][2 * d + 1] = hi_bf16(w[d]);
       }
     }
-    // The lane's D/4 (cos, sin) entries, loaded unconditionally (the row
-    // index is clamped into the table) so all loads are in flight together;
-    // an out-of-range position rotates by the identity.
+    // The (cos, sin) entries of the lane's D/8 pairs (its D/4 dims), loaded
+    // unconditionally (the row index is clamped into the table) so all loads
+    // are in flight together; every index is < D/2, inside the position's
+    // row.  An out-of-range position rotates by the identity.
     const bool pos_ok = qpos >= 0 && qpos < p.max_position;
     const f32x4* rrow = p.rope + int64_t(pos_ok ? qpos : 0) * (D / 2);
-    constexpr int NCS = D / 4;
+    constexpr int NCS = D / 8;
     f32x4 cs[NCS];
 #pragma unroll
     for (int n = 0; n < NCS; ++n) {
