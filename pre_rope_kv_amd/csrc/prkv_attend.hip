@@ -202,8 +202,10 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   const int nb = min(p.bt_len[r], p.bt_stride);
 
   // 1. The lane's dims 32kb + 8a + e of its rotated query row, as hi + lo bf16.
-  bf16x8 qh[KB], ql[KB];
-  {
+  bf16x8 qh[KB] = {}, ql[KB] = {};
+  // With several key groups only group 0 loads and rotates the query rows;
+  // it hands them to the others through LDS (below).
+  if (KG == 1 || kg == 0) {
     float x[KB][8];
     const uint16_t* qr = p.q + ((int64_t(r) * p.q_len + qi) * p.num_q_heads + hq) * D;
 #pragma unroll
@@ -288,11 +290,32 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   // The table is staged in LDS when it fits (nb <= bt_stride <= kBtLds, the
   // dynamic LDS size); a longer one (contexts beyond kBtLds blocks) is read
   // from global memory, where the slots are computed kStages tiles ahead.
+  // group 0's rotated query rows for the other key groups, in the first
+  // ring (free until the first tile is issued, after two more barriers)
+  u32x4* q_share = reinterpret_cast<u32x4*>(&s_kv[0][0][0][0]);
+  if constexpr (KG > 1) {
+    if (kg == 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        q_share[(2 * kb) * kThreads + lt] = __builtin_bit_cast(u32x4, qh[kb]);
+        q_share[(2 * kb + 1) * kThreads + lt] = __builtin_bit_cast(u32x4, ql[kb]);
+      }
+    }
+  }
   if constexpr (BT_LDS) {
     if (int(threadIdx.x) < nb) s_bt[threadIdx.x] = bt_first;
     for (int i = threadIdx.x + NT; i < nb; i += NT) s_bt[i] = btr[i];
   }
   __syncthreads();
+  if constexpr (KG > 1) {
+    if (kg > 0) {
+#pragma unroll
+      for (int kb = 0; kb < KB; ++kb) {
+        qh[kb] = __builtin_bit_cast(bf16x8, q_share[(2 * kb) * kThreads + lt]);
+        ql[kb] = __builtin_bit_cast(bf16x8, q_share[(2 * kb + 1) * kThreads + lt]);
+      }
+    }
+  }
   // Slot of position pos < ctx, or -2 when its block is missing from the table.
   auto slot_of = [&](int pos) -> int {
     const int bi = p.bs_shift >= 0 ? pos >> p.bs_shift : pos / p.block_size;
