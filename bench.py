@@ -482,6 +482,66 @@ def k_sweep(args):
                       "sweep": rows}), flush=True)
 
 
+def single_user_step(args, torch, lib, w, dw, time_fn):
+    """One request's GPU part of the time to first token: retrieve_topk over
+    its store (ids written into the device batch), inject_topk_device, then
+    attend_paged for 16 query tokens (the context's last positions) x 4
+    query heads per KV head; the three calls back to back per step."""
+    import math
+
+    from pre_rope_kv_amd import prkv
+
+    spec = w.spec
+    # the prefix slots hold zeros (they are never injected), as in the
+    # attention figure of the main workload
+    with torch.cuda.stream(dw.stream):
+        dw.k_cache.zero_()
+        dw.v_cache.zero_()
+    torch.cuda.synchronize()
+    embs = [w.store_embeddings(si, "cuda") for si in range(spec.n_requests)]
+    emb = torch.cat(embs, 0).contiguous()
+    q_emb = w.query_embeddings("cuda", emb=embs)
+    ws_b = prkv.retrieve_workspace_bytes(spec.n_requests, spec.facts_per_store)
+    rws = torch.empty(ws_b, dtype=torch.uint8, device="cuda")
+    d_rs = torch.as_tensor(w.req_store(), device="cuda")
+    rargs = (emb.data_ptr(), spec.n_requests, spec.facts_per_store, spec.emb_dim,
+             q_emb.data_ptr(), d_rs.data_ptr(), spec.n_requests, spec.k, dw.d_ids.data_ptr(),
+             None, rws.data_ptr(), ws_b, dw.status.data_ptr(), dw.stream.cuda_stream)
+    q_len, hq, D, L = ATTN_Q_LEN, ATTN_GROUP * spec.num_kv_heads, spec.head_dim, spec.num_layers
+    ctxs = [int(w.prefix[r]) + sum(w.length_of(f) for f in ids)
+            for r, ids in enumerate(w.retrieved)]
+    g = torch.Generator(device="cuda")
+    g.manual_seed(13)
+    qt = torch.randn((spec.n_requests, q_len, hq, D), generator=g,
+                     device="cuda").to(torch.bfloat16).view(torch.int16)
+    q_start = torch.as_tensor([c - q_len for c in ctxs], dtype=torch.int32, device="cuda")
+    out = torch.empty((L, spec.n_requests, q_len, hq, D), dtype=torch.float32, device="cuda")
+    ab = prkv.attn_batch(spec.n_requests, q_len, hq, dw.d_bt.shape[1], qt, q_start, dw.d_bt,
+                         dw.d_bt_len, out)
+    kp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in dw.k_layers()])
+    vp = (ctypes.c_void_p * L)(*[t.data_ptr() for t in dw.v_layers()])
+    aargs = (dw.store.handle, ctypes.byref(ab), kp, vp, spec.block_size, w.num_blocks,
+             1.0 / math.sqrt(D), dw.status.data_ptr(), dw.stream.cuda_stream)
+    dargs = dw.inject_device_args()
+
+    def calls(*fa):
+        for f, a in fa:
+            rc = f(*a)
+            if rc != 0:
+                raise prkv.PrkvError(rc, f.__name__, lib.last_error_string().decode())
+        return 0
+
+    retrieve_ms = time_fn(lambda *a: calls((lib.retrieve_topk, rargs)), ())
+    attend_ms = time_fn(lambda *a: calls((lib.attend_paged, aargs)), ())
+    step_ms = time_fn(lambda *a: calls((lib.retrieve_topk, rargs),
+                                       (lib.inject_topk_device, dargs),
+                                       (lib.attend_paged, aargs)), ())
+    assert bool(torch.isfinite(out).all()), "attention produced non-finite values"
+    return {"what": "retrieve_topk + inject_topk_device + attend_paged (16 query tokens), "
+                    "back to back, one request",
+            "ms": step_ms, "retrieve_ms": retrieve_ms, "attend_ms": attend_ms}
+
+
 def other_workloads(args, torch, lib, names):
     """Device step and inject kernel alone on each of `names` (after the main
     workload's memory is released): tokens/s of the step, algorithmic GB/s of
@@ -531,6 +591,9 @@ def other_workloads(args, torch, lib, names):
             "traffic": read_profile_traffic(name) if profiled else None,
             "bytes_per_launch": alg,
         }
+        if spec.n_requests == 1 and spec.head_dim in (64, 128) and not args.no_retrieve \
+                and not args.no_attend:
+            rows[name]["serving_step"] = single_user_step(args, torch, lib, w, dw, time_fn)
         del dw, w, w0
         gc.collect()
         torch.cuda.synchronize()
