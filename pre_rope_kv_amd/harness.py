@@ -221,6 +221,16 @@ class DeviceWorkload:
         # advanced indices around a slice: the result is [n][L][H][D]
         return cache[:, slots // bs, :, slots % bs].permute(1, 0, 2, 3)
 
+    def slot_rows_layer(self, cache, layer, slots):
+        """Rows of the given slots (device int64 tensor) in one layer: a
+        device tensor [n][H][D] whatever the cache layout."""
+        c = cache[layer]
+        if not self.hnd:
+            sp = self.w.spec
+            return c.view(-1, sp.num_kv_heads, sp.head_dim)[slots]
+        bs = self.w.spec.block_size
+        return c[slots // bs, :, slots % bs]   # [block][H][bs][D] -> [n][H][D]
+
     def set_slot_row(self, cache, layer, slot, value):
         """Write one slot's [H][D] row of one layer."""
         bs = self.w.spec.block_size

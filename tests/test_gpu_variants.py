@@ -66,17 +66,20 @@ def test_variant_llama8b_k50_hnd():
     run_full(variant_workload("llama3_8b_k50", "hnd"), path="device")
 
 
-def test_variant_batch64_full_size_sampled():
-    _full_size("llama3_8b_batch64_k50", 256, seed=5, path="device", **VARIANTS["all_three"])
+@pytest.mark.timeout(900)
+def test_variant_batch64_full_size():
+    _full_size("llama3_8b_batch64_k50", paths=("device",), **VARIANTS["all_three"])
 
 
-def test_variant_batch64_full_size_sampled_hnd():
-    _full_size("llama3_8b_batch64_k50", 256, seed=6, path="device", **VARIANTS["hnd"])
+@pytest.mark.timeout(900)
+def test_variant_batch64_full_size_hnd():
+    _full_size("llama3_8b_batch64_k50", paths=("device",), **VARIANTS["hnd"])
 
 
-def test_variant_llama70b_full_size_sampled_hnd():
+@pytest.mark.timeout(900)
+def test_variant_llama70b_full_size_hnd():
     # block size 32, fact starts that straddle blocks
-    _full_size("llama3_70b_batch16_k50", 128, seed=7, path="device", **VARIANTS["hnd"])
+    _full_size("llama3_70b_batch16_k50", paths=("device",), **VARIANTS["hnd"])
 
 
 HND_EDGE = ["prefix0_len1", "len256_straddle_bs32", "dup_fact_in_request", "h1_d64", "h1_d16",
