@@ -296,6 +296,29 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
                        void* d_workspace, size_t workspace_bytes, int32_t* d_status,
                        void* stream);
 
+/* inject_topk_device without a caller workspace, for callers that cannot
+ * allocate device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  Same arguments, kernels, results and
+ * d_status bits as inject_topk_device; the workspace is instead a static
+ * array of PRKV_NOALLOC_SCRATCH_BYTES in this library's device code, one per
+ * GPU, held until the process ends.  The call allocates nothing (no
+ * hipMalloc, no host-side allocation on success).  Limits: the batch bounds
+ * must fit the array, i.e. inject_device_workspace_bytes(batch->max_facts,
+ * batch->max_tokens) <= PRKV_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. 4,096 facts
+ * and 1,300,000 tokens), else PRKV_ERR_BUFFER_TOO_SMALL with nothing
+ * enqueued.  Every call on one GPU shares that GPU's array and leaves the
+ * last call's mapping in it; nothing in it needs to start at zero.  Calls
+ * that overlap on one GPU (several streams, several threads or processes'
+ * streams at once) race on the array: serialize them, or use
+ * inject_topk_device with separate workspaces.  The first call on a device
+ * looks up the array's device address (hipGetSymbolAddress) with that
+ * device current. */
+#define PRKV_NOALLOC_SCRATCH_BYTES (16u << 20)
+int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
+                               const prkv_device_batch* batch, void* const* k_cache_layers,
+                               void* const* v_cache_layers, int32_t block_size,
+                               int64_t num_blocks, int32_t* d_status, void* stream);
+
 /* Exact top-k retrieval by inner product, the step before injection.
  * Source: InferScale review, "Referee Report" Summary (facts retrieved at
  * serving time through a GPU index, then resolved to their KV) and Figure 2

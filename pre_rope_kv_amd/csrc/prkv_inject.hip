@@ -63,10 +63,17 @@
 #include <algorithm>
 #include <atomic>
 #include <cstdint>
+#include <mutex>
 #include <vector>
 
 #include "prkv_device_common.h"
 #include "prkv_internal.h"
+
+// Workspace of inject_topk_device_noalloc, for callers that cannot allocate
+// device memory: one array per GPU, held until the process ends.  Host code
+// never passes this name to a kernel (on the host it is only a stand-in); it
+// uses the device address hipGetSymbolAddress returns (scratch_address).
+static __device__ __align__(256) unsigned char scratch[PRKV_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 using namespace prkv_dev;
@@ -1008,12 +1015,17 @@ int inject_device_workspace_bytes(int32_t max_facts_batch, int64_t max_tokens, s
   return PRKV_OK;
 }
 
-int inject_topk_device(const prkv_store* st, const void* d_fact_table,
+}  // extern "C"
+
+namespace {
+
+// inject_topk_device's work on a given workspace (the caller's, or the
+// library's scratch array for inject_topk_device_noalloc).
+int inject_device_impl(const prkv_store* st, const void* d_fact_table,
                        const prkv_device_batch* batch, void* const* k_cache_layers,
                        void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
                        void* d_workspace, size_t workspace_bytes, int32_t* d_status,
                        void* stream) {
-  prkv::clear_error();
   if (int rc = check_cache_args(st, block_size, num_blocks, k_cache_layers, v_cache_layers))
     return rc;
   if (!batch) return prkv::fail(PRKV_ERR_INVALID_ARG, "batch is NULL");
@@ -1087,6 +1099,68 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
   return launch_inject(st, b.max_tokens, db.n_tokens_out, db.src_row, db.pos, db.slot,
                        k_cache_layers, v_cache_layers, block_size, num_blocks, d_status, s,
                        nullptr, expect);
+}
+
+// Device address of this library's scratch array on the current device,
+// looked up once per device (each GPU holds its own copy of the array at its
+// own address; the array's name in host code is only a host-side stand-in).
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+int scratch_address(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  if (dev < 0 || dev >= kMaxDevices)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "device %d beyond the %d the library tracks", dev,
+                      kMaxDevices);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
+      return prkv::fail(PRKV_ERR_HIP, "scratch array has no 256-byte aligned device address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return PRKV_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int inject_topk_device(const prkv_store* st, const void* d_fact_table,
+                       const prkv_device_batch* batch, void* const* k_cache_layers,
+                       void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
+                       void* d_workspace, size_t workspace_bytes, int32_t* d_status,
+                       void* stream) {
+  prkv::clear_error();
+  return inject_device_impl(st, d_fact_table, batch, k_cache_layers, v_cache_layers, block_size,
+                            num_blocks, d_workspace, workspace_bytes, d_status, stream);
+}
+
+int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
+                               const prkv_device_batch* batch, void* const* k_cache_layers,
+                               void* const* v_cache_layers, int32_t block_size,
+                               int64_t num_blocks, int32_t* d_status, void* stream) {
+  prkv::clear_error();
+  if (!batch) return prkv::fail(PRKV_ERR_INVALID_ARG, "batch is NULL");
+  if (batch->max_facts < 0 || batch->max_tokens < 0 || batch->max_tokens > INT32_MAX)
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "negative or oversized batch bounds");
+  const size_t need = Workspace(batch->max_facts, batch->max_tokens).total;
+  if (need > size_t(PRKV_NOALLOC_SCRATCH_BYTES))
+    return prkv::fail(PRKV_ERR_BUFFER_TOO_SMALL,
+                      "batch bounds (max_facts %d, max_tokens %lld) need %zu workspace bytes; "
+                      "the library's scratch holds %zu",
+                      batch->max_facts, (long long)batch->max_tokens, need,
+                      size_t(PRKV_NOALLOC_SCRATCH_BYTES));
+  void* ws = nullptr;
+  if (int rc = scratch_address(&ws)) return rc;
+  return inject_device_impl(st, d_fact_table, batch, k_cache_layers, v_cache_layers, block_size,
+                            num_blocks, ws, size_t(PRKV_NOALLOC_SCRATCH_BYTES), d_status, stream);
 }
 
 }  // extern "C"

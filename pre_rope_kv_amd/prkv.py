@@ -29,7 +29,11 @@ CODES = {v: k for k, v in ERRORS.items()}
 EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
            "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
            "last_error_string", "store_upload_fact_table", "inject_device_workspace_bytes",
-           "inject_topk_device", "retrieve_workspace_bytes", "retrieve_topk", "attend_paged"]
+           "inject_topk_device", "inject_topk_device_noalloc", "retrieve_workspace_bytes",
+           "retrieve_topk", "attend_paged"]
+
+# Size of the library's own workspace for inject_topk_device_noalloc.
+NOALLOC_SCRATCH_BYTES = 16 << 20
 
 
 class PrkvError(RuntimeError):
@@ -131,6 +135,9 @@ def lib():
                                               ctypes.POINTER(_vp), ctypes.POINTER(_vp),
                                               ctypes.c_int32, ctypes.c_int64, _vp,
                                               ctypes.c_size_t, _vp, _vp]),
+        "inject_topk_device_noalloc": (ctypes.c_int, [_vp, _vp, ctypes.POINTER(DeviceBatch),
+                                                      ctypes.POINTER(_vp), ctypes.POINTER(_vp),
+                                                      ctypes.c_int32, ctypes.c_int64, _vp, _vp]),
         "retrieve_workspace_bytes": (ctypes.c_int, [ctypes.c_int32, ctypes.c_int32,
                                                     ctypes.POINTER(ctypes.c_size_t)]),
         "retrieve_topk": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32,
@@ -356,6 +363,20 @@ def inject_topk_device(st, d_fact_table, batch, k_cache_layers, v_cache_layers, 
                                     int(block_size), int(num_blocks), _ptr(d_workspace),
                                     int(workspace_bytes), _ptr(d_status), _stream(stream)),
            "inject_topk_device")
+
+
+def inject_topk_device_noalloc(st, d_fact_table, batch, k_cache_layers, v_cache_layers,
+                               block_size, num_blocks, d_status=None, stream=None):
+    """inject_topk_device on the library's own per-GPU workspace (no allocation)."""
+    L = len(k_cache_layers)
+    if len(v_cache_layers) != L or L != st.desc.num_layers:
+        raise ValueError("need one K and one V cache pointer per layer")
+    kp = (_vp * L)(*[_ptr(t) for t in k_cache_layers])
+    vp = (_vp * L)(*[_ptr(t) for t in v_cache_layers])
+    _check(lib().inject_topk_device_noalloc(st.handle, _ptr(d_fact_table), ctypes.byref(batch),
+                                            kp, vp, int(block_size), int(num_blocks),
+                                            _ptr(d_status), _stream(stream)),
+           "inject_topk_device_noalloc")
 
 
 def retrieve_workspace_bytes(n_req, facts_per_store):
