@@ -68,6 +68,13 @@ def parse():
     ap.add_argument("--flush", action="store_true",
                     help="evict the 256 MB Infinity Cache with a 1 GiB fill before every timed "
                          "launch and time launches one by one (for workloads far below 1 GiB)")
+    ap.add_argument("--no-ceiling", action="store_true",
+                    help="skip the hand-written streaming-copy reference of the same bytes")
+    ap.add_argument("--no-slot-check", action="store_true",
+                    help="skip timing the step with the device duplicate-slot check on")
+    ap.add_argument("--cpu-worker", action="store_true",
+                    help="(used by the bench itself) one worker of the multi-core CPU-oracle "
+                         "baseline: read a task as JSON on stdin, print the result")
     ap.add_argument("--summarize-profile", nargs=3, metavar=("TRACE_DIR", "FETCH_DIR", "WRITE_DIR"),
                     help="turn rocprofv3 output of this script into profiles/<kernel>_<workload>.md")
     return ap.parse_args()
@@ -232,7 +239,7 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, commands):
 
 
 def copy_ceiling_gbps(torch, nbytes=4 << 30, reps=10):
-    """Read + write bytes / time of two plain copies of `nbytes`, for context:
+    """Read + write bytes / time of two library copies of `nbytes`, for context:
     a device-to-device memcpy, and an elementwise int16 negate kernel (whose
     FETCH_SIZE / WRITE_SIZE counters calibrate the HBM-traffic counters)."""
     src = torch.empty(nbytes // 2, dtype=torch.int16, device="cuda")
@@ -253,6 +260,140 @@ def copy_ceiling_gbps(torch, nbytes=4 << 30, reps=10):
         out[name] = 2 * nbytes / (s.elapsed_time(e) / reps * 1e-3) / 1e9
     del src, dst
     torch.cuda.empty_cache()
+    return out
+
+
+_CEILING = None
+
+
+def ceiling_lib():
+    """libprkv_ceiling.so (built by pre_rope_kv_amd.build): the plain copy the
+    inject kernel is measured against."""
+    global _CEILING
+    if _CEILING is None:
+        path = os.path.join(ROOT, "pre_rope_kv_amd", "libprkv_ceiling.so")
+        if not os.path.exists(path):
+            raise ImportError(f"{path} is missing: build with `python -m pre_rope_kv_amd.build`")
+        lib = ctypes.CDLL(path)
+        vp = ctypes.c_void_p
+        i32, i64 = ctypes.c_int32, ctypes.c_int64
+        lib.ceiling_gather_scatter.argtypes = [vp, vp, i64, vp, vp, i64, vp, vp, i64, i32, i32,
+                                               i32, i32, vp]
+        lib.ceiling_gather_scatter.restype = ctypes.c_int
+        lib.ceiling_empty.argtypes = [ctypes.c_int32, vp]
+        lib.ceiling_empty.restype = ctypes.c_int
+        _CEILING = lib
+    return _CEILING
+
+
+class Flusher:
+    """Evicts the 256 MB Infinity Cache (MALL) with a 1 GiB fill on a stream,
+    so that the next launch finds none of its data cached."""
+
+    def __init__(self, torch):
+        self.buf = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
+        self.i = 0
+
+    def __call__(self, torch, stream):
+        self.i += 1
+        with torch.cuda.stream(stream):
+            self.buf.fill_(self.i)
+
+
+def time_launches(torch, fn, stream, steps, warmup, flusher=None):
+    """Mean and median ms per launch of fn() on `stream`: back to back (warm),
+    or, with a flusher, one at a time each after a MALL-evicting fill (cold)."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    if flusher is None:
+        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        evs[0].record(stream)
+        for i in range(steps):
+            fn()
+            evs[i + 1].record(stream)
+        torch.cuda.synchronize()
+        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+        return evs[0].elapsed_time(evs[steps]) / steps, per[len(per) // 2]
+    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+             for _ in range(steps)]
+    for a, b in pairs:
+        flusher(torch, stream)
+        a.record(stream)
+        fn()
+        b.record(stream)
+    torch.cuda.synchronize()
+    per = sorted(a.elapsed_time(b) for a, b in pairs)
+    return sum(per) / len(per), per[len(per) // 2]
+
+
+def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
+    """Read + write GB/s of a plain copy that moves exactly the bytes of the
+    workload's inject launch (libprkv_ceiling.so): every token's K and V row
+    of every layer from its arena row to a cache row, with no rotation.
+    "mapped": the batch's own arena rows and cache slots (the inject launch's
+    addresses); "contiguous": rows t -> t of the same arena and cache.  Each
+    is the best of token- and layer-major wave orders x 64 / 256 / 1024-lane
+    workgroups; with a flusher the best shape is also timed cold.  It
+    overwrites cache rows, so the cache is reset and the batch re-injected
+    afterwards.  None when the layout has no such copy (HND cache, host
+    store, rows other than 1, 2 or 4 KiB)."""
+    sp, w = dw.w.spec, dw.w
+    if dw.hnd or dw.store_location != "device" or sp.row_bytes not in (1024, 2048, 4096):
+        return None
+    lib = ceiling_lib()
+    stream = dw.stream
+    n, L = dw.n_tokens, sp.num_layers
+    num_slots = w.num_blocks * sp.block_size
+    src, _, slot = dw.d_map
+    # every row index inside its buffer (the copy trusts them)
+    assert 0 <= int(src[:n].min()) and int(src[:n].max()) < w.capacity_rows
+    assert 0 <= int(slot[:n].min()) and int(slot[:n].max()) < num_slots
+    assert n <= w.capacity_rows and n <= num_slots
+    nbytes = n * sp.bytes_per_token
+    out = {"bytes_per_launch": nbytes}
+    for name, rows in (("mapped", (src.data_ptr(), slot.data_ptr())), ("contiguous", (None, None))):
+        best = None
+        for order in (0, 1):
+            for threads in (64, 256, 1024):
+                args = (dw.k_arena.data_ptr(), dw.v_arena.data_ptr(), w.capacity_rows * sp.row_bytes,
+                        dw.k_cache.data_ptr(), dw.v_cache.data_ptr(), num_slots * sp.row_bytes,
+                        rows[0], rows[1], n, L, sp.row_bytes, order, threads, stream.cuda_stream)
+
+                def fn(a=args):
+                    rc = lib.ceiling_gather_scatter(*a)
+                    if rc != 0:
+                        raise RuntimeError(f"ceiling_gather_scatter failed ({rc})")
+
+                ms, _ = time_launches(torch, fn, stream, steps, warmup)
+                if best is None or ms < best[0]:
+                    best = (ms, order, threads, fn)
+        ms, order, threads, fn = best
+        row = {"gbps": nbytes / (ms * 1e-3) / 1e9, "ms": ms,
+               "order": "token-major" if order == 0 else "layer-major", "threads": threads}
+        if flusher is not None:
+            c_ms, c_med = time_launches(torch, fn, stream, steps, 2, flusher)
+            row.update({"cold_ms": c_ms, "cold_median_ms": c_med,
+                        "cold_gbps": nbytes / (c_ms * 1e-3) / 1e9})
+        out[name] = row
+    out["gbps"] = max(out["mapped"]["gbps"], out["contiguous"]["gbps"])
+    if flusher is not None:
+        out["cold_gbps"] = max(out["mapped"]["cold_gbps"], out["contiguous"]["cold_gbps"])
+    dw.reset_cache()
+    dw.inject()
+    torch.cuda.synchronize()
+    return out
+
+
+def launch_floor(torch, stream, steps=200):
+    """ms per launch of an empty kernel, back to back: one workgroup, and one
+    of 2,048 workgroups (the shortest time any launch can take here)."""
+    lib = ceiling_lib()
+    out = {}
+    for grid in (1, 2048):
+        ms, med = time_launches(torch, lambda g=grid: lib.ceiling_empty(g, stream.cuda_stream),
+                                stream, steps, 10)
+        out[f"grid_{grid}_ms"] = ms
     return out
 
 
@@ -338,6 +479,7 @@ def _pool_worker(task):
     block_size, num_kv_heads, head_dim, theta = spec_vals
     done, spent = 0, 0.0
     for r, (ids, prefix, bt, rows) in enumerate(reqs):
+        rows = {int(f): tuple(v) for f, v in rows.items()}
         k_ar = np.load(os.path.join(folder, f"k{r}.npy"), mmap_mode="r")[layers[0]:layers[1]]
         v_ar = np.load(os.path.join(folder, f"v{r}.npy"), mmap_mode="r")[layers[0]:layers[1]]
         k_ar, v_ar = np.ascontiguousarray(k_ar), np.ascontiguousarray(v_ar)
@@ -351,18 +493,67 @@ def _pool_worker(task):
     return done, spent
 
 
-def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
-    """The same oracle spread over the host's cores (a process pool, split by
-    layer, as the work is independent per layer) on the first n_requests
-    requests: tokens/s = sampled tokens / the slowest worker's compute time."""
-    import multiprocessing
+def cpu_worker_main():
+    """--cpu-worker: wait for one task (JSON on stdin), run it, print the result."""
+    os.environ.setdefault("OMP_NUM_THREADS", "1")
+    line = sys.stdin.readline()
+    if not line.strip():
+        return            # the bench ended without using this worker
+    done, spent = _pool_worker(json.loads(line))
+    print(json.dumps({"done": done, "spent": spent}), flush=True)
+
+
+# the host CPU share that comes with one GPU here; more workers than that
+# would compete with each other, not add cores
+CPU_WORKER_CAP = 16
+
+
+def start_cpu_workers():
+    """Start the multi-core baseline's worker processes, idle until fed.  Called
+    before this process makes any GPU call, so no child is ever started by a
+    process that has initialised the GPU."""
+    import subprocess
+    visible = len(os.sched_getaffinity(0))
+    n = min(visible, CPU_WORKER_CAP)
+    env = dict(os.environ, OMP_NUM_THREADS="1", OPENBLAS_NUM_THREADS="1", MKL_NUM_THREADS="1")
+    procs = [subprocess.Popen([sys.executable, "-u", os.path.abspath(__file__), "--cpu-worker"],
+                              stdin=subprocess.PIPE, stdout=subprocess.PIPE, text=True, env=env)
+             for _ in range(n)]
+    return {"procs": procs, "visible_cores": visible}
+
+
+def stop_cpu_workers(workers):
+    """End every worker: close its input (an idle worker then exits) and wait;
+    kill the exact PID only if it does not exit."""
+    if not workers:
+        return
+    for p in workers["procs"]:
+        try:
+            if p.stdin and not p.stdin.closed:
+                p.stdin.close()
+        except OSError:
+            pass
+    for p in workers["procs"]:
+        try:
+            p.wait(timeout=60)
+        except Exception:
+            p.kill()
+            p.wait()
+
+
+def cpu_baseline_pool(w, n_requests, workers, gen_device="cuda"):
+    """The same oracle spread over the host's cores (the started worker
+    processes, split by layer, as the work is independent per layer) on the
+    first n_requests requests: tokens/s = sampled tokens / the slowest
+    worker's compute time."""
     import shutil
     import tempfile
 
     import numpy as np
 
     sp = w.spec
-    cores = min(len(os.sched_getaffinity(0)), max_workers, sp.num_layers)
+    procs = workers["procs"]
+    cores = min(len(procs), sp.num_layers)
     folder = tempfile.mkdtemp(prefix="prkv_pool_")
     try:
         reqs = []
@@ -373,7 +564,7 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
                 k, v = w.fact_kv(f, device=gen_device)
                 ks.append(k.cpu().numpy().view(np.uint16))
                 vs.append(v.cpu().numpy().view(np.uint16))
-                rows[f] = (row, w.length_of(f))
+                rows[int(f)] = (row, w.length_of(f))
                 row += w.length_of(f)
             np.save(os.path.join(folder, f"k{r}.npy"), np.concatenate(ks, 1))
             np.save(os.path.join(folder, f"v{r}.npy"), np.concatenate(vs, 1))
@@ -381,11 +572,17 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
             n_tok += sum(w.length_of(f) for f in ids)
         edges = np.linspace(0, sp.num_layers, cores + 1).round().astype(int)
         vals = (sp.block_size, sp.num_kv_heads, sp.head_dim, sp.rope_theta)
-        tasks = [(folder, (int(edges[i]), int(edges[i + 1])), reqs, vals) for i in range(cores)]
-        # fresh interpreters (spawn): the workers never touch the GPU
-        with multiprocessing.get_context("spawn").Pool(cores) as pool:
-            res = pool.map(_pool_worker, tasks)
+        for i, p in enumerate(procs[:cores]):
+            task = (folder, (int(edges[i]), int(edges[i + 1])), reqs, vals)
+            p.stdin.write(json.dumps(task) + "\n")
+            p.stdin.flush()
+            p.stdin.close()
+        res = []
+        for p in procs[:cores]:
+            out = json.loads(p.stdout.readline())
+            res.append((out["done"], out["spent"]))
     finally:
+        stop_cpu_workers(workers)
         shutil.rmtree(folder, ignore_errors=True)
     token_layers = sum(d for d, _ in res)
     assert token_layers == n_tok * sp.num_layers
@@ -394,21 +591,69 @@ def cpu_baseline_pool(w, n_requests, max_workers=16, gen_device="cuda"):
         "value": n_tok / slowest,
         "unit": "injected KV tokens/s",
         "cores": cores,
+        "cores_visible": workers["visible_cores"],
+        "cores_cap": CPU_WORKER_CAP,
         "cpu_model": cpu_model(),
         "kind": "oracle",
         "sample": (f"{n_tok} tokens of the first {len(reqs)} request(s), all {sp.num_layers} "
-                   f"layers split over {cores} worker processes; rotate + scatter only; "
+                   f"layers split over {cores} worker processes (one per core, "
+                   f"{workers['visible_cores']} cores visible, at most {CPU_WORKER_CAP} used: "
+                   f"the host share of one GPU); rotate + scatter only; "
                    f"slowest worker {slowest:.1f} s, {sum(t for _, t in res):.1f} core-s in all"),
     }
 
 
+def k_sweep_rows(args, torch, lib, w, dw, flusher):
+    """The pages' retrieval-budget sweep (k = 5, 10, 20, 50) on one request:
+    the device step (mapping + inject) for the first k facts of the drawn
+    request of the 2,000-fact store, with the fused mapping (one launch) and
+    with the separate plan and mapping kernels (forced by a max_facts bound
+    above the fused limit), back to back (warm) and one launch at a time after
+    a 1 GiB fill that evicts the MALL (cold)."""
+    from pre_rope_kv_amd import prkv
+
+    stream = dw.stream
+    rows = []
+    ptr_cap = 257        # a max_facts bound above the fused mapping's limit (256)
+    big_ws = torch.zeros(prkv.inject_device_workspace_bytes(ptr_cap, dw.max_tokens),
+                         dtype=torch.uint8, device=dw.device)
+
+    def step_fn(k, max_facts, workspace):
+        ptr = torch.tensor([0, k], dtype=torch.int32, device=dw.device)
+        batch = prkv.device_batch(1, dw.d_bt.shape[1], max_facts, dw.max_tokens, ptr, dw.d_ids,
+                                  dw.d_start, dw.d_bt, dw.d_bt_len)
+        a = list(dw.inject_device_args())
+        a[2] = ctypes.byref(batch)
+        a[7], a[8] = workspace.data_ptr(), workspace.numel()
+
+        def step(keep=(ptr, batch)):
+            rc = lib.inject_topk_device(*a)
+            if rc != 0:
+                raise prkv.PrkvError(rc, "inject_topk_device", lib.last_error_string().decode())
+        return step
+
+    for k in (5, 10, 20, 50):
+        fused = step_fn(k, k, dw.workspace)
+        three = step_fn(k, ptr_cap, big_ws)
+        ms, _ = time_launches(torch, fused, stream, args.steps, args.warmup)
+        ms3, _ = time_launches(torch, three, stream, args.steps, args.warmup)
+        ms_cold, med_cold = time_launches(torch, fused, stream, args.steps, args.warmup, flusher)
+        assert int(dw.status.item()) == 0
+        n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
+        nb = n_tok * w.spec.bytes_per_token
+        rows.append({"k": k, "tokens": n_tok, "bytes_per_launch": nb,
+                     "step_ms": ms, "tokens_per_s": n_tok / (ms * 1e-3),
+                     "hbm_gbps": nb / (ms * 1e-3) / 1e9,
+                     "step_ms_three_kernels": ms3,
+                     "step_ms_cold": ms_cold, "step_median_ms_cold": med_cold,
+                     "tokens_per_s_cold": n_tok / (ms_cold * 1e-3),
+                     "hbm_gbps_cold": nb / (ms_cold * 1e-3) / 1e9})
+    del big_ws
+    return rows
+
+
 def k_sweep(args):
-    """The retrieval-budget sweep of the pages (k = 5 .. 50) on one request:
-    the device step (mapping + inject) for the first k facts of one drawn
-    request of the 2,000-fact store, each k timed over args.steps launches,
-    with the fused mapping (one launch) and with the separate plan and mapping
-    kernels (forced by a max_facts bound above the fused limit), back to back
-    and cold (each launch after a 1 GiB fill that evicts the MALL)."""
+    """--k-sweep: only the retrieval-budget sweep, as one JSON line."""
     import torch
 
     from pre_rope_kv_amd import harness, prkv, workloads
@@ -418,63 +663,7 @@ def k_sweep(args):
     w = workloads.make("llama3_8b_k50")
     dw = harness.DeviceWorkload(w)
     dw.setup_device_batch()
-    stream = dw.stream
-    rows = []
-    ptr_cap = 257        # a max_facts bound above the fused mapping's limit (256)
-    big_ws = torch.zeros(prkv.inject_device_workspace_bytes(ptr_cap, dw.max_tokens),
-                         dtype=torch.uint8, device=dw.device)
-
-    scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda")
-
-    def time_step(k, max_facts, workspace, cold=False):
-        ptr = torch.tensor([0, k], dtype=torch.int32, device=dw.device)
-        batch = prkv.device_batch(1, dw.d_bt.shape[1], max_facts, dw.max_tokens, ptr, dw.d_ids,
-                                  dw.d_start, dw.d_bt, dw.d_bt_len)
-        a = list(dw.inject_device_args())
-        a[2] = ctypes.byref(batch)
-        a[7], a[8] = workspace.data_ptr(), workspace.numel()
-
-        def step():
-            rc = lib.inject_topk_device(*a)
-            if rc != 0:
-                raise prkv.PrkvError(rc, "inject_topk_device", lib.last_error_string().decode())
-
-        for _ in range(args.warmup):
-            step()
-        torch.cuda.synchronize()
-        if cold:
-            # one launch at a time, each after a 1 GiB fill that evicts the 256 MB MALL
-            n = min(args.steps, 50)
-            ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-                  for _ in range(n)]
-            for i in range(n):
-                with torch.cuda.stream(stream):
-                    scratch.fill_(i)
-                ev[i][0].record(stream)
-                step()
-                ev[i][1].record(stream)
-            torch.cuda.synchronize()
-            assert int(dw.status.item()) == 0
-            return sum(a.elapsed_time(b) for a, b in ev) / n
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record(stream)
-        for _ in range(args.steps):
-            step()
-        e1.record(stream)
-        torch.cuda.synchronize()
-        assert int(dw.status.item()) == 0
-        return e0.elapsed_time(e1) / args.steps
-
-    for k in (5, 10, 20, 50):
-        ms = time_step(k, k, dw.workspace)              # fused mapping: one launch
-        ms3 = time_step(k, ptr_cap, big_ws)             # plan + mapping + inject kernels
-        ms_cold = time_step(k, k, dw.workspace, cold=True)
-        n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
-        rows.append({"k": k, "tokens": n_tok, "step_ms": ms,
-                     "tokens_per_s": n_tok / (ms * 1e-3),
-                     "hbm_gbps": n_tok * w.spec.bytes_per_token / (ms * 1e-3) / 1e9,
-                     "step_ms_three_kernels": ms3,
-                     "step_ms_cold": ms_cold})
+    rows = k_sweep_rows(args, torch, lib, w, dw, Flusher(torch))
     print(json.dumps({"metric": "device step time vs retrieval budget k, 1 request, 1 MI355X",
                       "unit": "ms", "higher_is_better": False, "n_gpus": 1,
                       "steps": args.steps, "warmup": args.warmup, "dtype": "f32",
@@ -542,15 +731,24 @@ def single_user_step(args, torch, lib, w, dw, time_fn):
             "ms": step_ms, "retrieve_ms": retrieve_ms, "attend_ms": attend_ms}
 
 
+# workloads far below the 256 MB MALL's reach are also timed cold
+COLD_BELOW_BYTES = 1 << 30
+
+
 def other_workloads(args, torch, lib, names):
-    """Device step and inject kernel alone on each of `names` (after the main
-    workload's memory is released): tokens/s of the step, algorithmic GB/s of
-    the kernel.  Back-to-back launches, events around args.steps of each."""
+    """Device step and inject kernel alone on each of `names`, each workload
+    set up and released in turn: tokens/s of the step, algorithmic GB/s of
+    the kernel, warm (back-to-back launches, events around args.steps of
+    them) and, for workloads below 1 GiB per launch, cold (each launch after a
+    1 GiB fill that evicts the MALL, so none of its data is cached); next to
+    them the hand-written streaming copy of the same bytes, the step with the
+    duplicate-slot check, and on the 2,000-fact store the k sweep."""
     import gc
 
     from pre_rope_kv_amd import harness, prkv, workloads
 
-    rows = {}
+    flusher = Flusher(torch)
+    rows = {"launch_floor": launch_floor(torch, torch.cuda.current_stream())}
     for name in names:
         spec = workloads.SPECS[name]
         if args.cache_layout == "hnd":
@@ -563,37 +761,68 @@ def other_workloads(args, torch, lib, names):
         dw.setup_device_batch()
         stream = dw.stream
 
-        def time_fn(fn, a):
-            for _ in range(args.warmup):
+        def caller(fn, a):
+            def call():
                 rc = fn(*a)
                 if rc != 0:
                     raise prkv.PrkvError(rc, fn.__name__, lib.last_error_string().decode())
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            torch.cuda.synchronize()
-            e0.record(stream)
-            for _ in range(args.steps):
-                fn(*a)
-            e1.record(stream)
-            torch.cuda.synchronize()
-            assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
-            return e0.elapsed_time(e1) / args.steps
+            return call
 
-        step_ms = time_fn(lib.inject_topk_device, dw.inject_device_args())
-        kernel_ms = time_fn(lib.inject_topk, dw.inject_args())
+        def time_fn(fn, a):       # the single-user step's signature
+            ms, _ = time_launches(torch, caller(fn, a), stream, args.steps, args.warmup)
+            assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
+            return ms
+
+        step = caller(lib.inject_topk_device, dw.inject_device_args())
+        kernel = caller(lib.inject_topk, dw.inject_args())
+        step_ms, step_med = time_launches(torch, step, stream, args.steps, args.warmup)
+        kernel_ms, kernel_med = time_launches(torch, kernel, stream, args.steps, args.warmup)
+        assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
         alg = dw.n_tokens * spec.bytes_per_token
         profiled = w is w0 and args.cache_layout == "nhd"
-        rows[name] = {
-            "tokens": dw.n_tokens, "layers": spec.num_layers, "requests": spec.n_requests,
-            "k": spec.k, "block_size": spec.block_size, "num_blocks": w.num_blocks,
-            "step_ms": step_ms, "tokens_per_s": dw.n_tokens / (step_ms * 1e-3),
-            "kernel_ms": kernel_ms, "hbm_gbps": alg / (kernel_ms * 1e-3) / 1e9,
-            "frac_of_peak": alg / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS,
+        row = {
+            "tokens": dw.n_tokens, "layers": spec.num_layers, "kv_heads": spec.num_kv_heads,
+            "requests": spec.n_requests, "k": spec.k, "block_size": spec.block_size,
+            "num_blocks": w.num_blocks, "bytes_per_launch": alg,
+            "warm": {"step_ms": step_ms, "step_median_ms": step_med,
+                     "tokens_per_s": dw.n_tokens / (step_ms * 1e-3),
+                     "kernel_ms": kernel_ms, "kernel_median_ms": kernel_med,
+                     "hbm_gbps": alg / (kernel_ms * 1e-3) / 1e9,
+                     "frac_of_peak": alg / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
             "traffic": read_profile_traffic(name) if profiled else None,
-            "bytes_per_launch": alg,
         }
+        cold = alg < COLD_BELOW_BYTES
+        if cold:
+            c_step, c_step_med = time_launches(torch, step, stream, args.steps, args.warmup,
+                                               flusher)
+            c_kern, c_kern_med = time_launches(torch, kernel, stream, args.steps, args.warmup,
+                                               flusher)
+            assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
+            row["cold"] = {"step_ms": c_step, "step_median_ms": c_step_med,
+                           "tokens_per_s": dw.n_tokens / (c_step * 1e-3),
+                           "kernel_ms": c_kern, "kernel_median_ms": c_kern_med,
+                           "hbm_gbps": alg / (c_kern * 1e-3) / 1e9,
+                           "frac_of_peak": alg / (c_kern * 1e-3) / 1e9 / PEAK_HBM_GBPS}
+        ceil = None if args.no_ceiling else \
+            gather_scatter_ceiling(torch, dw, args.steps, args.warmup, flusher if cold else None)
+        if ceil is not None:
+            row["ceiling_copy"] = ceil
+            row["warm"]["frac_of_ceiling"] = row["warm"]["hbm_gbps"] / ceil["gbps"]
+            if cold:
+                row["cold"]["frac_of_ceiling"] = row["cold"]["hbm_gbps"] / ceil["cold_gbps"]
+        if not args.no_slot_check:
+            dw.setup_device_batch(flags=prkv.BATCH_CHECK_SLOTS)
+            chk = caller(lib.inject_topk_device, dw.inject_device_args())
+            chk_ms, _ = time_launches(torch, chk, stream, args.steps, args.warmup)
+            assert int(dw.status.item()) == 0, f"{name}: slot check flagged a valid batch"
+            row["slot_check"] = {"step_ms": chk_ms, "added_ms": chk_ms - step_ms}
+            dw.setup_device_batch()
+        if name == "llama3_8b_k50":
+            row["k_sweep"] = k_sweep_rows(args, torch, lib, w, dw, flusher)
         if spec.n_requests == 1 and spec.head_dim in (64, 128) and not args.no_retrieve \
                 and not args.no_attend:
-            rows[name]["serving_step"] = single_user_step(args, torch, lib, w, dw, time_fn)
+            row["serving_step"] = single_user_step(args, torch, lib, w, dw, time_fn)
+        rows[name] = row
         del dw, w, w0
         gc.collect()
         torch.cuda.synchronize()
@@ -617,6 +846,9 @@ def other_workloads_child(args, names):
 
 def main():
     args = parse()
+    if args.cpu_worker:
+        cpu_worker_main()
+        return
     if args.other_workloads_only:
         import torch
 
@@ -654,6 +886,30 @@ def main():
               f"WORLD_SIZE {world}); the inject path needs no collective and shards by "
               "request, KV head or layer range with no exchange step.", file=sys.stderr)
         sys.exit(2)
+    # Every child process is started here, before this process makes any GPU
+    # call: the CPU-baseline workers (idle until fed) and, run to completion,
+    # the other-workloads child.
+    workers = None
+    if not args.no_cpu_baseline and args.pool_requests > 0:
+        workers = start_cpu_workers()
+    try:
+        run(args, workers)
+    finally:
+        stop_cpu_workers(workers)
+
+
+def run(args, workers):
+    # The other workloads first, in a child process, while this process has
+    # not touched the GPU: timed after this process had allocated and freed
+    # the 64-request batch, the 80-layer batch ran 7 % slower than on a fresh
+    # device (5.61 vs 5.24 ms on one box).
+    others = None
+    if not args.no_other_workloads and args.store == "device" and not args.flush:
+        names = [n for n in ("tiny_L1_H2_D64", "llama3_8b_k5", "llama3_8b_k50",
+                             "llama3_8b_batch64_k50", "llama3_70b_batch16_k50",
+                             "llama3_8b_batch64_k50_h1")
+                 if n != args.workload]
+        others = other_workloads_child(args, names)
 
     import torch
 
@@ -661,17 +917,6 @@ def main():
 
     lib = prkv.lib()
     torch.cuda.set_device(0)
-
-    # The other workloads first, in a child process, while this process
-    # holds no large allocation: timed after this process had allocated and
-    # freed the 64-request batch, the 80-layer batch ran 7 % slower than on a
-    # fresh device (5.61 vs 5.24 ms on one box).
-    others = None
-    if not args.no_other_workloads and args.store == "device" and not args.flush:
-        names = [n for n in ("tiny_L1_H2_D64", "llama3_8b_k5", "llama3_8b_k50",
-                             "llama3_8b_batch64_k50", "llama3_70b_batch16_k50")
-                 if n != args.workload]
-        others = other_workloads_child(args, names)
 
     ceiling = copy_ceiling_gbps(torch)
 
@@ -704,22 +949,21 @@ def main():
     def step_kernel():
         call(lib.inject_topk, kargs, "inject_topk")
 
-    scratch = torch.empty(1 << 29, dtype=torch.int16, device="cuda") if args.flush else None
+    flusher = Flusher(torch) if args.flush else None
 
     def timed(step):
         """(wall seconds, sorted per-launch ms, mean ms) of args.steps launches."""
         for _ in range(args.warmup):
             step()
         torch.cuda.synchronize()
-        if scratch is not None:
+        if flusher is not None:
             # launches timed one by one, each after a 1 GiB fill that evicts the MALL
             starts = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
             ends = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps)]
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for i in range(args.steps):
-                with torch.cuda.stream(stream):
-                    scratch.fill_(i)
+                flusher(torch, stream)
                 starts[i].record(stream)
                 step()
                 ends[i].record(stream)
@@ -742,10 +986,15 @@ def main():
     # the step: the whole path on the device from the HBM-resident batch
     wall_s, step_per_ms, step_ms = timed(step_device)
     assert int(dw.status.item()) == 0, "device path reported skipped tokens"
-    ms_per_step = step_ms if scratch is not None else max(wall_s * 1e3 / args.steps, step_ms)
+    ms_per_step = step_ms if flusher is not None else max(wall_s * 1e3 / args.steps, step_ms)
     # the dominant kernel alone (same kernel, mapping already resident)
     _, per_ms, kernel_ms = timed(step_kernel)
     assert int(dw.status.item()) == 0
+
+    # the plain copy of the same bytes between the same addresses (and a
+    # contiguous one), for the attainable-bandwidth reference
+    own_ceiling = None if args.no_ceiling else \
+        gather_scatter_ceiling(torch, dw, args.steps, args.warmup, flusher)
 
     graph = None
     if args.graph:
@@ -790,6 +1039,23 @@ def main():
         perm = {"what": "the step with every request's facts in a shuffled order",
                 "ms": p_ms, "ratio_to_step": p_ms / step_ms}
         step_device()   # facts back in drawn order
+
+    slot_check = None
+    if not args.no_slot_check:
+        # the same step with the device duplicate-slot check on
+        dw.setup_device_batch(flags=prkv.BATCH_CHECK_SLOTS)
+        cargs = dw.inject_device_args()
+
+        def step_checked():
+            call(lib.inject_topk_device, cargs, "inject_topk_device")
+
+        _, _, c_ms = timed(step_checked)
+        assert int(dw.status.item()) == 0, "the slot check flagged a valid batch"
+        slot_check = {"what": "the step with PRKV_BATCH_CHECK_SLOTS (slot set cleared, "
+                              "filled by the mapping kernel, colliding tokens marked)",
+                      "ms": c_ms, "added_ms": c_ms - step_ms}
+        dw.setup_device_batch()
+        dargs = dw.inject_device_args()
 
     n_tok = dw.n_tokens
     alg_bytes = n_tok * spec.bytes_per_token
@@ -901,8 +1167,8 @@ def main():
     cpu = cpu_pool = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
-        if args.pool_requests > 0:
-            cpu_pool = cpu_baseline_pool(w, args.pool_requests)
+        if workers is not None:
+            cpu_pool = cpu_baseline_pool(w, args.pool_requests, workers)
 
 
     out = {
@@ -930,8 +1196,14 @@ def main():
         },
         "hbm_gbps": achieved,
         "pct_of_peak": 100.0 * achieved / PEAK_HBM_GBPS,
-        "pct_of_copy_ceiling": 100.0 * achieved / max(ceiling.values()),
-        "copy_ceiling_gbps": ceiling,
+        "pct_of_copy_ceiling": (100.0 * achieved / own_ceiling["gbps"]) if own_ceiling else None,
+        "copy_ceiling": {
+            "what": "plain copy of the launch's bytes (libprkv_ceiling.so): every token's K "
+                    "and V row of every layer from arena to cache, no rotation, 16-byte "
+                    "nontemporal loads and stores; mapped = the batch's own arena rows and "
+                    "cache slots, contiguous = rows t -> t; best of two wave orders x three "
+                    "workgroup sizes",
+            "hand_written": own_ceiling, "library_copies_gbps": ceiling},
         "step": "inject_topk_device: plan + per-token mapping + inject kernels, batch "
                 "(fact ids, prefixes, block tables) resident in HBM",
         "step_ms": {"mean": step_ms, "median": step_per_ms[len(step_per_ms) // 2]},
@@ -953,6 +1225,7 @@ def main():
         "cpu_baseline": cpu,
         "cpu_baseline_all_cores": cpu_pool,
         "permuted_order": perm,
+        "slot_check": slot_check,
         "graph_replay": graph,
         "retrieval": retrieval,
         "attention": attn,

@@ -233,12 +233,14 @@ int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row
  * req_fact_ptr[r+1]) in rank order, a prefix of start_pos[r] tokens, and
  * block table block_tables[r*bt_stride .. + bt_len[r]).  max_facts bounds
  * req_fact_ptr[n_req]; max_tokens bounds the injected token count and sizes
- * the workspace. */
+ * the workspace.  flags: 0, or PRKV_BATCH_CHECK_SLOTS (see
+ * inject_topk_device). */
+#define PRKV_BATCH_CHECK_SLOTS 1
 typedef struct prkv_device_batch {
   int32_t n_req;
   int32_t bt_stride;
   int32_t max_facts;
-  int32_t pad_;
+  int32_t flags;
   int64_t max_tokens;
   const int32_t* req_fact_ptr;  /* [n_req + 1] */
   const int32_t* fact_ids;      /* [req_fact_ptr[n_req]] */
@@ -261,7 +263,10 @@ int store_upload_fact_table(const prkv_store* st, void* d_table, size_t table_by
  * at 8; per-fact plan (16 bytes each) at 256; then the per-token arrays
  * src_row, pos, slot (int32 [max_tokens] each) -- the same mapping
  * build_slot_mapping produces on the host, valid after the call's kernels
- * have run (a row of -1 marks a token that failed validation). */
+ * have run (a row of -1 marks a token that failed validation or, with
+ * PRKV_BATCH_CHECK_SLOTS, whose slot another token also maps to); then the
+ * duplicate-slot set used by PRKV_BATCH_CHECK_SLOTS: uint32 entries, as many
+ * as the smallest power of two >= max(64, 2 * max_tokens). */
 int inject_device_workspace_bytes(int32_t max_facts, int64_t max_tokens, size_t* bytes);
 
 /* The whole retrieve-and-inject step on the device, from a batch resident in
@@ -285,11 +290,20 @@ int inject_device_workspace_bytes(int32_t max_facts, int64_t max_tokens, size_t*
  * the device never faults: the token is skipped and d_status (optional) gets
  * 2 (position out of range), 4 (block table too short or block id out of
  * range), 8 (unknown fact id), 16 (more than max_tokens tokens; the excess is
- * dropped) or 32 (more than max_facts facts).  Duplicate slots are NOT
- * detected on the device (block tables from one allocator never overlap);
- * build_slot_mapping checks them on the host.  Host-side argument errors
- * return INVALID_ARG / ALIGNMENT / BUFFER_TOO_SMALL / NO_DEVICE with nothing
- * enqueued. */
+ * dropped) or 32 (more than max_facts facts).
+ * Duplicate slots (two tokens of the batch mapped to one cache slot, e.g.
+ * block tables that share a block; the result would depend on write order)
+ * are detected only when batch->flags has PRKV_BATCH_CHECK_SLOTS: every
+ * token whose slot another token of the batch also maps to is skipped (none
+ * of them is written, the rest of the batch is) and d_status gets 128.  The
+ * check always takes the separate kernels, plus a clear of the workspace's
+ * slot set and a pass that marks the colliding tokens (KV-connector axiom,
+ * section 3.4: blocks are allocated to the request, then scatter-copied;
+ * build_slot_mapping rejects such a batch on the host with DUPLICATE_SLOT).
+ * Without the flag duplicate slots are not detected (block tables from one
+ * allocator never overlap) and the colliding writes race.
+ * Host-side argument errors (including unknown flags) return INVALID_ARG /
+ * ALIGNMENT / BUFFER_TOO_SMALL / NO_DEVICE with nothing enqueued. */
 int inject_topk_device(const prkv_store* st, const void* d_fact_table,
                        const prkv_device_batch* batch, void* const* k_cache_layers,
                        void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,
@@ -305,7 +319,7 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
  * hipMalloc, no host-side allocation on success).  Limits: the batch bounds
  * must fit the array, i.e. inject_device_workspace_bytes(batch->max_facts,
  * batch->max_tokens) <= PRKV_NOALLOC_SCRATCH_BYTES (16 MiB: e.g. 4,096 facts
- * and 1,300,000 tokens), else PRKV_ERR_BUFFER_TOO_SMALL with nothing
+ * and 690,000 tokens), else PRKV_ERR_BUFFER_TOO_SMALL with nothing
  * enqueued.  Every call on one GPU shares that GPU's array and leaves the
  * last call's mapping in it; nothing in it needs to start at zero.  Calls
  * that overlap on one GPU (several streams, several threads or processes'

@@ -3,7 +3,9 @@
     python -m pre_rope_kv_amd.build        (or __graft_entry__.build())
 
 The host half (prkv_host.cpp) is plain C++17 built with g++; the device half
-(prkv_inject.hip) is built with hipcc for gfx950 only.  Packed fp32 VALU
+(prkv_inject.hip, prkv_retrieve.hip, prkv_attend.hip) is built with hipcc for
+gfx950 only.  libprkv_ceiling.so (prkv_ceiling.hip, a plain streaming copy)
+is built beside it for the bench's attainable-bandwidth reference.  Packed fp32 VALU
 instructions are disabled and FP contraction is off: the compensated
 rotation relies on every product and sum being rounded exactly as written.
 """
@@ -18,6 +20,9 @@ CSRC = os.path.join(HERE, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libprkv.so")
+# bench-only: a plain streaming copy with the inject kernel's memory
+# instructions, the attainable-bandwidth reference the bench reports
+CEILING_LIB = os.path.join(HERE, "libprkv_ceiling.so")
 ROCM = os.environ.get("ROCM_PATH", "/opt/rocm")
 ARCH = "gfx950"
 DEVICE_SOURCES = ["prkv_inject.hip", "prkv_retrieve.hip", "prkv_attend.hip"]
@@ -55,6 +60,12 @@ def build(verbose=False):
     _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
           f"-Wl,-rpath,{ROCM}/lib"], verbose)
     os.replace(tmp, LIB)
+    ceil_o = os.path.join(BUILD, "prkv_ceiling.o")
+    _run([hipcc, *HIP_FLAGS, "-c", os.path.join(CSRC, "prkv_ceiling.hip"), "-o", ceil_o], verbose)
+    tmp = CEILING_LIB + ".tmp"
+    _run([hipcc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, ceil_o,
+          f"-Wl,-rpath,{ROCM}/lib"], verbose)
+    os.replace(tmp, CEILING_LIB)
     return LIB
 
 

@@ -1,0 +1,152 @@
+// libprkv_ceiling.so: a measuring stick for the inject kernel, not part of
+// the path.  A plain copy over the inject launch's own buffers and
+// addresses, with no rotation, metadata staging or index arithmetic beyond
+// the row lookup: for every token t and layer l,
+//
+//   K_dst[l][dst_row[t]] = K_src[l][src_row[t]]
+//   V_dst[l][dst_row[t]] = V_src[l][src_row[t]]          (rows of row_bytes)
+//
+// With src_row = the arena rows and dst_row = the cache slots of a mapped
+// batch, it moves exactly the bytes of that batch's inject launch between
+// exactly the same addresses; with both NULL (rows t -> t) it is a
+// contiguous copy of the same amount.  16-byte nontemporal loads and stores
+// like the inject kernel's, 64-bit addressing.  One wave per (token, layer):
+// it loads the K and V rows (row_bytes / 1024 vectors of 16 bytes per lane
+// each) and then stores them.  Waves are ordered token-major (consecutive
+// waves: the layers of one token) or layer-major (consecutive waves: the
+// tokens of one layer), in workgroups of 64, 256 or 1024 lanes; the bench
+// takes the fastest.  Every row index must lie inside its buffer; the caller
+// checks them before the call.
+//
+// C ABI (bench use only):
+//   ceiling_gather_scatter(k_src, v_src, src_layer_bytes, k_dst, v_dst,
+//                          dst_layer_bytes, src_row, dst_row, n_tokens,
+//                          num_layers, row_bytes, order, threads, stream)
+//     row_bytes: 1024, 2048 or 4096; order: 0 token-major, 1 layer-major;
+//     threads: 64, 256 or 1024 per workgroup.  Returns 0, -1 for bad
+//     arguments, -10 for a launch error.
+//   ceiling_empty(grid, stream)
+//     an empty kernel of `grid` 256-lane workgroups (the launch floor).
+
+#include <hip/hip_runtime.h>
+
+#include <cstdint>
+
+namespace {
+
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+constexpr int kWave = 64;
+
+template <int THREADS, int ORDER, int PER_LANE>
+__global__ __launch_bounds__(THREADS) void gather_scatter_kernel(
+    const u32x4* __restrict__ ks, const u32x4* __restrict__ vs, int64_t src_layer_vecs,
+    u32x4* __restrict__ kd, u32x4* __restrict__ vd, int64_t dst_layer_vecs,
+    const int32_t* __restrict__ src_row, const int32_t* __restrict__ dst_row, int64_t n,
+    int num_layers) {
+  constexpr int kRowVecs = PER_LANE * kWave;
+  const int lane = threadIdx.x % kWave;
+  const int64_t w = (int64_t(blockIdx.x) * THREADS + threadIdx.x) / kWave;
+  if (w >= n * num_layers) return;
+  int64_t t;
+  int64_t l;
+  if (ORDER == 0) {
+    t = w / num_layers;
+    l = w % num_layers;
+  } else {
+    l = w / n;
+    t = w % n;
+  }
+  const int64_t s = (src_row ? int64_t(src_row[t]) : t) * kRowVecs + lane;
+  const int64_t d = (dst_row ? int64_t(dst_row[t]) : t) * kRowVecs + lane;
+  const u32x4* a = ks + l * src_layer_vecs + s;
+  const u32x4* b = vs + l * src_layer_vecs + s;
+  u32x4 x[PER_LANE], y[PER_LANE];
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    x[j] = __builtin_nontemporal_load(a + j * kWave);
+    y[j] = __builtin_nontemporal_load(b + j * kWave);
+  }
+  u32x4* c = kd + l * dst_layer_vecs + d;
+  u32x4* e = vd + l * dst_layer_vecs + d;
+#pragma unroll
+  for (int j = 0; j < PER_LANE; ++j) {
+    __builtin_nontemporal_store(x[j], c + j * kWave);
+    __builtin_nontemporal_store(y[j], e + j * kWave);
+  }
+}
+
+__global__ __launch_bounds__(256) void empty_kernel() {}
+
+template <int THREADS, int ORDER>
+int launch(const void* ks, const void* vs, int64_t src_layer_vecs, void* kd, void* vd,
+           int64_t dst_layer_vecs, const int32_t* sr, const int32_t* dr, int64_t n, int L,
+           int per_lane, hipStream_t s) {
+  const int64_t grid = (n * L * kWave + THREADS - 1) / THREADS;
+  if (grid > INT32_MAX) return -1;
+  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(THREADS), 1, 1};
+  const u32x4* k_in = static_cast<const u32x4*>(ks);
+  const u32x4* v_in = static_cast<const u32x4*>(vs);
+  u32x4* k_out = static_cast<u32x4*>(kd);
+  u32x4* v_out = static_cast<u32x4*>(vd);
+  switch (per_lane) {
+    case 1: hipLaunchKernelGGL((gather_scatter_kernel<THREADS, ORDER, 1>), g, b, 0, s, k_in, v_in,
+                               src_layer_vecs, k_out, v_out, dst_layer_vecs, sr, dr, n, L); break;
+    case 2: hipLaunchKernelGGL((gather_scatter_kernel<THREADS, ORDER, 2>), g, b, 0, s, k_in, v_in,
+                               src_layer_vecs, k_out, v_out, dst_layer_vecs, sr, dr, n, L); break;
+    case 4: hipLaunchKernelGGL((gather_scatter_kernel<THREADS, ORDER, 4>), g, b, 0, s, k_in, v_in,
+                               src_layer_vecs, k_out, v_out, dst_layer_vecs, sr, dr, n, L); break;
+    default: return -1;
+  }
+  return 0;
+}
+
+template <int ORDER>
+int launch_threads(int threads, const void* ks, const void* vs, int64_t slv, void* kd, void* vd,
+                   int64_t dlv, const int32_t* sr, const int32_t* dr, int64_t n, int L,
+                   int per_lane, hipStream_t s) {
+  switch (threads) {
+    case 64: return launch<64, ORDER>(ks, vs, slv, kd, vd, dlv, sr, dr, n, L, per_lane, s);
+    case 256: return launch<256, ORDER>(ks, vs, slv, kd, vd, dlv, sr, dr, n, L, per_lane, s);
+    case 1024: return launch<1024, ORDER>(ks, vs, slv, kd, vd, dlv, sr, dr, n, L, per_lane, s);
+    default: return -1;
+  }
+}
+
+}  // namespace
+
+extern "C" {
+
+int ceiling_gather_scatter(const void* k_src, const void* v_src, int64_t src_layer_bytes,
+                           void* k_dst, void* v_dst, int64_t dst_layer_bytes,
+                           const int32_t* src_row, const int32_t* dst_row, int64_t n_tokens,
+                           int32_t num_layers, int32_t row_bytes, int32_t order,
+                           int32_t threads, void* stream) {
+  if (!k_src || !v_src || !k_dst || !v_dst || n_tokens < 0 || num_layers < 1 ||
+      (row_bytes != 1024 && row_bytes != 2048 && row_bytes != 4096) || (order != 0 && order != 1))
+    return -1;
+  if (((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src) |
+        reinterpret_cast<uintptr_t>(k_dst) | reinterpret_cast<uintptr_t>(v_dst)) & 15u) ||
+      (src_layer_bytes % 16) || (dst_layer_bytes % 16))
+    return -1;
+  if (n_tokens == 0) return 0;
+  const int per_lane = row_bytes / 1024;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int64_t slv = src_layer_bytes / 16, dlv = dst_layer_bytes / 16;
+  const int rc = order == 0
+      ? launch_threads<0>(threads, k_src, v_src, slv, k_dst, v_dst, dlv, src_row, dst_row,
+                          n_tokens, num_layers, per_lane, s)
+      : launch_threads<1>(threads, k_src, v_src, slv, k_dst, v_dst, dlv, src_row, dst_row,
+                          n_tokens, num_layers, per_lane, s);
+  if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+int ceiling_empty(int32_t grid, void* stream) {
+  if (grid <= 0) return -1;
+  hipLaunchKernelGGL(empty_kernel, dim3(unsigned(grid)), dim3(256), 0,
+                     static_cast<hipStream_t>(stream));
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+}  // extern "C"

@@ -107,6 +107,8 @@ struct DeviceBatch {
   int32_t* pos;
   int32_t* slot;
   int32_t* status;
+  uint32_t* slot_table;        // workspace: open-addressing set of slots, or NULL (no check)
+  uint32_t table_mask;         // capacity - 1 (capacity a power of two)
   int64_t max_tokens;
   int64_t num_blocks;
   int32_t n_req;
@@ -193,6 +195,41 @@ __device__ __forceinline__ int pair_slot(int j) {
 
 __device__ __forceinline__ void flag(int32_t* status, int bits) {
   if (status) atomicOr(status, bits);
+}
+
+constexpr uint32_t kSlotEmpty = 0xFFFFFFFFu;   // never a slot (slots are < 2^31 - 1)
+constexpr uint32_t kSlotDup = 0x80000000u;
+constexpr int kStatusDuplicateSlot = 128;
+
+__device__ __forceinline__ uint32_t slot_hash(uint32_t slot, uint32_t mask) {
+  return (slot * 0x9E3779B1u) & mask;   // Fibonacci hashing; slots are not
+}                                       // multiples of the capacity in general
+
+// Inserts `slot` into the set; on finding it present, marks it as duplicate.
+__device__ __forceinline__ void slot_insert(const DeviceBatch& b, uint32_t slot) {
+  uint32_t h = slot_hash(slot, b.table_mask);
+  for (uint64_t probe = 0; probe <= uint64_t(b.table_mask); ++probe) {
+    const uint32_t prev = atomicCAS(b.slot_table + h, kSlotEmpty, slot);
+    if (prev == kSlotEmpty) return;
+    if ((prev & ~kSlotDup) == slot) {
+      if (!(prev & kSlotDup)) atomicOr(b.slot_table + h, kSlotDup);
+      flag(b.status, kStatusDuplicateSlot);
+      return;
+    }
+    h = (h + 1) & b.table_mask;
+  }
+}
+
+// Whether `slot` (inserted by this call's mapping) is marked duplicate.
+__device__ __forceinline__ bool slot_marked(const DeviceBatch& b, uint32_t slot) {
+  uint32_t h = slot_hash(slot, b.table_mask);
+  for (uint64_t probe = 0; probe <= uint64_t(b.table_mask); ++probe) {
+    const uint32_t e = b.slot_table[h];
+    if (e == kSlotEmpty) return false;
+    if ((e & ~kSlotDup) == slot) return (e & kSlotDup) != 0;
+    h = (h + 1) & b.table_mask;
+  }
+  return false;
 }
 
 // ---------------------------------------------------------------------------
@@ -687,10 +724,37 @@ __global__ __launch_bounds__(kThreads) void materialize_kernel(DeviceBatch b) {
     if (bad) {
       flag(b.status, bad);
       row = -1;
+    } else if (b.slot_table) {
+      slot_insert(b, slot);
     }
     b.src_row[tok] = row;
     b.pos[tok] = bad ? 0 : int32_t(b.chunk_local ? pos0 : ps);
     b.slot[tok] = slot;
+  }
+}
+
+// Duplicate-slot check (optional, PRKV_BATCH_CHECK_SLOTS): the mapping
+// kernel inserts every valid token's slot into an open-addressing set in the
+// workspace (capacity a power of two >= 2 * max_tokens, so an empty entry is
+// always found); a slot found already present is marked with the top bit
+// (slots are < 2^31) and status bit 128 is set.  resolve_kernel then turns
+// every token whose slot is marked into a skipped token (row -1), so neither
+// of two colliding tokens is written, as the host builder rejects the batch.
+// The set is cleared at the start of every call (clear_table_kernel).
+
+__global__ __launch_bounds__(kThreads) void clear_table_kernel(u32x4* table, int64_t n_vec) {
+  const u32x4 empty = {kSlotEmpty, kSlotEmpty, kSlotEmpty, kSlotEmpty};
+  for (int64_t i = int64_t(blockIdx.x) * kThreads + threadIdx.x; i < n_vec;
+       i += int64_t(gridDim.x) * kThreads)
+    table[i] = empty;
+}
+
+__global__ __launch_bounds__(kThreads) void resolve_kernel(DeviceBatch b) {
+  const int64_t n = *b.n_tokens_out;
+  for (int64_t t = int64_t(blockIdx.x) * kThreads + threadIdx.x; t < n;
+       t += int64_t(gridDim.x) * kThreads) {
+    if (b.src_row[t] < 0) continue;
+    if (slot_marked(b, uint32_t(b.slot[t]))) b.src_row[t] = -1;
   }
 }
 
@@ -744,16 +808,21 @@ hipError_t launch(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& v
 
 // Workspace of inject_topk_device: header (n_tokens int64 at 0, n_facts
 // int32 at 8), the per-fact plan at 256, then src_row, pos and slot arrays of
-// max_tokens int32 each, every part 256-byte aligned.
+// max_tokens int32 each, then the duplicate-slot set (table_entries uint32,
+// a power of two >= 2 * max_tokens and >= 64), every part 256-byte aligned.
 struct Workspace {
-  size_t plan, src_row, pos, slot, total;
+  size_t plan, src_row, pos, slot, table, total;
+  uint64_t table_entries;   // <= 2^32 (max_tokens <= 2^31 - 1)
   Workspace(int64_t max_facts, int64_t max_tokens) {
     auto up = [](size_t v) { return (v + 255u) / 256u * 256u; };
     plan = 256;
     src_row = plan + up(size_t(max_facts) * sizeof(FactPlan));
     pos = src_row + up(size_t(max_tokens) * 4u);
     slot = pos + up(size_t(max_tokens) * 4u);
-    total = slot + up(size_t(max_tokens) * 4u);
+    table = slot + up(size_t(max_tokens) * 4u);
+    table_entries = 64;
+    while (table_entries < 2 * uint64_t(max_tokens)) table_entries *= 2;
+    total = table + size_t(table_entries) * 4u;
   }
 };
 
@@ -1032,6 +1101,9 @@ int inject_device_impl(const prkv_store* st, const void* d_fact_table,
   const prkv_device_batch& b = *batch;
   if (b.n_req < 0 || b.max_facts < 0 || b.max_tokens < 0 || b.bt_stride < 0)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "negative batch size");
+  if (b.flags & ~int32_t(PRKV_BATCH_CHECK_SLOTS))
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "unknown batch flags 0x%x", unsigned(b.flags));
+  if (b.max_tokens > INT32_MAX) return prkv::fail(PRKV_ERR_INVALID_ARG, "max_tokens > 2^31-1");
   const int64_t num_slots = num_blocks * int64_t(block_size);
   if (b.max_tokens > num_slots)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "max_tokens %lld exceeds the cache's %lld slots",
@@ -1077,6 +1149,9 @@ int inject_device_impl(const prkv_store* st, const void* d_fact_table,
   db.block_size = block_size;
   db.max_position = st->desc.max_position;
   db.chunk_local = st->desc.key_layout == PRKV_KEYS_CHUNK_LOCAL;
+  const bool check = (b.flags & PRKV_BATCH_CHECK_SLOTS) != 0;
+  db.slot_table = check ? reinterpret_cast<uint32_t*>(base + ws.table) : nullptr;
+  db.table_mask = uint32_t(ws.table_entries - 1);
 
   // Expected token count: max_facts facts of the store's mean length, plus
   // 10 %.  The kernels stay correct for any count up to max_tokens.
@@ -1086,16 +1161,34 @@ int inject_device_impl(const prkv_store* st, const void* d_fact_table,
     expect = std::min<int64_t>(b.max_tokens, int64_t(1.1 * mean * b.max_facts) + 1);
   }
   hipStream_t s = static_cast<hipStream_t>(stream);
-  if (b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs && expect <= kFuseTokens)  // one launch
+  // one launch for small batches; the duplicate check needs the whole
+  // mapping before any write, so it always takes the separate kernels
+  if (!check && b.max_facts <= kFuseFacts && b.n_req <= kFuseReqs && expect <= kFuseTokens)
     return launch_inject(st, b.max_tokens, nullptr, nullptr, nullptr, nullptr, k_cache_layers,
                          v_cache_layers, block_size, num_blocks, d_status, s, &db, expect);
+  hipError_t e;
+  if (check) {
+    const int64_t n_vec = int64_t(ws.table_entries / 4);
+    const int64_t cgrid = std::min<int64_t>((n_vec + kThreads - 1) / kThreads, 1024);
+    hipLaunchKernelGGL(clear_table_kernel, dim3(unsigned(cgrid)), dim3(kThreads), 0, s,
+                       reinterpret_cast<u32x4*>(db.slot_table), n_vec);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "slot table clear launch");
+  }
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(kPlanThreads), 0, s, db);
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "plan launch");
   const int64_t mgrid = (int64_t(b.max_facts) + kWavesPerGroup - 1) / kWavesPerGroup;
   hipLaunchKernelGGL(materialize_kernel, dim3(unsigned(mgrid)), dim3(kThreads), 0, s, db);
   e = hipGetLastError();
   if (e != hipSuccess) return hip_fail(e, "materialize launch");
+  if (check) {
+    const int64_t rgrid =
+        std::max<int64_t>(1, std::min<int64_t>((expect + kThreads - 1) / kThreads, 2048));
+    hipLaunchKernelGGL(resolve_kernel, dim3(unsigned(rgrid)), dim3(kThreads), 0, s, db);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, "duplicate-slot resolve launch");
+  }
   return launch_inject(st, b.max_tokens, db.n_tokens_out, db.src_row, db.pos, db.slot,
                        k_cache_layers, v_cache_layers, block_size, num_blocks, d_status, s,
                        nullptr, expect);

@@ -113,29 +113,48 @@ class DeviceWorkload:
         req_ptr, ids, start, bt, bt_len = w.csr()
         self.req_ptr, self.ids, self.start, self.bt, self.bt_len = req_ptr, ids, start, bt, bt_len
         n = w.n_tokens
-        self.h_map = [torch.empty(max(n, 1), dtype=torch.int32, pin_memory=True)
-                      for _ in range(3)]
+        # two sets of pinned host buffers, used in turn by map_and_copy; each
+        # set's event marks the end of the last copy out of it
+        self.h_maps = [[torch.empty(max(n, 1), dtype=torch.int32, pin_memory=True)
+                        for _ in range(3)] for _ in range(2)]
+        self.h_events = [None, None]
+        self.h_turn = 0
         src, pos, slot = prkv.build_slot_mapping(
             self.store, req_ptr, ids, start, bt, bt_len, w.spec.block_size, w.num_blocks,
-            out=tuple(t.numpy() for t in self.h_map))
+            out=tuple(t.numpy() for t in self.h_maps[0]))
         self.n_tokens = len(src)
-        self.d_map = [t.to(self.device, non_blocking=True) for t in self.h_map]
+        with torch.cuda.stream(self.stream):
+            self.d_map = [t.to(self.device, non_blocking=True) for t in self.h_maps[0]]
         self.stream.synchronize()
         return src, pos, slot
 
     def map_and_copy(self):
-        """Host slot mapping into pinned buffers + async H2D of the three arrays."""
+        """Host slot mapping into pinned buffers + async H2D of the three arrays.
+
+        The host writes a buffer set only after the previous copy out of it
+        has finished (its event), so a mapping that changes between calls can
+        never be torn by a copy still queued behind earlier kernels; with two
+        sets the host mapping of one call overlaps the copy and kernel of the
+        previous one."""
         w = self.w
+        self.h_turn ^= 1
+        bufs, ev = self.h_maps[self.h_turn], self.h_events[self.h_turn]
+        if ev is not None:
+            ev.synchronize()
         prkv.build_slot_mapping(self.store, self.req_ptr, self.ids, self.start, self.bt,
                                 self.bt_len, w.spec.block_size, w.num_blocks,
-                                out=tuple(t.numpy() for t in self.h_map))
+                                out=tuple(t.numpy() for t in bufs))
         with torch.cuda.stream(self.stream):
-            for d, h in zip(self.d_map, self.h_map):
+            for d, h in zip(self.d_map, bufs):
                 d.copy_(h, non_blocking=True)
+            ev = torch.cuda.Event()
+            ev.record(self.stream)
+        self.h_events[self.h_turn] = ev
 
     # -- device-resident batch (device-side slot mapping) --------------------
-    def setup_device_batch(self, max_tokens=None, max_facts=None):
-        """Upload the batch description, the fact table and a workspace."""
+    def setup_device_batch(self, max_tokens=None, max_facts=None, flags=0):
+        """Upload the batch description, the fact table and a workspace.
+        flags: prkv.BATCH_CHECK_SLOTS to detect duplicate slots on the device."""
         w = self.w
         req_ptr, ids, start, bt, bt_len = w.csr()
         dev = self.device
@@ -154,7 +173,7 @@ class DeviceWorkload:
         self.ws_layout = prkv.workspace_layout(self.max_facts, self.max_tokens)
         self.batch = prkv.device_batch(len(req_ptr) - 1, bt.shape[1], self.max_facts,
                                        self.max_tokens, self.d_req_ptr, self.d_ids, self.d_start,
-                                       self.d_bt, self.d_bt_len)
+                                       self.d_bt, self.d_bt_len, flags=flags)
         self.stream.synchronize()
 
     def inject_device(self):

@@ -69,7 +69,7 @@ class DeviceBatch(ctypes.Structure):
         ("n_req", ctypes.c_int32),
         ("bt_stride", ctypes.c_int32),
         ("max_facts", ctypes.c_int32),
-        ("pad_", ctypes.c_int32),
+        ("flags", ctypes.c_int32),
         ("max_tokens", ctypes.c_int64),
         ("req_fact_ptr", ctypes.c_void_p),
         ("fact_ids", ctypes.c_void_p),
@@ -339,15 +339,24 @@ def workspace_layout(max_facts, max_tokens):
     src_row = plan + up(max_facts * 16)
     pos = src_row + up(max_tokens * 4)
     slot = pos + up(max_tokens * 4)
+    table = slot + up(max_tokens * 4)
+    entries = 64
+    while entries < 2 * max_tokens:
+        entries *= 2
     return {"n_tokens": 0, "n_facts": 8, "plan": plan, "src_row": src_row, "pos": pos,
-            "slot": slot, "total": slot + up(max_tokens * 4)}
+            "slot": slot, "slot_table": table, "slot_table_entries": entries,
+            "total": table + 4 * entries}
+
+
+BATCH_CHECK_SLOTS = 1
 
 
 def device_batch(n_req, bt_stride, max_facts, max_tokens, req_fact_ptr, fact_ids, start_pos,
-                 block_tables, bt_len):
+                 block_tables, bt_len, flags=0):
     """prkv_device_batch over device tensors; it holds raw pointers only, so
-    the caller keeps the tensors alive while the batch is in use."""
-    return DeviceBatch(int(n_req), int(bt_stride), int(max_facts), 0, int(max_tokens),
+    the caller keeps the tensors alive while the batch is in use.  flags:
+    0 or BATCH_CHECK_SLOTS (detect duplicate slots on the device)."""
+    return DeviceBatch(int(n_req), int(bt_stride), int(max_facts), int(flags), int(max_tokens),
                        _ptr(req_fact_ptr), _ptr(fact_ids), _ptr(start_pos),
                        _ptr(block_tables), _ptr(bt_len))
 

@@ -86,6 +86,8 @@ def test_inject_topk_device_argument_errors(dw):
     for fields, want in ((dict(max_tokens=dw.w.num_blocks * dw.w.spec.block_size + 1),
                           "INVALID_ARG"),
                          (dict(n_req=-1), "INVALID_ARG"),
+                         (dict(flags=2), "INVALID_ARG"),          # unknown flag bit
+                         (dict(flags=-1), "INVALID_ARG"),
                          (dict(fact_ids=None), "INVALID_ARG"),
                          (dict(start_pos=b.start_pos + 2), "ALIGNMENT")):
         nbatch = with_batch(**fields)

@@ -11,6 +11,7 @@ of the tokens the device must skip put back to the sentinel.
 """
 
 import dataclasses
+from collections import Counter
 
 import numpy as np
 import pytest
@@ -354,3 +355,107 @@ def test_two_streams_inject_concurrently():
     assert int(dw.status.item()) == 0
     got_k, got_v = dw.listed_blocks_host(blocks)
     assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v)
+
+
+@dataclasses.dataclass
+class _SharedBlocks(workloads.Workload):
+    """A workload whose block tables share blocks (listed once each)."""
+
+    def listed_blocks(self):
+        return sorted(set(super().listed_blocks()))
+
+
+def _shared_block_workload(name, L=2, H=8, D=128):
+    """Two requests; request 1's first block is request 0's second block, so
+    positions 16 + o of request 0 and o of request 1 land in one slot."""
+    facts = {0: 9, 1: 14, 2: 5, 3: 20}
+    w = custom_workload(name, L, H, D, 16, facts, [([0, 1], 7), ([2, 3], 3)])
+    bt0, bt1 = w.block_tables
+    bt1 = bt1.copy()
+    bt1[0] = bt0[1]
+    fields = {f.name: getattr(w, f.name) for f in dataclasses.fields(w)}
+    fields["block_tables"] = [bt0, bt1]
+    return _SharedBlocks(**fields)
+
+
+@pytest.mark.parametrize("max_facts", [None, FUSE_LIMIT + 44], ids=["small", "kernels"])
+def test_duplicate_slots_detected_with_check_flag(max_facts):
+    """With PRKV_BATCH_CHECK_SLOTS, tokens whose slot another token of the
+    batch also maps to are all skipped (neither is written), status gets 128,
+    and everything else matches the oracle; the host builder rejects the same
+    batch with DUPLICATE_SLOT."""
+    w = _shared_block_workload("dup_slots")
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    req_ptr, ids, start, bt, bt_len = w.csr()
+    with pytest.raises(prkv.PrkvError) as err:
+        prkv.build_slot_mapping(dw.store, req_ptr, ids, start, bt, bt_len, 16, w.num_blocks)
+    assert err.value.name == "DUPLICATE_SLOT"
+    dw.setup_device_batch(max_facts=max_facts, flags=prkv.BATCH_CHECK_SLOTS)
+    dw.status.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 128
+    src, _, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
+    dups = sorted(s for s, c in Counter(slot).items() if c > 1)
+    assert len(dups) == 11          # request 0's positions 19..29, request 1's 3..13
+    # the device mapping marks exactly the colliding tokens as skipped
+    n, d_src, _, d_slot = dw.device_mapping()
+    assert n == len(slot) and np.array_equal(d_slot, np.array(slot, np.int32))
+    skipped = {t for t, s in enumerate(slot) if s in set(dups)}
+    assert all((d_src[t] == -1) == (t in skipped) for t in range(n))
+    blocks = w.listed_blocks()
+    img_k, img_v, mask = _expect(w, blocks, dups)
+    gk, gv = dw.listed_blocks_host(blocks)
+    compare(img_k, img_v, gk, gv, mask)
+    sp = w.spec
+    assert dw.count_non_sentinel() == \
+        2 * sp.num_layers * int(mask.sum()) * sp.num_kv_heads * sp.head_dim
+
+
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k5"])
+def test_check_flag_on_a_valid_batch_changes_nothing(name):
+    """A batch without duplicates: with the check the cache, status and
+    mapping equal those of the unchecked step, bit for bit."""
+    w = workloads.make(name)
+    dw = harness.DeviceWorkload(w, host_mapping=False, gen_device="cuda")
+    out = []
+    for flags in (0, prkv.BATCH_CHECK_SLOTS):
+        dw.reset_cache()
+        dw.setup_device_batch(flags=flags)
+        dw.status.zero_()
+        dw.inject_device()
+        torch.cuda.synchronize()
+        gk, gv = dw.listed_blocks_host(w.listed_blocks())
+        n, src, pos, slot = dw.device_mapping()
+        out.append((int(dw.status.item()), n, src.copy(), pos.copy(), slot.copy(), gk, gv))
+    a, b = out
+    assert a[0] == b[0] == 0 and a[1] == b[1] == w.n_tokens
+    assert all(np.array_equal(x, y) for x, y in zip(a[2:], b[2:]))
+    _check(dw, w)
+
+
+def test_check_flag_many_duplicates():
+    """Two requests with identical block tables and prefixes: every position
+    of request 0 (39 tokens) collides with request 1's (41 tokens), so only
+    request 1's last two tokens and the third request are written."""
+    facts = {f: 10 + 3 * f for f in range(8)}
+    w = custom_workload("dup_all", 3, 4, 64, 16, facts,
+                        [([0, 1, 2], 5), ([3, 4], 5), ([5, 6, 7], 2)], num_blocks=512)
+    bts = list(w.block_tables)
+    bts[1] = bts[0].copy()            # request 1 shares request 0's blocks
+    fields = {f.name: getattr(w, f.name) for f in dataclasses.fields(w)}
+    fields["block_tables"] = bts
+    w = _SharedBlocks(**fields)
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    dw.setup_device_batch(flags=prkv.BATCH_CHECK_SLOTS)
+    dw.status.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 128
+    _, _, slot = paged.token_mapping(w.requests(), w.fact_rows, 16)
+    dups = sorted(s for s, c in Counter(slot).items() if c > 1)
+    assert len(dups) == sum(facts[f] for f in (0, 1, 2))
+    blocks = w.listed_blocks()
+    img_k, img_v, mask = _expect(w, blocks, dups)
+    gk, gv = dw.listed_blocks_host(blocks)
+    compare(img_k, img_v, gk, gv, mask)

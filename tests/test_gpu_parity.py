@@ -520,3 +520,25 @@ def test_host_dram_store(name, path):
     compare(img_k, img_v, gk, gv, written_mask(w, blocks))
     sp = w.spec
     assert dw.count_non_sentinel() == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
+
+
+def test_map_and_copy_alternating_batches():
+    """The host-mapped step repeated with the batch changing every call (two
+    orders of the same facts: the same slots, other positions), each mapping
+    built into pinned buffers while earlier copies and kernels may still be
+    queued: the cache after the last call is exactly the last order's."""
+    facts = {0: 37, 1: 12, 2: 58, 3: 21, 4: 9}
+    orders = ([0, 1, 2, 3, 4], [3, 0, 4, 2, 1])
+    w = custom_workload("alternate", 4, 8, 128, 16, facts, [(orders[0], 11)])
+    dw = harness.DeviceWorkload(w)
+    for i in range(9):
+        dw.ids = np.asarray(orders[i % 2], np.int32)
+        dw.map_and_copy()
+        dw.inject()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    last = workloads.dataclasses.replace(w, retrieved=[orders[0]])   # i = 8: order 0
+    blocks = w.listed_blocks()
+    gk, gv = dw.listed_blocks_host(blocks)
+    img_k, img_v, _ = oracle_images(last, "cuda")
+    compare(img_k, img_v, gk, gv, written_mask(last, blocks))
