@@ -80,6 +80,11 @@ def parse():
     return ap.parse_args()
 
 
+# bench.py under rocprofv3: no child processes (the profiler's library has
+# initialised the GPU before the program starts) and only the path's kernels
+PROFILE_FLAGS = ("--no-cpu-baseline --no-e2e --no-other-workloads --no-ceiling "
+                 "--no-slot-check")
+
 # kernels with committed rocprofv3 summaries: name prefix -> source file
 PROFILED = {"inject_kernel": "prkv_inject.hip", "attend_kernel": "prkv_attend.hip"}
 ATTN_Q_LEN = 16        # query tokens per request in the attention section
@@ -221,6 +226,28 @@ def summarize_profile(workload, trace_dir, fetch_dir, write_dir, commands):
             f"- kernel_source_sha256: `{kernel_source_sha(kernel)}`",
             "",
         ]
+        groups = sorted({r["Grid_Size_X"] for r in all_trace if r["Kernel_Name"].startswith(kernel)},
+                        key=int)
+        if len(groups) > 1:
+            # several launch shapes of one kernel (e.g. the fused single-launch
+            # step and the kernel alone on a host-built mapping)
+            lines += ["## Launch shapes (grouped by grid size)", "",
+                      "| grid (workgroups) | calls | median ms | min ms | fetch B/launch | "
+                      "write B/launch | traffic / algorithmic |", "|---|---|---|---|---|---|---|"]
+            fr = rows(fetch_dir, "counter_collection.csv")
+            wr = rows(write_dir, "counter_collection.csv")
+            for g in groups:
+                d = [(int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e6 for r in all_trace
+                     if r["Kernel_Name"].startswith(kernel) and r["Grid_Size_X"] == g]
+                fv = [float(r["Counter_Value"]) for r in fr if r["Kernel_Name"].startswith(kernel)
+                      and r["Grid_Size"] == g and r["Counter_Name"] == "FETCH_SIZE"]
+                wv = [float(r["Counter_Value"]) for r in wr if r["Kernel_Name"].startswith(kernel)
+                      and r["Grid_Size"] == g and r["Counter_Name"] == "WRITE_SIZE"]
+                fb = statistics.mean(fv) * f_scale * 1024 if fv else float("nan")
+                wb = statistics.mean(wv) * w_scale * 1024 if wv else float("nan")
+                lines.append(f"| {int(g) // 256} | {len(d)} | {statistics.median(d):.4f} | "
+                             f"{min(d):.4f} | {fb:.0f} | {wb:.0f} | {(fb + wb) / alg:.4f} |")
+            lines.append("")
         with open(profile_path(workload, kernel), "w") as fh:
             fh.write("\n".join(lines))
         print(profile_path(workload, kernel))
@@ -300,14 +327,29 @@ class Flusher:
             self.buf.fill_(self.i)
 
 
-def time_launches(torch, fn, stream, steps, warmup, flusher=None):
+def queue_ahead(torch, stream, ms=2.0):
+    """Enqueue ~ms of GPU work that touches no memory (a clock spin) on
+    `stream`, so that launches the host enqueues meanwhile are already
+    waiting when the GPU reaches them: events around them then time the GPU,
+    not the host's launch rate (which bounds back-to-back launches of a few
+    microseconds)."""
+    with torch.cuda.stream(stream):
+        torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))   # cycles at ~2 GHz (bounded spin)
+
+
+def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False):
     """Mean and median ms per launch of fn() on `stream`: back to back (warm),
-    or, with a flusher, one at a time each after a MALL-evicting fill (cold)."""
+    or, with a flusher, one at a time each after a MALL-evicting fill (cold).
+    queued: warm launches are enqueued behind a clock spin (queue_ahead), so
+    the figures are GPU time even for launches shorter than the host's
+    launch cost."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     if flusher is None:
         evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+        if queued:
+            queue_ahead(torch, stream)
         evs[0].record(stream)
         for i in range(steps):
             fn()
@@ -351,6 +393,7 @@ def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
     assert 0 <= int(slot[:n].min()) and int(slot[:n].max()) < num_slots
     assert n <= w.capacity_rows and n <= num_slots
     nbytes = n * sp.bytes_per_token
+    queued = nbytes < COLD_BELOW_BYTES
     out = {"bytes_per_launch": nbytes}
     for name, rows in (("mapped", (src.data_ptr(), slot.data_ptr())), ("contiguous", (None, None))):
         best = None
@@ -365,7 +408,7 @@ def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
                     if rc != 0:
                         raise RuntimeError(f"ceiling_gather_scatter failed ({rc})")
 
-                ms, _ = time_launches(torch, fn, stream, steps, warmup)
+                ms, _ = time_launches(torch, fn, stream, steps, warmup, queued=queued)
                 if best is None or ms < best[0]:
                     best = (ms, order, threads, fn)
         ms, order, threads, fn = best
@@ -386,13 +429,14 @@ def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
 
 
 def launch_floor(torch, stream, steps=200):
-    """ms per launch of an empty kernel, back to back: one workgroup, and one
-    of 2,048 workgroups (the shortest time any launch can take here)."""
+    """ms per launch of an empty kernel, back to back behind a clock spin (so
+    the GPU, not the host, sets the pace): one workgroup, and 2,048 workgroups
+    (the shortest time any launch can take here)."""
     lib = ceiling_lib()
     out = {}
     for grid in (1, 2048):
         ms, med = time_launches(torch, lambda g=grid: lib.ceiling_empty(g, stream.cuda_stream),
-                                stream, steps, 10)
+                                stream, steps, 10, queued=True)
         out[f"grid_{grid}_ms"] = ms
     return out
 
@@ -635,8 +679,8 @@ def k_sweep_rows(args, torch, lib, w, dw, flusher):
     for k in (5, 10, 20, 50):
         fused = step_fn(k, k, dw.workspace)
         three = step_fn(k, ptr_cap, big_ws)
-        ms, _ = time_launches(torch, fused, stream, args.steps, args.warmup)
-        ms3, _ = time_launches(torch, three, stream, args.steps, args.warmup)
+        ms, _ = time_launches(torch, fused, stream, args.steps, args.warmup, queued=True)
+        ms3, _ = time_launches(torch, three, stream, args.steps, args.warmup, queued=True)
         ms_cold, med_cold = time_launches(torch, fused, stream, args.steps, args.warmup, flusher)
         assert int(dw.status.item()) == 0
         n_tok = sum(w.length_of(f) for f in w.retrieved[0][:k])
@@ -775,23 +819,27 @@ def other_workloads(args, torch, lib, names):
 
         step = caller(lib.inject_topk_device, dw.inject_device_args())
         kernel = caller(lib.inject_topk, dw.inject_args())
-        step_ms, step_med = time_launches(torch, step, stream, args.steps, args.warmup)
-        kernel_ms, kernel_med = time_launches(torch, kernel, stream, args.steps, args.warmup)
-        assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
         alg = dw.n_tokens * spec.bytes_per_token
+        cold = alg < COLD_BELOW_BYTES
+        step_ms, step_med = time_launches(torch, step, stream, args.steps, args.warmup,
+                                          queued=cold)
+        kernel_ms, kernel_med = time_launches(torch, kernel, stream, args.steps, args.warmup,
+                                              queued=cold)
+        assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
         profiled = w is w0 and args.cache_layout == "nhd"
         row = {
             "tokens": dw.n_tokens, "layers": spec.num_layers, "kv_heads": spec.num_kv_heads,
             "requests": spec.n_requests, "k": spec.k, "block_size": spec.block_size,
             "num_blocks": w.num_blocks, "bytes_per_launch": alg,
-            "warm": {"step_ms": step_ms, "step_median_ms": step_med,
+            "warm": {"timing": "back to back" + (", enqueued behind a clock spin so the events "
+                                                  "time the GPU, not the host" if cold else ""),
+                     "step_ms": step_ms, "step_median_ms": step_med,
                      "tokens_per_s": dw.n_tokens / (step_ms * 1e-3),
                      "kernel_ms": kernel_ms, "kernel_median_ms": kernel_med,
                      "hbm_gbps": alg / (kernel_ms * 1e-3) / 1e9,
                      "frac_of_peak": alg / (kernel_ms * 1e-3) / 1e9 / PEAK_HBM_GBPS},
             "traffic": read_profile_traffic(name) if profiled else None,
         }
-        cold = alg < COLD_BELOW_BYTES
         if cold:
             c_step, c_step_med = time_launches(torch, step, stream, args.steps, args.warmup,
                                                flusher)
@@ -864,14 +912,13 @@ def main():
         wl = "" if args.workload == DEFAULT_WORKLOAD else f"--workload {args.workload} "
         cmds = [
             f"rocprofv3 --kernel-trace --stats -T -d {trace_dir} -o inject -f csv -- "
-            f"python -u bench.py {wl}--steps 20 --warmup 5 --no-cpu-baseline --no-e2e "
-            "--no-other-workloads",
+            f"python -u bench.py {wl}--steps 20 --warmup 5 {PROFILE_FLAGS}",
             f"rocprofv3 --pmc FETCH_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {fetch_dir} -o fetch -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
-            "--no-cpu-baseline --no-e2e --no-other-workloads",
+            f"{PROFILE_FLAGS}",
             f"rocprofv3 --pmc WRITE_SIZE --kernel-include-regex \"{regex}\" "
             f"-T -d {write_dir} -o write -f csv -- python -u bench.py {wl}--steps 3 --warmup 1 "
-            "--no-cpu-baseline --no-e2e --no-other-workloads",
+            f"{PROFILE_FLAGS}",
             f"python bench.py --workload {args.workload} --summarize-profile {trace_dir} "
             f"{fetch_dir} {write_dir}",
         ]
