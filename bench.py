@@ -70,6 +70,8 @@ def parse():
                          "launch and time launches one by one (for workloads far below 1 GiB)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the hand-written streaming-copy reference of the same bytes")
+    ap.add_argument("--no-host-store", action="store_true",
+                    help="skip the host-DRAM store figures (zero-copy and staged)")
     ap.add_argument("--no-slot-check", action="store_true",
                     help="skip timing the step with the device duplicate-slot check on")
     ap.add_argument("--cpu-worker", action="store_true",
@@ -83,7 +85,7 @@ def parse():
 # bench.py under rocprofv3: no child processes (the profiler's library has
 # initialised the GPU before the program starts) and only the path's kernels
 PROFILE_FLAGS = ("--no-cpu-baseline --no-e2e --no-other-workloads --no-ceiling "
-                 "--no-slot-check")
+                 "--no-slot-check --no-host-store")
 
 # kernels with committed rocprofv3 summaries: name prefix -> source file
 PROFILED = {"inject_kernel": "prkv_inject.hip", "attend_kernel": "prkv_attend.hip"}
@@ -425,6 +427,63 @@ def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
     dw.reset_cache()
     dw.inject()
     torch.cuda.synchronize()
+    return out
+
+
+def host_store_figures(torch, lib, w, dw_hbm, steps, warmup, hbm_kernel_ms):
+    """The workload with its store in pinned host DRAM (the pages' capacity
+    lever), injected into the HBM workload's cache two ways, each step timed
+    by wall clock between synchronizations: zero-copy (the inject kernel
+    reads the retrieved rows over PCIe), and staged (store_stage_facts copies
+    the batch's facts into HBM in chunks on a second stream, each chunk
+    injected as soon as it has landed; the staging store reuses the HBM
+    workload's arenas, into which it writes the same rows it already holds).
+    added_ms = step - the HBM-resident inject kernel."""
+    from pre_rope_kv_amd import harness, prkv
+
+    t_setup = time.perf_counter()
+    hw = harness.DeviceWorkload(w, store_location="host", cache_from=dw_hbm)
+    setup_s = time.perf_counter() - t_setup
+    n = hw.n_tokens
+    pcie_bytes = n * w.spec.bytes_per_token // 2     # the reads cross PCIe, the writes do not
+
+    def wall(step):
+        for _ in range(warmup):
+            step()
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(steps):
+            step()
+        torch.cuda.synchronize()
+        assert int(hw.status.item()) == 0, "host-store inject reported skipped tokens"
+        return (time.perf_counter() - t0) * 1e3 / steps
+
+    kargs = hw.inject_args()
+
+    def zero_copy():
+        rc = lib.inject_topk(*kargs)
+        if rc != 0:
+            raise prkv.PrkvError(rc, "inject_topk", lib.last_error_string().decode())
+
+    zc_ms = wall(zero_copy)
+    out = {"setup_s": setup_s, "pcie_read_bytes": pcie_bytes,
+           "zero_copy": {"ms": zc_ms, "added_ms": zc_ms - hbm_kernel_ms,
+                         "pcie_gbps": pcie_bytes / (zc_ms * 1e-3) / 1e9}}
+    staged = {}
+    for chunks in (1, 4, 16):
+        st = harness.StagedInjector(hw, dw_hbm.k_arena, dw_hbm.v_arena, chunks=chunks)
+        ms = wall(st.step)
+        staged[str(len(st.pieces))] = {"ms": ms, "added_ms": ms - hbm_kernel_ms,
+                                       "pcie_gbps": pcie_bytes / (ms * 1e-3) / 1e9}
+        del st
+    out["staged_by_chunks"] = staged
+    best_chunks = min(staged, key=lambda c: staged[c]["ms"])
+    out["staged_best"] = dict(staged[best_chunks], chunks=int(best_chunks))
+    out["faster"] = "zero_copy" if zc_ms <= staged[best_chunks]["ms"] else "staged"
+    out["what"] = ("store in pinned host DRAM: zero-copy = inject_topk reading host memory; "
+                   "staged = store_stage_facts into HBM in chunks on a second stream + "
+                   "inject_topk per chunk; ms per step by wall clock")
+    del hw
     return out
 
 
@@ -867,6 +926,9 @@ def other_workloads(args, torch, lib, names):
             dw.setup_device_batch()
         if name == "llama3_8b_k50":
             row["k_sweep"] = k_sweep_rows(args, torch, lib, w, dw, flusher)
+        if name in ("llama3_8b_k5", "llama3_8b_k50") and not args.no_host_store:
+            row["host_store"] = host_store_figures(torch, lib, w, dw, min(args.steps, 20),
+                                                   2, kernel_ms)
         if spec.n_requests == 1 and spec.head_dim in (64, 128) and not args.no_retrieve \
                 and not args.no_attend:
             row["serving_step"] = single_user_step(args, torch, lib, w, dw, time_fn)
@@ -885,6 +947,9 @@ def other_workloads_child(args, names):
     cmd = [sys.executable, "-u", os.path.abspath(__file__), "--other-workloads-only",
            ",".join(names), "--steps", str(args.steps), "--warmup", str(args.warmup),
            "--cache-layout", args.cache_layout]
+    for flag in ("no_ceiling", "no_slot_check", "no_host_store", "no_retrieve", "no_attend"):
+        if getattr(args, flag):
+            cmd.append("--" + flag.replace("_", "-"))
     res = subprocess.run(cmd, capture_output=True, text=True, timeout=900)
     if res.returncode != 0:
         raise RuntimeError(f"other-workload timing failed (exit {res.returncode}):\n"
@@ -1211,6 +1276,10 @@ def run(args, workers):
         }
         del out, qt
 
+    host_store = None
+    if not args.no_host_store and args.store == "device" and not dw.hnd:
+        host_store = host_store_figures(torch, lib, w, dw, min(args.steps, 5), 1, kernel_ms)
+
     cpu = cpu_pool = None
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(w, args.cpu_seconds)
@@ -1273,6 +1342,7 @@ def run(args, workers):
         "cpu_baseline_all_cores": cpu_pool,
         "permuted_order": perm,
         "slot_check": slot_check,
+        "host_store": host_store,
         "graph_replay": graph,
         "retrieval": retrieval,
         "attention": attn,

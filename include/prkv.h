@@ -166,6 +166,27 @@ int store_create(const prkv_store_desc* desc, void* k_arena, void* v_arena,
 int store_put_fact(prkv_store* st, int32_t fact_id, int32_t len, const void* k_src,
                    const void* v_src, void* stream);
 
+/* Copy facts from one store into another: K and V rows of every listed
+ * fact, all layers, with one hipMemcpy2DAsync per fact and tensor on
+ * `stream`.  For a store kept in host DRAM ("If this is right" bullet 4 of
+ * the InferScale review: the store can live in host memory at a cost of
+ * milliseconds; Figure 1: only the retrieved facts' KV cross PCIe) this
+ * stages the retrieved facts into an HBM store before injecting from it, as
+ * an alternative to the kernel reading host memory directly; staging a
+ * batch in chunks on a second stream overlaps the copies with the injection
+ * of earlier chunks.
+ * src, dst: device-backed stores with equal num_layers, num_kv_heads,
+ * head_dim and key_layout (arenas may be device or pinned host memory).
+ * fact_ids: host int32[n_facts].  A fact already in dst (same length) has
+ * its rows overwritten in place; an absent one is appended (once, if listed
+ * twice).  Errors, all before anything is enqueued: INVALID_ARG (shapes,
+ * lengths), UNKNOWN_FACT (not in src), CAPACITY (dst rows or fact ids),
+ * NO_DEVICE, NO_MEMORY; HIP if a copy cannot be enqueued (copies enqueued
+ * before it stay enqueued, and dst records none of this call's appends).
+ * Asynchronous: src and dst must stay valid until the stream passes. */
+int store_stage_facts(const prkv_store* src, prkv_store* dst, int32_t n_facts,
+                      const int32_t* fact_ids, void* stream);
+
 /* Row range of a fact: *first_row and *len (UNKNOWN_FACT if never put). */
 int store_fact_info(const prkv_store* st, int32_t fact_id, int64_t* first_row,
                     int32_t* len);

@@ -1024,6 +1024,85 @@ int store_put_fact(prkv_store* st, int32_t fact_id, int32_t len, const void* k_s
   return PRKV_OK;
 }
 
+int store_stage_facts(const prkv_store* src, prkv_store* dst, int32_t n_facts,
+                      const int32_t* fact_ids, void* stream) {
+  prkv::clear_error();
+  if (!src || !dst) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (!src->device_backed() || !dst->device_backed())
+    return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store");
+  const prkv_store_desc& a = src->desc;
+  const prkv_store_desc& b = dst->desc;
+  if (a.num_layers != b.num_layers || a.num_kv_heads != b.num_kv_heads ||
+      a.head_dim != b.head_dim || a.key_layout != b.key_layout)
+    return prkv::fail(PRKV_ERR_INVALID_ARG,
+                      "stores differ in layers, KV heads, head_dim or key layout");
+  if (n_facts < 0 || (n_facts > 0 && !fact_ids))
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "bad fact list");
+  // Validate everything before enqueueing: each fact is in the source; in
+  // the destination it is either present with the same length (its rows are
+  // refreshed) or absent (appended; a fact listed twice is appended once).
+  std::vector<int64_t> rows;
+  std::vector<std::pair<int32_t, int64_t>> appended;   // (fact, row), in order
+  try {
+    rows.resize(size_t(n_facts));
+  } catch (const std::bad_alloc&) {
+    return prkv::fail(PRKV_ERR_NO_MEMORY, "staging plan");
+  }
+  int64_t next = dst->rows_used;
+  for (int32_t i = 0; i < n_facts; ++i) {
+    const int32_t f = fact_ids[i];
+    if (f < 0 || f >= a.max_facts || src->first_row[f] < 0)
+      return prkv::fail(PRKV_ERR_UNKNOWN_FACT, "fact %d not in the source store", f);
+    if (f >= b.max_facts)
+      return prkv::fail(PRKV_ERR_CAPACITY, "fact id %d outside the destination's [0, %d)", f,
+                        b.max_facts);
+    const int32_t len = src->length[f];
+    if (dst->first_row[f] >= 0) {
+      if (dst->length[f] != len)
+        return prkv::fail(PRKV_ERR_INVALID_ARG, "fact %d has length %d in the destination, %d "
+                          "in the source", f, dst->length[f], len);
+      rows[i] = dst->first_row[f];
+      continue;
+    }
+    int64_t row = -1;
+    for (const auto& pa : appended)
+      if (pa.first == f) row = pa.second;
+    if (row < 0) {
+      if (next + len > b.capacity_rows)
+        return prkv::fail(PRKV_ERR_CAPACITY, "fact %d: %d rows exceed the destination's "
+                          "capacity", f, len);
+      row = next;
+      next += len;
+      try {
+        appended.emplace_back(f, row);
+      } catch (const std::bad_alloc&) {
+        return prkv::fail(PRKV_ERR_NO_MEMORY, "staging plan");
+      }
+    }
+    rows[i] = row;
+  }
+  const size_t row_bytes = size_t(prkv::row_elems(a)) * 2u;
+  const size_t spitch = size_t(a.capacity_rows) * row_bytes;
+  const size_t dpitch = size_t(b.capacity_rows) * row_bytes;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  for (int32_t i = 0; i < n_facts; ++i) {
+    const int32_t f = fact_ids[i];
+    const size_t width = size_t(src->length[f]) * row_bytes;
+    const size_t soff = size_t(src->first_row[f]) * row_bytes;
+    const size_t doff = size_t(rows[i]) * row_bytes;
+    hipError_t e = hipMemcpy2DAsync(static_cast<char*>(dst->k_arena) + doff, dpitch,
+                                    static_cast<const char*>(src->k_arena) + soff, spitch, width,
+                                    size_t(a.num_layers), hipMemcpyDefault, s);
+    if (e == hipSuccess)
+      e = hipMemcpy2DAsync(static_cast<char*>(dst->v_arena) + doff, dpitch,
+                           static_cast<const char*>(src->v_arena) + soff, spitch, width,
+                           size_t(a.num_layers), hipMemcpyDefault, s);
+    if (e != hipSuccess) return hip_fail(e, "fact staging copy");
+  }
+  for (const auto& pa : appended) prkv::commit_put(dst, pa.first, src->length[pa.first]);
+  return PRKV_OK;
+}
+
 int inject_topk(const prkv_store* st, int64_t n_tokens, const int32_t* d_src_row,
                 const int32_t* d_pos, const int32_t* d_slot, void* const* k_cache_layers,
                 void* const* v_cache_layers, int32_t block_size, int64_t num_blocks,

@@ -38,7 +38,7 @@ class DeviceWorkload:
     """A workload resident on one GPU: store, cache, mapping."""
 
     def __init__(self, w: workloads.Workload, device="cuda", gen_device=None, stream=None,
-                 host_mapping=True, store_location="device"):
+                 host_mapping=True, store_location="device", cache_from=None):
         self.w = w
         sp = w.spec
         self.device = torch.device(device)
@@ -71,8 +71,14 @@ class DeviceWorkload:
             cshape = (sp.num_layers, w.num_blocks, sp.num_kv_heads, sp.block_size, sp.head_dim)
         else:          # [L][block][bs][H][D]
             cshape = (sp.num_layers, w.num_blocks, sp.block_size, sp.num_kv_heads, sp.head_dim)
-        self.k_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
-        self.v_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
+        if cache_from is not None:
+            # the paged cache of another workload of the same shape (e.g. the
+            # same batch with its store in HBM and in host DRAM)
+            assert tuple(cache_from.k_cache.shape) == cshape
+            self.k_cache, self.v_cache = cache_from.k_cache, cache_from.v_cache
+        else:
+            self.k_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
+            self.v_cache = torch.empty(cshape, dtype=torch.int16, device=self.device)
         self.reset_cache()
         self.status = torch.zeros(1, dtype=torch.int32, device=self.device)
         self.n_tokens = w.n_tokens
@@ -266,3 +272,70 @@ class DeviceWorkload:
             for s in range(0, flat.numel(), chunk_elems):
                 total += int((flat[s:s + chunk_elems] != workloads.SENTINEL_BF16).sum().item())
         return total
+
+
+class StagedInjector:
+    """Injection from a host-DRAM store through an HBM staging store: the
+    batch's facts are copied host -> HBM (store_stage_facts) in chunks on a
+    copy stream, and each chunk's tokens are injected on the workload's
+    stream as soon as its facts have landed, so the copies of later chunks
+    overlap the injection of earlier ones.  The staging store has the host
+    store's descriptor and row layout (rows reserved in the same put order),
+    so the host-built mapping serves both.
+
+    host_dw: a DeviceWorkload with store_location="host" and a host mapping.
+    k_arena, v_arena: HBM tensors with the host arenas' shape (they may be
+    another workload's arenas for the same facts: the staged rows are the
+    same rows with the same contents).
+    chunks: how many pieces the batch's fact list is cut into (at fact
+    boundaries, about equal token counts); 1 stages everything, then injects.
+    """
+
+    def __init__(self, host_dw, k_arena, v_arena, chunks=8, copy_stream=None):
+        assert host_dw.store_location == "host" and k_arena.is_cuda
+        assert tuple(k_arena.shape) == tuple(host_dw.k_arena.shape)
+        w = host_dw.w
+        self.dw = host_dw
+        self.k_arena, self.v_arena = k_arena, v_arena
+        self.store = prkv.store_create(host_dw.desc, k_arena, v_arena, host_dw.rope,
+                                       stream=host_dw.stream)
+        for f in w.put_order:      # the host store's rows, reserved (no data)
+            prkv.store_put_fact(self.store, f, w.length_of(f))
+        self.copy = copy_stream or torch.cuda.Stream(device=host_dw.device)
+        # chunks of the flattened fact list with about equal token counts
+        flat = [f for ids in w.retrieved for f in ids]
+        lens = np.array([w.length_of(f) for f in flat], np.int64)
+        ends = np.cumsum(lens)
+        total = int(ends[-1]) if len(ends) else 0
+        chunks = max(1, min(int(chunks), len(flat)))
+        cuts = [0] + [int(np.searchsorted(ends, total * c / chunks, side="left")) + 1
+                      for c in range(1, chunks)] + [len(flat)]
+        cuts = sorted(set(min(max(c, 0), len(flat)) for c in cuts))
+        self.pieces = []
+        for a, b in zip(cuts[:-1], cuts[1:]):
+            if b <= a:
+                continue
+            t0 = int(ends[a - 1]) if a > 0 else 0
+            t1 = int(ends[b - 1])
+            facts = list(dict.fromkeys(flat[a:b]))
+            self.pieces.append((facts, t0, t1))
+        assert sum(t1 - t0 for _, t0, t1 in self.pieces) == host_dw.n_tokens
+        self.done = None   # event: the previous step's injections have read the staging rows
+
+    def step(self):
+        """Stage and inject the whole batch once (asynchronous)."""
+        dw, w = self.dw, self.dw.w
+        comp = dw.stream
+        if self.done is not None:
+            self.copy.wait_event(self.done)
+        src, pos, slot = dw.d_map
+        kl, vl = dw.k_layers(), dw.v_layers()
+        for facts, t0, t1 in self.pieces:
+            prkv.store_stage_facts(dw.store, self.store, facts, stream=self.copy)
+            ev = torch.cuda.Event()
+            ev.record(self.copy)
+            comp.wait_event(ev)
+            prkv.inject_topk(self.store, t1 - t0, src[t0:t1], pos[t0:t1], slot[t0:t1], kl, vl,
+                             w.spec.block_size, w.num_blocks, d_status=dw.status, stream=comp)
+        self.done = torch.cuda.Event()
+        self.done.record(comp)

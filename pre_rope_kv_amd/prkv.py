@@ -26,7 +26,8 @@ ERRORS = {
 CODES = {v: k for k, v in ERRORS.items()}
 
 # Names the header declares; the library must export every one of them.
-EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_fact_info",
+EXPORTS = ["store_required_bytes", "store_create", "store_put_fact", "store_stage_facts",
+           "store_fact_info",
            "store_destroy", "build_slot_mapping", "inject_topk", "rope_table_fill",
            "last_error_string", "store_upload_fact_table", "inject_device_workspace_bytes",
            "inject_topk_device", "inject_topk_device_noalloc", "retrieve_workspace_bytes",
@@ -118,6 +119,7 @@ def lib():
         "store_create": (ctypes.c_int, [ctypes.POINTER(StoreDesc), _vp, _vp, _vp, _vp,
                                         ctypes.POINTER(_vp)]),
         "store_put_fact": (ctypes.c_int, [_vp, ctypes.c_int32, ctypes.c_int32, _vp, _vp, _vp]),
+        "store_stage_facts": (ctypes.c_int, [_vp, _vp, ctypes.c_int32, _vp, _vp]),
         "store_fact_info": (ctypes.c_int, [_vp, ctypes.c_int32, _i64p, _i32p]),
         "store_destroy": (None, [_vp]),
         "build_slot_mapping": (ctypes.c_int, [_vp, ctypes.c_int32, _vp, _vp, _vp, _vp,
@@ -252,6 +254,15 @@ def store_put_fact(st, fact_id, length, k_src=None, v_src=None, stream=None):
     s = _stream(stream) if k_src is not None else None
     _check(lib().store_put_fact(st.handle, int(fact_id), int(length), _ptr(k_src), _ptr(v_src),
                                 s), "store_put_fact")
+
+
+def store_stage_facts(src, dst, fact_ids, stream=None):
+    """Copy the listed facts' K/V rows from store `src` into store `dst`
+    (refreshing facts dst already holds, appending the others)."""
+    ids = np.ascontiguousarray(np.asarray(fact_ids, dtype=np.int32))
+    _check(lib().store_stage_facts(src.handle, dst.handle, int(ids.size),
+                                   ids.ctypes.data if ids.size else None, _stream(stream)),
+           "store_stage_facts")
 
 
 def store_fact_info(st, fact_id):

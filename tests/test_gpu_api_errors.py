@@ -134,3 +134,39 @@ def test_attend_paged_rejects_head_dim_16():
     ab = prkv.attn_batch(1, 1, 4, d.d_bt.shape[1], q, qs, d.d_bt, d.d_bt_len, out)
     assert _code(prkv.attend_paged, d.store, ab, list(d.k_layers()), list(d.v_layers()), 16,
                  w.num_blocks, 0.25, stream=d.stream) == "INVALID_ARG"
+
+
+def test_store_stage_facts_errors(dw):
+    """Staging between stores: every bad argument is rejected before
+    anything is copied (the destination's arenas keep their fill)."""
+    w = dw.w
+    sp = w.spec
+    # room for 20 rows: fact 0 (9 rows) fits, facts 0 and 1 (9 + 14) do not
+    dst_desc = prkv.desc(sp.num_layers, sp.num_kv_heads, sp.head_dim, w.max_facts, 20,
+                         sp.max_position, sp.rope_theta)
+    k = torch.full((sp.num_layers, 20, sp.num_kv_heads, sp.head_dim), 7, dtype=torch.int16,
+                   device="cuda")
+    v = torch.full_like(k, 7)
+    rope = torch.empty(prkv.store_required_bytes(dst_desc)[1] // 4, dtype=torch.float32,
+                       device="cuda")
+    dst = prkv.store_create(dst_desc, k, v, rope)
+    assert _code(prkv.store_stage_facts, dw.store, dst, [5]) == "UNKNOWN_FACT"
+    assert _code(prkv.store_stage_facts, dw.store, dst, [-1]) == "UNKNOWN_FACT"
+    assert _code(prkv.store_stage_facts, dw.store, dst, [0, 1]) == "CAPACITY"
+    prkv.store_put_fact(dst, 1, 3)                 # fact 1 reserved with another length
+    assert _code(prkv.store_stage_facts, dw.store, dst, [1]) == "INVALID_ARG"
+    other = prkv.desc(sp.num_layers, sp.num_kv_heads, 64, w.max_facts, 20, sp.max_position,
+                      sp.rope_theta)
+    k2 = torch.zeros((sp.num_layers, 20, sp.num_kv_heads, 64), dtype=torch.int16, device="cuda")
+    rope2 = torch.empty(prkv.store_required_bytes(other)[1] // 4, dtype=torch.float32,
+                        device="cuda")
+    dst2 = prkv.store_create(other, k2, k2.clone(), rope2)
+    assert _code(prkv.store_stage_facts, dw.store, dst2, [0]) == "INVALID_ARG"    # head_dim
+    meta = prkv.store_create(dst_desc, None, None, None)
+    assert _code(prkv.store_stage_facts, dw.store, meta, [0]) == "NO_DEVICE"
+    torch.cuda.synchronize()
+    assert bool((k == 7).all()) and bool((v == 7).all())
+    prkv.store_stage_facts(dw.store, dst, [0])      # a valid call for contrast
+    torch.cuda.synchronize()
+    assert not bool((k == 7).all())
+    _untouched(dw)

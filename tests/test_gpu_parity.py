@@ -310,7 +310,7 @@ def _compare_chunks(pool, got, want, chunk):
     return max(p[0] for p in parts), sum(p[1] for p in parts), sum(p[2] for p in parts)
 
 
-def _full_size(name, paths=("device", "host"), chunk=4096, **variant):
+def _full_size(name, paths=("device", "host"), chunk=4096, store_location="device", **variant):
     """A full-size workload, every element checked: for each path, V of every
     injected token bit-equal to the generator's, K of every injected token and
     layer within the bar of the oracle's value (computed from the generator's
@@ -321,11 +321,13 @@ def _full_size(name, paths=("device", "host"), chunk=4096, **variant):
     spec = workloads.dataclasses.replace(workloads.SPECS[name], **variant)
     # reserve: arenas + table + slack; the cache takes the rest (up to the spec)
     w0 = workloads.make(spec)
-    reserve = 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes + (1 << 30)
+    arenas = 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes
+    reserve = (arenas if store_location == "device" else 0) + (1 << 30)
     nb = harness.fit_num_blocks(spec, reserve)
     w = w0 if nb == spec.num_blocks else workloads.make(spec, num_blocks=nb)
-    _say(f"{name}: num_blocks {nb} (spec {spec.num_blocks}), tokens {w.n_tokens}")
-    dw = harness.DeviceWorkload(w)
+    _say(f"{name}: num_blocks {nb} (spec {spec.num_blocks}), tokens {w.n_tokens}, "
+         f"store in {store_location} memory")
+    dw = harness.DeviceWorkload(w, store_location=store_location)
     src, _, slot = (np.asarray(a) for a in
                     paged.token_mapping(w.requests(), w.fact_rows, spec.block_size))
     pos = np.asarray(paged.rotation_positions(w.requests(), w.fact_rows, is_chunk_local(spec)))
@@ -503,7 +505,7 @@ def test_permuted_fact_order_moves_positions():
 
 
 @pytest.mark.parametrize("path", ["host", "device"])
-@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k5"])
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k5", "llama3_8b_k50"])
 def test_host_dram_store(name, path):
     """Arenas in pinned host memory: the kernel reads the retrieved rows over
     PCIe; the result must be the same as from an HBM-resident store."""
@@ -542,3 +544,39 @@ def test_map_and_copy_alternating_batches():
     gk, gv = dw.listed_blocks_host(blocks)
     img_k, img_v, _ = oracle_images(last, "cuda")
     compare(img_k, img_v, gk, gv, written_mask(last, blocks))
+
+
+@pytest.mark.timeout(900)
+def test_host_dram_store_full_size():
+    """The 64-request batch with its store (16.8 GB of K/V) in pinned host
+    memory, read by the inject kernel over PCIe: every element checked, both
+    mapping paths."""
+    _full_size("llama3_8b_batch64_k50", store_location="host")
+
+
+@pytest.mark.parametrize("chunks", [1, 4])
+def test_staged_injection_equals_zero_copy(chunks):
+    """The host-DRAM store injected two ways into the same cache: the kernel
+    reading host memory (zero-copy), and the facts staged into an HBM store
+    in chunks on a second stream, each chunk injected once it has landed.
+    The two caches are identical bit for bit and meet the oracle."""
+    w = workloads.make("llama3_8b_k50")
+    dw = harness.DeviceWorkload(w, store_location="host")
+    blocks = w.listed_blocks()
+    dw.inject()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    zk, zv = dw.listed_blocks_host(blocks)
+    k_hbm = torch.empty_like(dw.k_arena, device="cuda")
+    v_hbm = torch.empty_like(dw.v_arena, device="cuda")
+    st = harness.StagedInjector(dw, k_hbm, v_hbm, chunks=chunks)
+    assert len(st.pieces) == chunks
+    for _ in range(2):                 # twice: the second call refreshes the staged rows
+        dw.reset_cache()
+        st.step()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    sk, sv = dw.listed_blocks_host(blocks)
+    assert np.array_equal(sk, zk) and np.array_equal(sv, zv)
+    img_k, img_v, _ = oracle_images(w, "cuda")
+    compare(img_k, img_v, sk, sv, written_mask(w, blocks))

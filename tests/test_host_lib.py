@@ -481,3 +481,14 @@ def test_build_slot_mapping_concurrent_calls_on_one_store():
             assert results[i][0] == "ok", results[i]
             for g, e in zip(results[i][1], want):
                 assert np.array_equal(g, e), i
+
+
+def test_stage_facts_needs_device_backed_stores():
+    """store_stage_facts between metadata-only stores: NO_DEVICE, no HIP call."""
+    a = prkv.store_create(_desc(), None, None, None)
+    b = prkv.store_create(_desc(), None, None, None)
+    prkv.store_put_fact(a, 0, 5)
+    with pytest.raises(prkv.PrkvError) as err:
+        prkv.store_stage_facts(a, b, [0], stream=0)    # the null stream: no torch device needed
+    assert err.value.name == "NO_DEVICE"
+    assert prkv.lib().store_stage_facts(None, b.handle, 0, None, None) == prkv.CODES["INVALID_ARG"]
