@@ -70,6 +70,9 @@ def parse():
                          "launch and time launches one by one (for workloads far below 1 GiB)")
     ap.add_argument("--no-ceiling", action="store_true",
                     help="skip the hand-written streaming-copy reference of the same bytes")
+    ap.add_argument("--placement-probe", action="store_true",
+                    help="instead of the bench: the workload's inject kernel and a plain copy "
+                         "between the same addresses on successive allocations of its buffers")
     ap.add_argument("--no-host-store", action="store_true",
                     help="skip the host-DRAM store figures (zero-copy and staged)")
     ap.add_argument("--no-slot-check", action="store_true",
@@ -940,6 +943,66 @@ def other_workloads(args, torch, lib, names):
     return rows
 
 
+def placement_probe(args):
+    """--placement-probe: one workload's inject kernel and a plain copy
+    between the same addresses (gather_scatter_ceiling), each timed on four
+    successive allocations of its store and cache in one process: the first,
+    the same freed and allocated again, one made after the 64-request batch
+    (256 GiB of cache) was allocated, injected and freed, and that one freed
+    and allocated again.  Prints one JSON line.  Shows whether a change of
+    rate follows the kernel or the buffers."""
+    import gc
+
+    import torch
+
+    from pre_rope_kv_amd import harness, prkv, workloads
+
+    lib = prkv.lib()
+    torch.cuda.set_device(0)
+    spec = workloads.SPECS[args.workload]
+    phases = []
+
+    def measure(tag):
+        w = workloads.make(spec)
+        dw = harness.DeviceWorkload(w)
+        kargs = dw.inject_args()
+
+        def kernel():
+            rc = lib.inject_topk(*kargs)
+            if rc != 0:
+                raise prkv.PrkvError(rc, "inject_topk", lib.last_error_string().decode())
+
+        ms, _ = time_launches(torch, kernel, dw.stream, args.steps, args.warmup)
+        ceil = gather_scatter_ceiling(torch, dw, args.steps, args.warmup)
+        nb = dw.n_tokens * spec.bytes_per_token
+        phases.append({"phase": tag, "kernel_ms": ms, "kernel_gbps": nb / (ms * 1e-3) / 1e9,
+                       "copy_mapped_gbps": ceil["mapped"]["gbps"],
+                       "copy_contiguous_gbps": ceil["contiguous"]["gbps"],
+                       "kernel_over_copy": nb / (ms * 1e-3) / 1e9 / ceil["mapped"]["gbps"],
+                       "k_cache_va": hex(dw.k_cache.data_ptr()),
+                       "v_cache_va": hex(dw.v_cache.data_ptr())})
+        print(json.dumps(phases[-1]), file=sys.stderr, flush=True)
+        del dw
+        gc.collect()
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+
+    measure("allocation 1")
+    measure("allocation 2: freed and allocated again")
+    big = harness.DeviceWorkload(workloads.make("llama3_8b_batch64_k50"))
+    big.inject()
+    torch.cuda.synchronize()
+    del big
+    gc.collect()
+    torch.cuda.synchronize()
+    torch.cuda.empty_cache()
+    measure("allocation 3: after the 64-request batch was allocated, injected and freed")
+    measure("allocation 4: freed and allocated again")
+    print(json.dumps({"what": "placement probe: inject kernel vs a plain copy between the same "
+                              "addresses on successive allocations", "workload": spec.name,
+                      "steps": args.steps, "phases": phases}), flush=True)
+
+
 def other_workloads_child(args, names):
     """other_workloads() in a child process of its own (started, not exec'd),
     so that its allocations see the device as a fresh process would."""
@@ -992,6 +1055,9 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.k_sweep and args.gpus == 1 and world == 1:
         k_sweep(args)
+        return
+    if args.placement_probe and args.gpus == 1 and world == 1:
+        placement_probe(args)
         return
     if args.gpus != 1 or world != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}, "

@@ -19,7 +19,11 @@ __device__ __forceinline__ unsigned pack_bf16(float a, float b) {
   return __builtin_bit_cast(unsigned, __builtin_convertvector(v, bf16x2));
 }
 
-// x1 * c - x2 * s with c = ch + cl, s = sh + sl.
+// x1 * c - x2 * s with c = ch + cl, s = sh + sl.  p and q (the products
+// with the hi parts) are exact with their FMA error terms e and f; p - q is
+// rounded once (exact when they nearly cancel), the small terms are summed,
+// and the total is rounded once more: within about one float32 ulp of the
+// exact value.
 __device__ __forceinline__ float rot_first(float x1, float x2, f32x4 cs) {
   const float p = x1 * cs.x;
   const float e = __builtin_fmaf(x1, cs.x, -p);

@@ -41,10 +41,16 @@
 //    is staged in LDS, laid out so lanes with consecutive c read consecutive
 //    16-byte words.
 //  - Rotation: x1' = x1 c - x2 s, x2' = x2 c + x1 s with c = c_hi + c_lo and
-//    s = s_hi + s_lo (float32 hi/lo of the float64 value); each product with
-//    the hi part is made exact with an FMA error term, so the only rounding
-//    before the final bf16 rounding is one float32 rounding of the result
-//    (plus terms ~2^-48 |x|).  Rounding to bf16 is nearest-even
+//    s = s_hi + s_lo (float32 hi/lo of the float64 value).  The two products
+//    with the hi parts are exact as p + e and q + f (FMA error terms); their
+//    difference a = p - q is rounded once to float32, which is exact when
+//    the products nearly cancel (Sterbenz) -- the case that needs the
+//    compensation -- and otherwise costs at most half an ulp of a; the error
+//    terms and the lo products are summed in float32 and added to a with one
+//    more rounding.  So before the bf16 rounding the value is within about
+//    one float32 ulp of the exact rotation, and the bf16 result is the
+//    correctly rounded one except near a bf16 rounding boundary, where it
+//    can be the neighbour (1 bf16 ulp).  Rounding to bf16 is nearest-even
 //    (v_cvt_pk_bf16_f32).
 //  - 16-byte nontemporal loads and stores; 64-bit addressing (one layer of
 //    a large cache exceeds 4 GiB).  The cache is NHD ([block][bs][H][D]: a
