@@ -274,6 +274,30 @@ class DeviceWorkload:
         return total
 
 
+def chunk_facts(facts, lengths, chunks):
+    """Cut a batch's flattened fact list (request order, then rank order)
+    into at most `chunks` consecutive pieces of about equal token counts.
+    Returns [(distinct facts of the piece in order, first token, end token)];
+    the token ranges are those of the batch's slot mapping, which lists the
+    tokens in the same order."""
+    lens = np.asarray(lengths, np.int64)
+    if len(lens) == 0:
+        return []
+    ends = np.cumsum(lens)
+    total = int(ends[-1])
+    chunks = max(1, min(int(chunks), len(lens)))
+    cuts = [0] + [int(np.searchsorted(ends, total * c / chunks, side="left")) + 1
+                  for c in range(1, chunks)] + [len(lens)]
+    cuts = sorted(set(min(max(c, 0), len(lens)) for c in cuts))
+    pieces = []
+    for a, b in zip(cuts[:-1], cuts[1:]):
+        if b <= a:
+            continue
+        t0 = int(ends[a - 1]) if a > 0 else 0
+        pieces.append((list(dict.fromkeys(facts[a:b])), t0, int(ends[b - 1])))
+    return pieces
+
+
 class StagedInjector:
     """Injection from a host-DRAM store through an HBM staging store: the
     batch's facts are copied host -> HBM (store_stage_facts) in chunks on a
@@ -302,23 +326,8 @@ class StagedInjector:
         for f in w.put_order:      # the host store's rows, reserved (no data)
             prkv.store_put_fact(self.store, f, w.length_of(f))
         self.copy = copy_stream or torch.cuda.Stream(device=host_dw.device)
-        # chunks of the flattened fact list with about equal token counts
         flat = [f for ids in w.retrieved for f in ids]
-        lens = np.array([w.length_of(f) for f in flat], np.int64)
-        ends = np.cumsum(lens)
-        total = int(ends[-1]) if len(ends) else 0
-        chunks = max(1, min(int(chunks), len(flat)))
-        cuts = [0] + [int(np.searchsorted(ends, total * c / chunks, side="left")) + 1
-                      for c in range(1, chunks)] + [len(flat)]
-        cuts = sorted(set(min(max(c, 0), len(flat)) for c in cuts))
-        self.pieces = []
-        for a, b in zip(cuts[:-1], cuts[1:]):
-            if b <= a:
-                continue
-            t0 = int(ends[a - 1]) if a > 0 else 0
-            t1 = int(ends[b - 1])
-            facts = list(dict.fromkeys(flat[a:b]))
-            self.pieces.append((facts, t0, t1))
+        self.pieces = chunk_facts(flat, [w.length_of(f) for f in flat], chunks)
         assert sum(t1 - t0 for _, t0, t1 in self.pieces) == host_dw.n_tokens
         self.done = None   # event: the previous step's injections have read the staging rows
 

@@ -459,3 +459,43 @@ def test_check_flag_many_duplicates():
     img_k, img_v, mask = _expect(w, blocks, dups)
     gk, gv = dw.listed_blocks_host(blocks)
     compare(img_k, img_v, gk, gv, mask)
+
+
+@pytest.mark.parametrize("seed", range(16))
+def test_random_shared_blocks_with_check(seed):
+    """Seeded random small batches in which one request's block-table entry
+    is replaced by a block of another request (so some of their slots may
+    collide, or none if their offsets do not meet), through the checked
+    device step (small and separate-kernel bounds alternate): exactly the
+    colliding tokens are skipped, status is 128 iff there is a collision,
+    and everything else meets the oracle."""
+    rng = np.random.default_rng(7000 + seed)
+    L, H, D = SHAPES[seed % len(SHAPES)]
+    n_facts = int(rng.integers(2, 12))
+    facts = {f: int(rng.integers(1, 40)) for f in range(n_facts)}
+    reqs = [([int(x) for x in rng.integers(0, n_facts, size=int(rng.integers(1, 6)))],
+             int(rng.integers(0, 60))) for _ in range(int(rng.integers(2, 5)))]
+    bs = int(rng.choice([1, 4, 16, 32]))
+    w = custom_workload(f"shared{seed}", L, H, D, bs, facts, reqs, num_blocks=4096)
+    bts = [t.copy() for t in w.block_tables]
+    r1, r2 = (int(x) for x in rng.choice(len(bts), 2, replace=False))
+    bts[r2][int(rng.integers(0, len(bts[r2])))] = bts[r1][int(rng.integers(0, len(bts[r1])))]
+    fields = {f.name: getattr(w, f.name) for f in dataclasses.fields(w)}
+    fields["block_tables"] = bts
+    w = _SharedBlocks(**fields)
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    dw.setup_device_batch(max_facts=None if seed % 2 else FUSE_LIMIT + 44,
+                          flags=prkv.BATCH_CHECK_SLOTS)
+    dw.status.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    _, _, slot = paged.token_mapping(w.requests(), w.fact_rows, bs)
+    dups = sorted(s for s, c in Counter(slot).items() if c > 1)
+    assert int(dw.status.item()) == (128 if dups else 0)
+    n, d_src, _, _ = dw.device_mapping()
+    assert n == len(slot)
+    assert all((d_src[t] == -1) == (s in set(dups)) for t, s in enumerate(slot))
+    blocks = w.listed_blocks()
+    img_k, img_v, mask = _expect(w, blocks, dups)
+    gk, gv = dw.listed_blocks_host(blocks)
+    compare(img_k, img_v, gk, gv, mask)

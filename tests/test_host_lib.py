@@ -492,3 +492,34 @@ def test_stage_facts_needs_device_backed_stores():
         prkv.store_stage_facts(a, b, [0], stream=0)    # the null stream: no torch device needed
     assert err.value.name == "NO_DEVICE"
     assert prkv.lib().store_stage_facts(None, b.handle, 0, None, None) == prkv.CODES["INVALID_ARG"]
+
+
+def test_chunk_facts_covers_the_batch_in_order():
+    """The staging injector's chunks: consecutive, covering every token once,
+    each piece's facts in order (a fact repeated inside a piece listed once),
+    at most the asked number of pieces, and close to equal token counts."""
+    from pre_rope_kv_amd import harness
+    rng = np.random.default_rng(3)
+    for trial in range(200):
+        n = int(rng.integers(1, 60))
+        facts = [int(x) for x in rng.integers(0, 40, size=n)]
+        lens = [int(x) for x in rng.integers(1, 300, size=n)]
+        chunks = int(rng.integers(1, 20))
+        pieces = harness.chunk_facts(facts, lens, chunks)
+        assert 1 <= len(pieces) <= min(chunks, n)
+        assert pieces[0][1] == 0 and pieces[-1][2] == sum(lens)
+        for (_, _, e), (_, s, _) in zip(pieces[:-1], pieces[1:]):
+            assert e == s
+        # rebuild the fact list from the token ranges
+        ends = np.cumsum(lens)
+        i = 0
+        for fs, t0, t1 in pieces:
+            j = int(np.searchsorted(ends, t1, side="left")) + 1
+            assert ends[j - 1] == t1 and (i == 0 or ends[i - 1] == t0)
+            assert fs == list(dict.fromkeys(facts[i:j]))
+            i = j
+        assert i == n
+        if len(pieces) == chunks and n >= 4 * chunks:
+            biggest = max(t1 - t0 for _, t0, t1 in pieces)
+            assert biggest <= sum(lens) / chunks + max(lens)
+    assert harness.chunk_facts([], [], 4) == []

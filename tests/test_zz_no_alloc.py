@@ -5,7 +5,8 @@ Checked against inject_topk_device on the same batch (caches and status bit
 for bit) and against the oracle at the parity bar, on three calls in a row
 that share the scratch array: a batch of 400 facts, then a smaller one of
 270 (both through the plan and mapping kernels, which use the workspace),
-then a 5-fact batch (the fused single launch).  A batch whose bounds do not
+then a 5-fact batch (the fused single launch); and with the duplicate-slot
+check, whose slot set lives in the array too.  A batch whose bounds do not
 fit the array is rejected before anything is enqueued.
 """
 
@@ -75,6 +76,32 @@ def test_noalloc_equals_workspace_path_on_consecutive_calls():
     _check_against_workspace_path(_workload("noalloc_270", 270, 2), 270)
     # a small batch: the fused launch, which writes its plan and mapping there too
     _check_against_workspace_path(workloads.make("tiny_L1_H2_D64"), None)
+
+
+def test_noalloc_with_the_duplicate_slot_check():
+    """The checked step (slot set in the scratch array too) on a batch whose
+    two requests share a block: the same skipped tokens, status and cache as
+    inject_topk_device with a caller workspace."""
+    import dataclasses
+    w = _workload("noalloc_dup", 300, 4)
+    bts = [t.copy() for t in w.block_tables]
+    bts[1][1] = bts[0][1]      # request 1 injects from position 17: its block 1 collides
+    w = dataclasses.replace(w, block_tables=bts)
+    blocks = sorted(set(int(b) for t in bts for b in t))
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    dw.setup_device_batch(max_facts=300, flags=prkv.BATCH_CHECK_SLOTS)
+    dw.status.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    ref_status = int(dw.status.item())
+    ref_k, ref_v = dw.listed_blocks_host(blocks)
+    dw.reset_cache()
+    dw.status.zero_()
+    _noalloc(dw)
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == ref_status == 128
+    got_k, got_v = dw.listed_blocks_host(blocks)
+    assert np.array_equal(got_k, ref_k) and np.array_equal(got_v, ref_v)
 
 
 def test_noalloc_rejects_bounds_beyond_the_scratch():
