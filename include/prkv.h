@@ -175,8 +175,9 @@ int store_put_fact(prkv_store* st, int32_t fact_id, int32_t len, const void* k_s
  * an alternative to the kernel reading host memory directly; staging a
  * batch in chunks on a second stream overlaps the copies with the injection
  * of earlier chunks.
- * src, dst: device-backed stores with equal num_layers, num_kv_heads,
- * head_dim and key_layout (arenas may be device or pinned host memory).
+ * src, dst: two different device-backed stores with equal num_layers,
+ * num_kv_heads, head_dim and key_layout (arenas may be device or pinned
+ * host memory).
  * fact_ids: host int32[n_facts].  A fact already in dst (same length) has
  * its rows overwritten in place; an absent one is appended (once, if listed
  * twice).  Errors, all before anything is enqueued: INVALID_ARG (shapes,
@@ -345,9 +346,11 @@ int inject_topk_device(const prkv_store* st, const void* d_fact_table,
  * last call's mapping in it; nothing in it needs to start at zero.  Calls
  * that overlap on one GPU (several streams, several threads or processes'
  * streams at once) race on the array: serialize them, or use
- * inject_topk_device with separate workspaces.  The first call on a device
- * looks up the array's device address (hipGetSymbolAddress) with that
- * device current. */
+ * inject_topk_device with separate workspaces.  The array used is the one
+ * of the device that runs `stream` (the current device for the null
+ * stream); the first call on a device looks up its address
+ * (hipGetSymbolAddress) with that device current, then restores the
+ * caller's current device. */
 #define PRKV_NOALLOC_SCRATCH_BYTES (16u << 20)
 int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
                                const prkv_device_batch* batch, void* const* k_cache_layers,

@@ -1034,6 +1034,7 @@ int store_stage_facts(const prkv_store* src, prkv_store* dst, int32_t n_facts,
                       const int32_t* fact_ids, void* stream) {
   prkv::clear_error();
   if (!src || !dst) return prkv::fail(PRKV_ERR_INVALID_ARG, "store is NULL");
+  if (src == dst) return prkv::fail(PRKV_ERR_INVALID_ARG, "source and destination are one store");
   if (!src->device_backed() || !dst->device_backed())
     return prkv::fail(PRKV_ERR_NO_DEVICE, "metadata-only store");
   const prkv_store_desc& a = src->desc;
@@ -1279,24 +1280,35 @@ int inject_device_impl(const prkv_store* st, const void* d_fact_table,
                        nullptr, expect);
 }
 
-// Device address of this library's scratch array on the current device,
-// looked up once per device (each GPU holds its own copy of the array at its
-// own address; the array's name in host code is only a host-side stand-in).
+// Device address of this library's scratch array on the device that runs
+// `stream`, looked up once per device with that device current (each GPU
+// holds its own copy of the array at its own address; the array's name in
+// host code is only a host-side stand-in).
 constexpr int kMaxDevices = 64;
 std::mutex g_scratch_mu;
 void* g_scratch_ptr[kMaxDevices] = {};
 
-int scratch_address(void** out) {
-  int dev = -1;
-  hipError_t e = hipGetDevice(&dev);
+int scratch_address(hipStream_t stream, void** out) {
+  int cur = -1;
+  hipError_t e = hipGetDevice(&cur);
   if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  hipDevice_t dev = cur;
+  if (stream) {
+    e = hipStreamGetDevice(stream, &dev);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+  }
   if (dev < 0 || dev >= kMaxDevices)
-    return prkv::fail(PRKV_ERR_INVALID_ARG, "device %d beyond the %d the library tracks", dev,
-                      kMaxDevices);
+    return prkv::fail(PRKV_ERR_INVALID_ARG, "device %d beyond the %d the library tracks",
+                      int(dev), kMaxDevices);
   std::lock_guard<std::mutex> lock(g_scratch_mu);
   if (!g_scratch_ptr[dev]) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
     void* p = nullptr;
     e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t back = hipSetDevice(cur);
+      if (e == hipSuccess) e = back;
+    }
     if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
     if (!p || (reinterpret_cast<uintptr_t>(p) & 255u))
       return prkv::fail(PRKV_ERR_HIP, "scratch array has no 256-byte aligned device address");
@@ -1336,7 +1348,7 @@ int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
                       batch->max_facts, (long long)batch->max_tokens, need,
                       size_t(PRKV_NOALLOC_SCRATCH_BYTES));
   void* ws = nullptr;
-  if (int rc = scratch_address(&ws)) return rc;
+  if (int rc = scratch_address(static_cast<hipStream_t>(stream), &ws)) return rc;
   return inject_device_impl(st, d_fact_table, batch, k_cache_layers, v_cache_layers, block_size,
                             num_blocks, ws, size_t(PRKV_NOALLOC_SCRATCH_BYTES), d_status, stream);
 }

@@ -162,6 +162,7 @@ def test_store_stage_facts_errors(dw):
                         device="cuda")
     dst2 = prkv.store_create(other, k2, k2.clone(), rope2)
     assert _code(prkv.store_stage_facts, dw.store, dst2, [0]) == "INVALID_ARG"    # head_dim
+    assert _code(prkv.store_stage_facts, dw.store, dw.store, [0]) == "INVALID_ARG"  # one store
     meta = prkv.store_create(dst_desc, None, None, None)
     assert _code(prkv.store_stage_facts, dw.store, meta, [0]) == "NO_DEVICE"
     torch.cuda.synchronize()

@@ -97,7 +97,11 @@ def test_noalloc_with_the_duplicate_slot_check():
     ref_k, ref_v = dw.listed_blocks_host(blocks)
     dw.reset_cache()
     dw.status.zero_()
-    _noalloc(dw)
+    side = torch.cuda.Stream()            # a stream of its own: the scratch of its device
+    side.wait_stream(dw.stream)
+    prkv.inject_topk_device_noalloc(dw.store, dw.fact_table, dw.batch, dw.k_layers(),
+                                    dw.v_layers(), w.spec.block_size, w.num_blocks,
+                                    d_status=dw.status, stream=side)
     torch.cuda.synchronize()
     assert int(dw.status.item()) == ref_status == 128
     got_k, got_v = dw.listed_blocks_host(blocks)
