@@ -129,3 +129,43 @@ def test_serving_step_graph_replays_match_eager(name):
         assert np.array_equal(out.cpu().numpy(), want_out), rep
         _say(f"{name}: serving-step replay {rep} equal to eager")
     assert int(dw.status.item()) == 0
+
+
+def test_checked_device_inject_graph_replays_match_eager():
+    """The device step with the duplicate-slot check (a clear kernel, not a
+    memset, empties its slot set) on a batch whose two requests share a
+    block, captured once: every replay skips the same tokens, reports the
+    same status and writes the same cache as the eager step."""
+    import dataclasses
+
+    from test_gpu_device_path import _shared_block_workload
+    w = _shared_block_workload("graph_dup")
+    dw = harness.DeviceWorkload(w, host_mapping=False)
+    dw.setup_device_batch(flags=prkv.BATCH_CHECK_SLOTS)
+    blocks = w.listed_blocks()
+    dw.status.zero_()
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 128
+    want_k, want_v = dw.listed_blocks_host(blocks)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    old_stream = dw.stream
+    with torch.cuda.graph(g, stream=side):
+        dw.stream = torch.cuda.current_stream()
+        dw.inject_device()
+    dw.stream = old_stream
+    torch.cuda.synchronize()
+    for rep in range(3):
+        dw.reset_cache()                 # eager work between replays
+        dw.status.zero_()
+        torch.cuda.synchronize()
+        g.replay()
+        torch.cuda.synchronize()
+        assert int(dw.status.item()) == 128, rep
+        got_k, got_v = dw.listed_blocks_host(blocks)
+        assert np.array_equal(got_k, want_k) and np.array_equal(got_v, want_v), rep
+    assert dataclasses.is_dataclass(w)
