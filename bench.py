@@ -91,7 +91,8 @@ PROFILE_FLAGS = ("--no-cpu-baseline --no-e2e --no-other-workloads --no-ceiling "
                  "--no-slot-check --no-host-store")
 
 # kernels with committed rocprofv3 summaries: name prefix -> source file
-PROFILED = {"inject_kernel": "prkv_inject.hip", "attend_kernel": "prkv_attend.hip"}
+PROFILED = {"inject_kernel": "prkv_inject.hip", "attend_kernel": "prkv_attend.hip",
+            "score_kernel": "prkv_retrieve.hip"}
 ATTN_Q_LEN = 16        # query tokens per request in the attention section
 ATTN_GROUP = 4         # query heads per KV head
 
@@ -145,6 +146,12 @@ def algorithmic_bytes(kernel, w):
     if kernel == "inject_kernel":
         return w.n_tokens * w.spec.bytes_per_token, (
             "read K and V rows, write K and V rows: tokens x layers x 4 x H x D x 2 B")
+    if kernel == "score_kernel":
+        sp = w.spec
+        emb = sp.n_requests * sp.facts_per_store * sp.emb_dim * 2
+        return emb + sp.n_requests * sp.emb_dim * 2 + sp.n_requests * sp.facts_per_store * 8, (
+            "every fact embedding of every request's store once (bf16), the queries once, "
+            "one float64 score per fact written")
     return attention_bytes(w)[1], (
         f"K and V rows of every context position once, {ATTN_Q_LEN} bf16 query rows x "
         f"{ATTN_GROUP} heads per KV head, float32 outputs (all layers)")
@@ -1285,6 +1292,9 @@ def run(args, workers):
             "retrieve_embedding_gbps": emb_bytes / (r_ms * 1e-3) / 1e9,
             "retrieve_and_inject_ms": b_ms,
             "retrieve_and_inject_tokens_per_s": n_tok / (b_ms * 1e-3),
+            "score_kernel_bytes_per_launch": algorithmic_bytes("score_kernel", w)[0],
+            "score_kernel_traffic": (read_profile_traffic(spec.name, "score_kernel")
+                                     if profiled_config else None),
         }
         del emb, q, rws
 
