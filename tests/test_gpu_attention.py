@@ -347,16 +347,22 @@ def test_attention_query_positions_out_of_range_are_reported():
     assert np.array_equal(got[:, 2], ref[:, 2])
 
 
-@pytest.mark.parametrize("name,n_pairs,layout", [("llama3_8b_batch64_k50", 24, 0),
-                                                 ("llama3_70b_batch16_k50", 16, 0),
-                                                 ("llama3_8b_batch64_k50", 12, 1)])
-def test_attention_full_size_sampled(name, n_pairs, layout):
+@pytest.mark.timeout(900)
+@pytest.mark.parametrize("name,layers,layout", [("llama3_8b_batch64_k50", (0, 11, 22, 31), 0),
+                                                ("llama3_70b_batch16_k50", (0, 26, 53, 79), 0),
+                                                ("llama3_8b_batch64_k50", (5, 17, 29), 1)])
+def test_attention_full_size(name, layers, layout):
     """The launch the bench times: the whole batch injected by the device
     path into a zeroed cache, then one attend_paged over every request's
     whole context (16 query tokens = the context's last 16 positions, 4 query
-    heads per KV head, all layers); sampled (layer, request) outputs against
-    the oracle's attention over the same cache contents.  layout 1: the HND
+    heads per KV head, all layers); the outputs of every request at the
+    listed layers (first, last and between) against the oracle's attention
+    over the same cache contents (one layer's K and V gathered at a time,
+    (layer, request) pairs spread over host threads).  layout 1: the HND
     cache layout."""
+    from concurrent.futures import ThreadPoolExecutor
+
+    from test_gpu_parity import _oracle_threads
     spec = workloads.dataclasses.replace(workloads.SPECS[name], cache_layout=layout)
     w0 = workloads.make(spec)
     nb = harness.fit_num_blocks(spec, 2 * w0.capacity_rows * spec.num_layers * spec.row_bytes +
@@ -387,25 +393,31 @@ def test_attention_full_size_sampled(name, n_pairs, layout):
     torch.cuda.synchronize()
     assert int(dw.status.item()) == 0
     assert bool(torch.isfinite(out).all())
-    rng = np.random.default_rng(len(name))
-    pairs = {(int(rng.integers(0, L)), int(rng.integers(0, spec.n_requests)))
-             for _ in range(n_pairs)}
-    worst = 0.0
-    for l, r in sorted(pairs):
-        ctx = ctxs[r]
-        bt = w.block_tables[r]
-        slots = torch.as_tensor([int(bt[p // spec.block_size]) * spec.block_size +
-                                 p % spec.block_size for p in range(ctx)], device=dw.device)
-        kk = bf16.bf16_bits_to_f64(dw.slot_rows(dw.k_cache, slots)[l].cpu().numpy()
-                                   .view(np.uint16))
-        vv = bf16.bf16_bits_to_f64(dw.slot_rows(dw.v_cache, slots)[l].cpu().numpy()
-                                   .view(np.uint16))
-        q_pos = np.arange(ctx - q_len, ctx)
-        q_rot = rope.rotate(bf16.bf16_bits_to_f64(q_bits[r].numpy().view(np.uint16)),
-                            q_pos[:, None], spec.rope_theta, **rope_kwargs(spec))
-        want = attention.causal_gqa(q_rot, q_pos, kk, vv, np.arange(ctx), 1.0 / math.sqrt(D))
-        got = out[l, r].cpu().numpy().astype(np.float64)
-        worst = max(worst, float(np.max(np.abs(got - want))))
-    _say(f"{name}: {len(pairs)} (layer, request) pairs, max |gpu - oracle over gpu cache| "
-         f"= {worst:.3g}")
+    # every request's context positions, as cache slots, concatenated
+    bs = spec.block_size
+    starts = np.concatenate([[0], np.cumsum(ctxs)])
+    slots = np.concatenate([np.asarray(w.block_tables[r], np.int64)[np.arange(c) // bs] * bs +
+                            np.arange(c) % bs for r, c in enumerate(ctxs)])
+    d_slots = torch.as_tensor(slots, device=dw.device)
+    q_rot = [rope.rotate(bf16.bf16_bits_to_f64(q_bits[r].numpy().view(np.uint16)),
+                         np.arange(c - q_len, c)[:, None], spec.rope_theta, **rope_kwargs(spec))
+             for r, c in enumerate(ctxs)]
+    kv = {l: (dw.slot_rows_layer(dw.k_cache, l, d_slots).cpu().numpy().view(np.uint16),
+              dw.slot_rows_layer(dw.v_cache, l, d_slots).cpu().numpy().view(np.uint16),
+              out[l].cpu().numpy().astype(np.float64)) for l in layers}
+
+    def one(pair):
+        l, r = pair
+        kl, vl, got = kv[l]
+        a, b, c = starts[r], starts[r + 1], ctxs[r]
+        want = attention.causal_gqa(q_rot[r], np.arange(c - q_len, c),
+                                    bf16.bf16_bits_to_f64(kl[a:b]), bf16.bf16_bits_to_f64(vl[a:b]),
+                                    np.arange(c), 1.0 / math.sqrt(D))
+        return float(np.max(np.abs(got[r] - want)))
+
+    pairs = [(l, r) for l in layers for r in range(spec.n_requests)]
+    with ThreadPoolExecutor(_oracle_threads()) as pool:
+        worst = max(pool.map(one, pairs))
+    _say(f"{name}: {len(pairs)} (layer, request) outputs (every request at layers {layers}), "
+         f"max |gpu - oracle over gpu cache| = {worst:.3g}")
     assert worst <= TOL_SAME_CACHE
