@@ -334,7 +334,7 @@ class Flusher:
         self.i = 0
 
     def __call__(self, torch, stream):
-        self.i += 1
+        self.i = (self.i + 1) % 32000      # a new value each time, within int16
         with torch.cuda.stream(stream):
             self.buf.fill_(self.i)
 
@@ -345,8 +345,11 @@ def queue_ahead(torch, stream, ms=2.0):
     waiting when the GPU reaches them: events around them then time the GPU,
     not the host's launch rate (which bounds back-to-back launches of a few
     microseconds)."""
+    spin = getattr(torch.cuda, "_sleep", None)
+    if spin is None:        # no spin kernel in this torch build: launches are timed as enqueued
+        return
     with torch.cuda.stream(stream):
-        torch.cuda._sleep(int(ms * 1e-3 * 2.0e9))   # cycles at ~2 GHz (bounded spin)
+        spin(int(ms * 1e-3 * 2.0e9))   # cycles at ~2 GHz (bounded spin)
 
 
 def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False):
