@@ -21,12 +21,16 @@
 //
 // topk_kernel: 1024-lane workgroups, one per request, or up to 16 per
 // request when few requests have many facts (each takes a slice of the
-// scores).  Each wave streams 64-score chunks, sorts a chunk with an
-// in-register bitonic network and merges it into its running top-64
-// (elementwise best of the list and the reversed chunk, then a bitonic
+// scores).  Each wave loads two 64-score chunks at a time, sorts each with an
+// in-register bitonic network and merges them into its running top-64 (the
+// lane-wise better of a best-first and a worst-first list, then a bitonic
 // merge); the 16 wave lists are merged in LDS as a tree (4 rounds).  With
 // several slices, topk_merge_kernel merges their top-64 lists the same way
-// (k <= 64, so the request's best k are among them).
+// (k <= 64, so the request's best k are among them).  The partner exchanges
+// of the networks stay in the VALU (DPP row permutations for lane xor 1, 2,
+// 4, 8; the permlane swaps for xor 16 and 32) and every compare-exchange is
+// branch-free, so the kernel is bound by the VALU work of its 16 waves on
+// one CU rather than by LDS round trips.
 // Order: higher score first, then smaller fact id, so ties are deterministic.
 
 #include <hip/hip_runtime.h>
@@ -140,49 +144,101 @@ __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.key > b.key || (a.key == b.key && a.id < b.id);
 }
 
-__device__ __forceinline__ Cand shfl_xor_cand(const Cand& c, int m) {
+// The value lane (lane ^ M) holds, for M a power of two below 64, without a
+// trip through LDS: xor 1 and 2 are DPP quad permutations, xor 4 is the
+// quad reversal (xor 3) followed by the half-row mirror (xor 7), xor 8 is
+// the row rotation by 8; xor 16 and xor 32 use the permlane swaps, which
+// exchange the odd 16-lane rows (upper 32 lanes) of their first operand with
+// the even rows (lower 32 lanes) of their second, so with both operands x a
+// lane finds its partner's value in the first result if its own bit is set,
+// else in the second.  Every lane of the wave must be active.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const int y = __builtin_amdgcn_mov_dpp(int(x), 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
+    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
+
+template <int M>
+__device__ __forceinline__ Cand xor_cand(const Cand& c, int lane) {
   Cand o;
-  const uint32_t lo = __shfl_xor(uint32_t(c.key), m, kWave);
-  const uint32_t hi = __shfl_xor(uint32_t(c.key >> 32), m, kWave);
+  const uint32_t lo = xor_lane<M>(uint32_t(c.key), lane);
+  const uint32_t hi = xor_lane<M>(uint32_t(c.key >> 32), lane);
   o.key = (uint64_t(hi) << 32) | lo;
-  o.id = __shfl_xor(c.id, m, kWave);
+  o.id = int32_t(xor_lane<M>(uint32_t(c.id), lane));
   return o;
 }
 
-// Bitonic compare-exchange step so that, within blocks of size `blk`, lanes
-// end up ordered best-first (blocks alternate direction below 64).
-__device__ __forceinline__ Cand cx(const Cand& v, int lane, int stride, int blk) {
-  const Cand o = shfl_xor_cand(v, stride);
-  const bool lower = (lane & stride) == 0;
-  const bool best_first = (lane & blk) == 0;
-  const bool take_better = lower == best_first;
-  const bool ob = better(o, v);
-  return (take_better ? ob : !ob) ? o : v;
+// Bitonic compare-exchange with the partner lane ^ ST: within blocks of BLK
+// lanes the lower lane keeps the better candidate when the block runs
+// best-first.  Blocks alternate direction by the BLK bit of the lane (BLK =
+// 128: one block, the whole wave); DESC flips every direction, so a network
+// built from these steps sorts worst-first instead.
+template <int ST, int BLK, bool DESC>
+__device__ __forceinline__ Cand cx(const Cand& v, int lane) {
+  const Cand o = xor_cand<ST>(v, lane);
+  // the lane keeps the worse of the pair where it is the upper lane of a
+  // best-first block or the lower lane of a worst-first one
+  const bool flip = ((lane & ST) == 0) != (((lane & BLK) == 0) != DESC);
+  const bool ob = (o.key > v.key) | ((o.key == v.key) & (o.id < v.id));
+  const bool take = ob != flip;
+  Cand r;
+  r.key = take ? o.key : v.key;
+  r.id = take ? o.id : v.id;
+  return r;
 }
 
+// Bitonic merge of a bitonic sequence over the wave: strides 32, 16, ..., 1.
+template <int BLK, bool DESC>
+__device__ __forceinline__ Cand bitonic_merge(Cand v, int lane) {
+  v = cx<32, BLK, DESC>(v, lane);
+  v = cx<16, BLK, DESC>(v, lane);
+  v = cx<8, BLK, DESC>(v, lane);
+  v = cx<4, BLK, DESC>(v, lane);
+  v = cx<2, BLK, DESC>(v, lane);
+  return cx<1, BLK, DESC>(v, lane);
+}
+
+// The wave's 64 candidates sorted best-first (DESC: worst-first): bitonic
+// sort, blocks of 2, 4, ..., 64 lanes.
+template <bool DESC>
 __device__ __forceinline__ Cand sort64(Cand v, int lane) {
-#pragma unroll
-  for (int blk = 2; blk <= kWave; blk <<= 1)
-#pragma unroll
-    for (int st = blk >> 1; st > 0; st >>= 1) v = cx(v, lane, st, blk == kWave ? 2 * kWave : blk);
-  return v;
+  v = cx<1, 2, DESC>(v, lane);
+  v = cx<2, 4, DESC>(v, lane);
+  v = cx<1, 4, DESC>(v, lane);
+  v = cx<4, 8, DESC>(v, lane);
+  v = cx<2, 8, DESC>(v, lane);
+  v = cx<1, 8, DESC>(v, lane);
+  v = cx<8, 16, DESC>(v, lane);
+  v = cx<4, 16, DESC>(v, lane);
+  v = cx<2, 16, DESC>(v, lane);
+  v = cx<1, 16, DESC>(v, lane);
+  v = cx<16, 32, DESC>(v, lane);
+  v = cx<8, 32, DESC>(v, lane);
+  v = cx<4, 32, DESC>(v, lane);
+  v = cx<2, 32, DESC>(v, lane);
+  v = cx<1, 32, DESC>(v, lane);
+  return bitonic_merge<128, DESC>(v, lane);
 }
 
-// a, b sorted best-first: returns the 64 best of both, sorted best-first.
-__device__ __forceinline__ Cand merge64(Cand a, Cand b, int lane) {
-  // b reversed: lane i takes b[63 - i]
-  Cand br;
-  {
-    const int src = kWave - 1 - lane;
-    const uint32_t lo = __shfl(uint32_t(b.key), src, kWave);
-    const uint32_t hi = __shfl(uint32_t(b.key >> 32), src, kWave);
-    br.key = (uint64_t(hi) << 32) | lo;
-    br.id = __shfl(b.id, src, kWave);
-  }
-  Cand v = better(br, a) ? br : a;  // bitonic sequence holding the 64 best
-#pragma unroll
-  for (int st = kWave / 2; st > 0; st >>= 1) v = cx(v, lane, st, 2 * kWave);
-  return v;
+// a sorted best-first, b worst-first: the 64 best of both, best-first.  The
+// lane-wise better of the two is a bitonic sequence that holds them.
+__device__ __forceinline__ Cand merge64(const Cand& a, const Cand& b, int lane) {
+  return bitonic_merge<128, false>(better(b, a) ? b : a, lane);
 }
 
 struct TopkParams {
@@ -221,10 +277,11 @@ struct RetrieveWs {
   }
 };
 
-// The waves' sorted lists (one Cand per lane) merged in LDS as a tree; wave 0
-// returns the best 64 of the workgroup, best first.  In each round wave
-// w < half merges in the list of wave w + half (it writes only its own slots,
-// which no wave reads in that round).
+// The waves' sorted lists (one Cand per lane, best first) merged in LDS as a
+// tree; wave 0 returns the best 64 of the workgroup, best first (the other
+// waves return their last list).  In each round wave w < half merges in the
+// list of wave w + half, read back to front so that it runs worst-first; it
+// writes only its own slots, which no wave reads in that round.
 __device__ Cand block_merge(Cand best, uint64_t* s_key, int32_t* s_id) {
   const int lane = threadIdx.x % kWave, wave = threadIdx.x / kWave;
   constexpr int nw = kTopkThreads / kWave;
@@ -233,15 +290,14 @@ __device__ Cand block_merge(Cand best, uint64_t* s_key, int32_t* s_id) {
   __syncthreads();
   for (int half = nw / 2; half >= 1; half /= 2) {
     if (wave < half) {
-      const Cand mine = {s_key[threadIdx.x], s_id[threadIdx.x]};
-      const Cand other = {s_key[(wave + half) * kWave + lane], s_id[(wave + half) * kWave + lane]};
-      const Cand m = merge64(mine, other, lane);
-      s_key[threadIdx.x] = m.key;
-      s_id[threadIdx.x] = m.id;
+      const int o = (wave + half) * kWave + (kWave - 1 - lane);
+      best = merge64(best, Cand{s_key[o], s_id[o]}, lane);
+      s_key[threadIdx.x] = best.key;
+      s_id[threadIdx.x] = best.id;
     }
     __syncthreads();
   }
-  return Cand{s_key[lane], s_id[lane]};
+  return best;
 }
 
 // Lane i < k of wave 0 writes the request's i-th best fact (global id) and
@@ -268,18 +324,31 @@ __global__ __launch_bounds__(kTopkThreads) void topk_kernel(TopkParams p) {
   const bool ok = s >= 0 && s < p.n_stores;
   const double* sc = p.scores + int64_t(r) * p.facts_per_store;
   const Cand worst = {0, INT32_MAX};
-  Cand best = worst;
-  const int F = ok ? p.facts_per_store : 0;
+  // The score row's address depends only on r, so its loads issue together
+  // with that of req_store; a request whose store is out of range takes no
+  // candidate (its row in the workspace exists but was not written).
+  const int F = p.facts_per_store;
   const int lo = int(int64_t(F) * part / p.parts), hi = int(int64_t(F) * (part + 1) / p.parts);
-  for (int c0 = lo + wave * kWave; c0 < hi; c0 += nw * kWave) {
-    const int f = c0 + lane;
-    Cand v = worst;
-    if (f < hi) {
-      v.key = order_key(sc[f]);
-      v.id = f;
+  // Two 64-score chunks per round, both loaded before either is sorted.  In
+  // the first round the chunks are sorted in opposite directions and merged
+  // into the running list directly; later rounds sort both worst-first and
+  // merge each into it.
+  const int64_t step = nw * kWave;
+  Cand best = worst;
+  for (int64_t c0 = lo + wave * kWave; c0 < hi; c0 += 2 * step) {
+    const int64_t f = c0 + lane, g = c0 + step + lane;
+    Cand a = worst, b = worst;
+    if (f < hi) a = Cand{order_key(sc[f]), int32_t(f)};
+    if (g < hi) b = Cand{order_key(sc[g]), int32_t(g)};
+    if (!ok) a = b = worst;
+    const bool two = c0 + step < hi;
+    if (c0 == lo + wave * kWave) {
+      best = two ? merge64(sort64<false>(a, lane), sort64<true>(b, lane), lane)
+                 : sort64<false>(a, lane);
+    } else {
+      best = merge64(best, sort64<true>(a, lane), lane);
+      if (two) best = merge64(best, sort64<true>(b, lane), lane);
     }
-    v = sort64(v, lane);
-    best = merge64(best, v, lane);
   }
   const Cand acc = block_merge(best, s_key, s_id);
   if (p.parts == 1) {

@@ -85,7 +85,11 @@ def test_retrieve_matches_oracle(name):
                                      # widths that are not multiples of 512: a partial
                                      # last chunk (384, 768, 1000, 8) or a single one
                                      (2000, 50, 384), (1500, 20, 768), (300, 64, 1000),
-                                     (100, 10, 8), (257, 5, 4088)])
+                                     (100, 10, 8), (257, 5, 4088),
+                                     # more than 2,048 scores per top-k workgroup (16
+                                     # slices of 2,500 / 4,375): the waves run 3-5
+                                     # chunk rounds before the lists are merged
+                                     (40000, 50, 512), (70000, 64, 256)])
 def test_retrieve_shapes(F, k, dim):
     g = torch.Generator(device="cuda")
     g.manual_seed(F * 131 + k * 7 + dim)
