@@ -69,7 +69,8 @@ def parse():
                     help="evict the 256 MB Infinity Cache with a 1 GiB fill before every timed "
                          "launch and time launches one by one (for workloads far below 1 GiB)")
     ap.add_argument("--no-ceiling", action="store_true",
-                    help="skip the hand-written streaming-copy reference of the same bytes")
+                    help="skip the hand-written streaming-copy (inject) and streaming-read "
+                         "(retrieval) references of the same bytes")
     ap.add_argument("--placement-probe", action="store_true",
                     help="instead of the bench: the workload's inject kernel and a plain copy "
                          "between the same addresses on successive allocations of its buffers")
@@ -307,7 +308,7 @@ _CEILING = None
 
 def ceiling_lib():
     """libprkv_ceiling.so (built by pre_rope_kv_amd.build): the plain copy the
-    inject kernel is measured against."""
+    inject kernel is measured against, and the plain read the retrieval is."""
     global _CEILING
     if _CEILING is None:
         path = os.path.join(ROOT, "pre_rope_kv_amd", "libprkv_ceiling.so")
@@ -321,6 +322,8 @@ def ceiling_lib():
         lib.ceiling_gather_scatter.restype = ctypes.c_int
         lib.ceiling_empty.argtypes = [ctypes.c_int32, vp]
         lib.ceiling_empty.restype = ctypes.c_int
+        lib.ceiling_read.argtypes = [vp, i64, vp, i32, i32, vp]
+        lib.ceiling_read.restype = ctypes.c_int
         _CEILING = lib
     return _CEILING
 
@@ -1287,12 +1290,33 @@ def run(args, workers):
         _, _, b_ms = timed(step_both)
         assert int(dw.status.item()) == 0, "retrieve + inject reported skipped tokens"
         emb_bytes = spec.n_requests * spec.facts_per_store * spec.emb_dim * 2
+        read_ceiling = None
+        if not args.no_ceiling:
+            # the same embedding bytes read once by a plain streaming kernel (16-byte
+            # nontemporal loads, slices per workgroup), fastest of 16 launch shapes
+            clib = ceiling_lib()
+            sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+            for per_lane in (1, 2, 4, 8):
+                for grid in (1024, 2048, 4096, 8192):
+                    def step_read(pl=per_lane, g=grid):
+                        rc = clib.ceiling_read(emb.data_ptr(), emb_bytes, sink.data_ptr(), pl, g,
+                                               stream.cuda_stream)
+                        if rc != 0:
+                            raise RuntimeError(f"ceiling_read failed ({rc})")
+                    _, _, c_ms = timed(step_read)
+                    if read_ceiling is None or c_ms < read_ceiling["ms"]:
+                        read_ceiling = {"ms": c_ms, "gbps": emb_bytes / (c_ms * 1e-3) / 1e9,
+                                        "per_lane": per_lane, "grid": grid}
+            del sink
         retrieval = {
             "what": "retrieve_topk: exact inner-product top-k over each request's store "
                     f"({spec.facts_per_store} facts x {spec.emb_dim} bf16), then "
                     "inject_topk_device on the retrieved ids",
             "retrieve_ms": r_ms,
             "retrieve_embedding_gbps": emb_bytes / (r_ms * 1e-3) / 1e9,
+            "read_ceiling": read_ceiling,
+            "retrieve_pct_of_read_ceiling": (100.0 * read_ceiling["ms"] / r_ms
+                                             if read_ceiling else None),
             "retrieve_and_inject_ms": b_ms,
             "retrieve_and_inject_tokens_per_s": n_tok / (b_ms * 1e-3),
             "score_kernel_bytes_per_launch": algorithmic_bytes("score_kernel", w)[0],

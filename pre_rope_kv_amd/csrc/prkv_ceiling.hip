@@ -27,6 +27,15 @@
 //     arguments, -10 for a launch error.
 //   ceiling_empty(grid, stream)
 //     an empty kernel of `grid` 256-lane workgroups (the launch floor).
+//   ceiling_read(src, bytes, sink, per_lane, grid, stream)
+//     a streaming read of `bytes` (a multiple of 16, 16-byte aligned): each
+//     of `grid` 256-lane workgroups reads one contiguous slice with 16-byte
+//     nontemporal loads, `per_lane` (1, 2, 4 or 8) in flight per lane, and
+//     folds them with xor; a lane stores its fold to sink[lane] only if it
+//     equals a value no fold of real data reaches here (so the loads are
+//     kept and nothing is written).  sink holds 256 uint32.  The read-only
+//     counterpart of the gather-scatter copy, for the retrieval score
+//     kernel (which reads the fact embeddings once).
 
 #include <hip/hip_runtime.h>
 
@@ -77,6 +86,25 @@ __global__ __launch_bounds__(THREADS) void gather_scatter_kernel(
 }
 
 __global__ __launch_bounds__(256) void empty_kernel() {}
+
+template <int PER_LANE>
+__global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src, int64_t n_vec,
+                                                   uint32_t* __restrict__ sink) {
+  // workgroup b reads vectors [lo, hi) of the buffer, PER_LANE x 256 at a time
+  const int64_t lo = n_vec * blockIdx.x / gridDim.x, hi = n_vec * (blockIdx.x + 1) / gridDim.x;
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  int64_t i = lo + threadIdx.x;
+  for (; i + (PER_LANE - 1) * 256 < hi; i += PER_LANE * 256) {
+    u32x4 x[PER_LANE];
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) x[j] = __builtin_nontemporal_load(src + i + j * 256);
+#pragma unroll
+    for (int j = 0; j < PER_LANE; ++j) acc ^= x[j];
+  }
+  for (; i < hi; i += 256) acc ^= __builtin_nontemporal_load(src + i);
+  const uint32_t f = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (f == 0x9e3779b9u && acc.x == 0x7f4a7c15u && acc.y == 0xf39cc060u) sink[threadIdx.x] = f;
+}
 
 template <int THREADS, int ORDER>
 int launch(const void* ks, const void* vs, int64_t src_layer_vecs, void* kd, void* vd,
@@ -139,6 +167,25 @@ int ceiling_gather_scatter(const void* k_src, const void* v_src, int64_t src_lay
       : launch_threads<1>(threads, k_src, v_src, slv, k_dst, v_dst, dlv, src_row, dst_row,
                           n_tokens, num_layers, per_lane, s);
   if (rc) return rc;
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+int ceiling_read(const void* src, int64_t bytes, uint32_t* sink, int32_t per_lane, int32_t grid,
+                 void* stream) {
+  if (!src || !sink || bytes < 0 || bytes % 16 || grid <= 0 ||
+      (reinterpret_cast<uintptr_t>(src) & 15u))
+    return -1;
+  if (bytes == 0) return 0;
+  const int64_t n = bytes / 16;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* p = static_cast<const u32x4*>(src);
+  switch (per_lane) {
+    case 1: hipLaunchKernelGGL(read_kernel<1>, dim3(unsigned(grid)), dim3(256), 0, s, p, n, sink); break;
+    case 2: hipLaunchKernelGGL(read_kernel<2>, dim3(unsigned(grid)), dim3(256), 0, s, p, n, sink); break;
+    case 4: hipLaunchKernelGGL(read_kernel<4>, dim3(unsigned(grid)), dim3(256), 0, s, p, n, sink); break;
+    case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(unsigned(grid)), dim3(256), 0, s, p, n, sink); break;
+    default: return -1;
+  }
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
