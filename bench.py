@@ -397,9 +397,10 @@ def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
     workgroups; with a flusher the best shape is also timed cold.  It
     overwrites cache rows, so the cache is reset and the batch re-injected
     afterwards.  None when the layout has no such copy (HND cache, host
-    store, rows other than 1, 2 or 4 KiB)."""
+    store, rows other than 256 B - 4 KiB in powers of two)."""
     sp, w = dw.w.spec, dw.w
-    if dw.hnd or dw.store_location != "device" or sp.row_bytes not in (1024, 2048, 4096):
+    if dw.hnd or dw.store_location != "device" or \
+            sp.row_bytes not in (256, 512, 1024, 2048, 4096):
         return None
     lib = ceiling_lib()
     stream = dw.stream

@@ -22,9 +22,12 @@
 //   ceiling_gather_scatter(k_src, v_src, src_layer_bytes, k_dst, v_dst,
 //                          dst_layer_bytes, src_row, dst_row, n_tokens,
 //                          num_layers, row_bytes, order, threads, stream)
-//     row_bytes: 1024, 2048 or 4096; order: 0 token-major, 1 layer-major;
-//     threads: 64, 256 or 1024 per workgroup.  Returns 0, -1 for bad
-//     arguments, -10 for a launch error.
+//     row_bytes: 256, 512, 1024, 2048 or 4096; order: 0 token-major, 1
+//     layer-major; threads: 64, 256 or 1024 per workgroup.  Rows narrower
+//     than a wave's 1 KiB (256 and 512 bytes: one KV head, or two) are
+//     copied 4 or 2 tokens of one layer per wave, as the inject kernel does
+//     for such rows.  Returns 0, -1 for bad arguments, -10 for a launch
+//     error.
 //   ceiling_empty(grid, stream)
 //     an empty kernel of `grid` 256-lane workgroups (the launch floor).
 //   ceiling_read(src, bytes, sink, per_lane, grid, stream)
@@ -85,6 +88,39 @@ __global__ __launch_bounds__(THREADS) void gather_scatter_kernel(
   }
 }
 
+// Rows of ROW_VECS < 64 vectors: a wave copies 64 / ROW_VECS consecutive
+// tokens of one layer; w indexes (token group, layer) in the given order.
+template <int THREADS, int ORDER, int ROW_VECS>
+__global__ __launch_bounds__(THREADS) void gather_scatter_narrow_kernel(
+    const u32x4* __restrict__ ks, const u32x4* __restrict__ vs, int64_t src_layer_vecs,
+    u32x4* __restrict__ kd, u32x4* __restrict__ vd, int64_t dst_layer_vecs,
+    const int32_t* __restrict__ src_row, const int32_t* __restrict__ dst_row, int64_t n,
+    int num_layers) {
+  constexpr int kTpw = kWave / ROW_VECS;
+  const int lane = threadIdx.x % kWave;
+  const int64_t w = (int64_t(blockIdx.x) * THREADS + threadIdx.x) / kWave;
+  const int64_t groups = (n + kTpw - 1) / kTpw;
+  if (w >= groups * num_layers) return;
+  int64_t g;
+  int64_t l;
+  if (ORDER == 0) {
+    g = w / num_layers;
+    l = w % num_layers;
+  } else {
+    l = w / groups;
+    g = w % groups;
+  }
+  const int64_t t = g * kTpw + lane / ROW_VECS;
+  if (t >= n) return;
+  const int v = lane % ROW_VECS;
+  const int64_t s = (src_row ? int64_t(src_row[t]) : t) * ROW_VECS + v;
+  const int64_t d = (dst_row ? int64_t(dst_row[t]) : t) * ROW_VECS + v;
+  const u32x4 x = __builtin_nontemporal_load(ks + l * src_layer_vecs + s);
+  const u32x4 y = __builtin_nontemporal_load(vs + l * src_layer_vecs + s);
+  __builtin_nontemporal_store(x, kd + l * dst_layer_vecs + d);
+  __builtin_nontemporal_store(y, vd + l * dst_layer_vecs + d);
+}
+
 __global__ __launch_bounds__(256) void empty_kernel() {}
 
 template <int PER_LANE>
@@ -110,13 +146,29 @@ template <int THREADS, int ORDER>
 int launch(const void* ks, const void* vs, int64_t src_layer_vecs, void* kd, void* vd,
            int64_t dst_layer_vecs, const int32_t* sr, const int32_t* dr, int64_t n, int L,
            int per_lane, hipStream_t s) {
-  const int64_t grid = (n * L * kWave + THREADS - 1) / THREADS;
-  if (grid > INT32_MAX) return -1;
-  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(THREADS), 1, 1};
   const u32x4* k_in = static_cast<const u32x4*>(ks);
   const u32x4* v_in = static_cast<const u32x4*>(vs);
   u32x4* k_out = static_cast<u32x4*>(kd);
   u32x4* v_out = static_cast<u32x4*>(vd);
+  if (per_lane < 0) {  // rows of -per_lane vectors, narrower than a wave
+    const int tpw = kWave / -per_lane;
+    const int64_t grid = ((n + tpw - 1) / tpw * L * kWave + THREADS - 1) / THREADS;
+    if (grid > INT32_MAX) return -1;
+    const dim3 g{unsigned(grid), 1, 1}, b{unsigned(THREADS), 1, 1};
+    switch (-per_lane) {
+      case 16: hipLaunchKernelGGL((gather_scatter_narrow_kernel<THREADS, ORDER, 16>), g, b, 0, s,
+                                  k_in, v_in, src_layer_vecs, k_out, v_out, dst_layer_vecs, sr,
+                                  dr, n, L); break;
+      case 32: hipLaunchKernelGGL((gather_scatter_narrow_kernel<THREADS, ORDER, 32>), g, b, 0, s,
+                                  k_in, v_in, src_layer_vecs, k_out, v_out, dst_layer_vecs, sr,
+                                  dr, n, L); break;
+      default: return -1;
+    }
+    return 0;
+  }
+  const int64_t grid = (n * L * kWave + THREADS - 1) / THREADS;
+  if (grid > INT32_MAX) return -1;
+  const dim3 g{unsigned(grid), 1, 1}, b{unsigned(THREADS), 1, 1};
   switch (per_lane) {
     case 1: hipLaunchKernelGGL((gather_scatter_kernel<THREADS, ORDER, 1>), g, b, 0, s, k_in, v_in,
                                src_layer_vecs, k_out, v_out, dst_layer_vecs, sr, dr, n, L); break;
@@ -151,14 +203,17 @@ int ceiling_gather_scatter(const void* k_src, const void* v_src, int64_t src_lay
                            int32_t num_layers, int32_t row_bytes, int32_t order,
                            int32_t threads, void* stream) {
   if (!k_src || !v_src || !k_dst || !v_dst || n_tokens < 0 || num_layers < 1 ||
-      (row_bytes != 1024 && row_bytes != 2048 && row_bytes != 4096) || (order != 0 && order != 1))
+      (row_bytes != 256 && row_bytes != 512 && row_bytes != 1024 && row_bytes != 2048 &&
+       row_bytes != 4096) ||
+      (order != 0 && order != 1))
     return -1;
   if (((reinterpret_cast<uintptr_t>(k_src) | reinterpret_cast<uintptr_t>(v_src) |
         reinterpret_cast<uintptr_t>(k_dst) | reinterpret_cast<uintptr_t>(v_dst)) & 15u) ||
       (src_layer_bytes % 16) || (dst_layer_bytes % 16))
     return -1;
   if (n_tokens == 0) return 0;
-  const int per_lane = row_bytes / 1024;
+  // vectors of 16 B per lane, or (negative) the row's vectors when under a wave
+  const int per_lane = row_bytes >= 1024 ? row_bytes / 1024 : -(row_bytes / 16);
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int64_t slv = src_layer_bytes / 16, dlv = dst_layer_bytes / 16;
   const int rc = order == 0
