@@ -387,6 +387,24 @@ def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False):
     return sum(per) / len(per), per[len(per) // 2]
 
 
+def time_span(torch, fn, stream, steps, warmup):
+    """Mean ms per launch of fn() on `stream` over `steps` back-to-back
+    launches between two events, enqueued behind a clock spin: for launches of
+    tens of microseconds, where an event after every launch would add its own
+    time to each."""
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    queue_ahead(torch, stream)
+    e0.record(stream)
+    for _ in range(steps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / steps
+
+
 def gather_scatter_ceiling(torch, dw, steps, warmup, flusher=None):
     """Read + write GB/s of a plain copy that moves exactly the bytes of the
     workload's inject launch (libprkv_ceiling.so): every token's K and V row
@@ -1287,7 +1305,7 @@ def run(args, workers):
             step_retrieve()
             step_device()
 
-        _, _, r_ms = timed(step_retrieve)
+        r_ms = time_span(torch, step_retrieve, stream, args.steps, args.warmup)
         _, _, b_ms = timed(step_both)
         assert int(dw.status.item()) == 0, "retrieve + inject reported skipped tokens"
         emb_bytes = spec.n_requests * spec.facts_per_store * spec.emb_dim * 2
@@ -1304,7 +1322,7 @@ def run(args, workers):
                                                stream.cuda_stream)
                         if rc != 0:
                             raise RuntimeError(f"ceiling_read failed ({rc})")
-                    _, _, c_ms = timed(step_read)
+                    c_ms = time_span(torch, step_read, stream, args.steps, args.warmup)
                     if read_ceiling is None or c_ms < read_ceiling["ms"]:
                         read_ceiling = {"ms": c_ms, "gbps": emb_bytes / (c_ms * 1e-3) / 1e9,
                                         "per_lane": per_lane, "grid": grid}
