@@ -355,26 +355,36 @@ def queue_ahead(torch, stream, ms=2.0):
         spin(int(ms * 1e-3 * 2.0e9))   # cycles at ~2 GHz (bounded spin)
 
 
-def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False):
-    """Mean and median ms per launch of fn() on `stream`: back to back (warm),
-    or, with a flusher, one at a time each after a MALL-evicting fill (cold).
-    queued: warm launches are enqueued behind a clock spin (queue_ahead), so
-    the figures are GPU time even for launches shorter than the host's
-    launch cost."""
+def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False, reps=3):
+    """Mean and median ms per launch of fn() on `stream`.  Warm: `steps`
+    back-to-back launches split into `reps` runs, each enqueued behind a
+    clock spin (queue_ahead) and timed by two events around the run, so the
+    figures are GPU time even for launches shorter than the host's launch
+    cost, and no event sits between launches (an event after every launch
+    adds 3-5 us to each); mean = all runs' time / all launches, median = the
+    median of the runs' means.  Cold (a flusher): one launch at a time, each
+    after a MALL-evicting fill, timed by an event pair around it (which adds
+    that event cost).  `queued` is kept for callers: warm runs are always
+    queued."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
     if flusher is None:
-        evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
-        if queued:
+        per_run = max(1, steps // reps)
+        means, total = [], 0.0
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
             queue_ahead(torch, stream)
-        evs[0].record(stream)
-        for i in range(steps):
-            fn()
-            evs[i + 1].record(stream)
-        torch.cuda.synchronize()
-        per = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
-        return evs[0].elapsed_time(evs[steps]) / steps, per[len(per) // 2]
+            e0.record(stream)
+            for _ in range(per_run):
+                fn()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1)
+            total += ms
+            means.append(ms / per_run)
+        means.sort()
+        return total / (per_run * reps), means[len(means) // 2]
     pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
              for _ in range(steps)]
     for a, b in pairs:
@@ -532,6 +542,17 @@ def launch_floor(torch, stream, steps=200):
         ms, med = time_launches(torch, lambda g=grid: lib.ceiling_empty(g, stream.cuda_stream),
                                 stream, steps, 10, queued=True)
         out[f"grid_{grid}_ms"] = ms
+    # the same launches with an event recorded after each one: what an event
+    # pair around a single launch adds (the cold timings pay it)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    queue_ahead(torch, stream)
+    evs[0].record(stream)
+    for i in range(steps):
+        lib.ceiling_empty(1, stream.cuda_stream)
+        evs[i + 1].record(stream)
+    torch.cuda.synchronize()
+    out["grid_1_event_per_launch_ms"] = evs[0].elapsed_time(evs[steps]) / steps
     return out
 
 
@@ -925,8 +946,8 @@ def other_workloads(args, torch, lib, names):
             "tokens": dw.n_tokens, "layers": spec.num_layers, "kv_heads": spec.num_kv_heads,
             "requests": spec.n_requests, "k": spec.k, "block_size": spec.block_size,
             "num_blocks": w.num_blocks, "bytes_per_launch": alg,
-            "warm": {"timing": "back to back" + (", enqueued behind a clock spin so the events "
-                                                  "time the GPU, not the host" if cold else ""),
+            "warm": {"timing": "back to back in 3 runs, each enqueued behind a clock spin and "
+                               "timed by two events around it (none between launches)",
                      "step_ms": step_ms, "step_median_ms": step_med,
                      "tokens_per_s": dw.n_tokens / (step_ms * 1e-3),
                      "kernel_ms": kernel_ms, "kernel_median_ms": kernel_med,
@@ -940,7 +961,10 @@ def other_workloads(args, torch, lib, names):
             c_kern, c_kern_med = time_launches(torch, kernel, stream, args.steps, args.warmup,
                                                flusher)
             assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
-            row["cold"] = {"step_ms": c_step, "step_median_ms": c_step_med,
+            row["cold"] = {"timing": "one launch at a time after a 1 GiB fill that evicts the "
+                                     "MALL, an event pair around each (which adds its own few "
+                                     "microseconds: launch_floor.grid_1_event_per_launch_ms)",
+                           "step_ms": c_step, "step_median_ms": c_step_med,
                            "tokens_per_s": dw.n_tokens / (c_step * 1e-3),
                            "kernel_ms": c_kern, "kernel_median_ms": c_kern_med,
                            "hbm_gbps": alg / (c_kern * 1e-3) / 1e9,
