@@ -362,10 +362,12 @@ def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False, 
     figures are GPU time even for launches shorter than the host's launch
     cost, and no event sits between launches (an event after every launch
     adds 3-5 us to each); mean = all runs' time / all launches, median = the
-    median of the runs' means.  Cold (a flusher): one launch at a time, each
-    after a MALL-evicting fill, timed by an event pair around it (which adds
-    that event cost).  `queued` is kept for callers: warm runs are always
-    queued."""
+    median of the runs' means.  Cold (a flusher): every launch follows a
+    MALL-evicting fill; `reps` runs of `steps` (fill, launch) pairs and as
+    many runs of the fills alone, each between two events behind a clock
+    spin; a launch's cold time = (pairs - fills) / steps (the fills' jitter
+    averages out over the run), mean over the runs and their median.
+    `queued` is kept for callers: runs are always queued."""
     for _ in range(warmup):
         fn()
     torch.cuda.synchronize()
@@ -385,16 +387,23 @@ def time_launches(torch, fn, stream, steps, warmup, flusher=None, queued=False, 
             means.append(ms / per_run)
         means.sort()
         return total / (per_run * reps), means[len(means) // 2]
-    pairs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
-             for _ in range(steps)]
-    for a, b in pairs:
-        flusher(torch, stream)
-        a.record(stream)
-        fn()
-        b.record(stream)
-    torch.cuda.synchronize()
-    per = sorted(a.elapsed_time(b) for a, b in pairs)
-    return sum(per) / len(per), per[len(per) // 2]
+    def run(with_launch):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        queue_ahead(torch, stream)
+        e0.record(stream)
+        for _ in range(steps):
+            flusher(torch, stream)
+            if with_launch:
+                fn()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        return e0.elapsed_time(e1)
+
+    diffs = []
+    for _ in range(reps):
+        diffs.append((run(True) - run(False)) / steps)
+    diffs.sort()
+    return sum(diffs) / len(diffs), diffs[len(diffs) // 2]
 
 
 def time_span(torch, fn, stream, steps, warmup):
@@ -961,9 +970,9 @@ def other_workloads(args, torch, lib, names):
             c_kern, c_kern_med = time_launches(torch, kernel, stream, args.steps, args.warmup,
                                                flusher)
             assert int(dw.status.item()) == 0, f"{name}: skipped tokens"
-            row["cold"] = {"timing": "one launch at a time after a 1 GiB fill that evicts the "
-                                     "MALL, an event pair around each (which adds its own few "
-                                     "microseconds: launch_floor.grid_1_event_per_launch_ms)",
+            row["cold"] = {"timing": "every launch after a 1 GiB fill that evicts the MALL: "
+                                     "runs of (fill, launch) minus runs of fills alone, each "
+                                     "between two events",
                            "step_ms": c_step, "step_median_ms": c_step_med,
                            "tokens_per_s": dw.n_tokens / (c_step * 1e-3),
                            "kernel_ms": c_kern, "kernel_median_ms": c_kern_med,
