@@ -520,9 +520,31 @@ def host_store_figures(torch, lib, w, dw_hbm, steps, warmup, hbm_kernel_ms):
             raise prkv.PrkvError(rc, "inject_topk", lib.last_error_string().decode())
 
     zc_ms = wall(zero_copy)
+    # The link's attainable rate: the copy engine moving a contiguous run of
+    # the same pinned arena into HBM (the batch's byte count, at most 1 GiB per
+    # copy: the rate does not depend on size beyond that).
+    n_copy = min(pcie_bytes, 1 << 30) // 2
+    src = hw.k_arena.view(-1)[:n_copy]
+    h2d_gbps = None
+    try:
+        dst = torch.empty(n_copy, dtype=torch.int16, device="cuda")
+    except torch.cuda.OutOfMemoryError:
+        dst = None      # no room beside the workload: reported as null
+    if dst is not None:
+        n_h2d = max(3, min(30, int(8e9 // (2 * n_copy))))     # about 8 GB in all
+        dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for _ in range(n_h2d):
+            dst.copy_(src, non_blocking=True)
+        torch.cuda.synchronize()
+        h2d_gbps = n_h2d * 2 * n_copy / (time.perf_counter() - t0) / 1e9
+        del dst
+    zc_gbps = pcie_bytes / (zc_ms * 1e-3) / 1e9
     out = {"setup_s": setup_s, "pcie_read_bytes": pcie_bytes,
-           "zero_copy": {"ms": zc_ms, "added_ms": zc_ms - hbm_kernel_ms,
-                         "pcie_gbps": pcie_bytes / (zc_ms * 1e-3) / 1e9}}
+           "zero_copy": {"ms": zc_ms, "added_ms": zc_ms - hbm_kernel_ms, "pcie_gbps": zc_gbps},
+           "h2d_copy_engine_gbps": h2d_gbps,
+           "zero_copy_frac_of_h2d_copy": zc_gbps / h2d_gbps if h2d_gbps else None}
     staged = {}
     for chunks in (1, 4, 16):
         st = harness.StagedInjector(hw, dw_hbm.k_arena, dw_hbm.v_arena, chunks=chunks)
@@ -552,7 +574,7 @@ def launch_floor(torch, stream, steps=200):
                                 stream, steps, 10, queued=True)
         out[f"grid_{grid}_ms"] = ms
     # the same launches with an event recorded after each one: what an event
-    # pair around a single launch adds (the cold timings pay it)
+    # between launches adds to each
     evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     queue_ahead(torch, stream)
