@@ -114,6 +114,12 @@ def inject_via(dw, path):
     dw.setup_device_batch()
     dw.inject_device()
     torch.cuda.synchronize()
+    check_device_mapping(dw)
+
+
+def check_device_mapping(dw):
+    """The mapping inject_topk_device built in its workspace equals the
+    oracle's (arena row, rotation position, slot) of every token."""
     n, src, pos, slot = dw.device_mapping()
     o_src, _, o_slot = paged.token_mapping(dw.w.requests(), dw.w.fact_rows,
                                            dw.w.spec.block_size)
@@ -310,14 +316,17 @@ def _compare_chunks(pool, got, want, chunk):
     return max(p[0] for p in parts), sum(p[1] for p in parts), sum(p[2] for p in parts)
 
 
-def _full_size(name, paths=("device", "host"), chunk=4096, store_location="device", **variant):
+def _full_size(name, paths=("device", "host"), chunk=4096, store_location="device", via=None,
+               prepare=None, **variant):
     """A full-size workload, every element checked: for each path, V of every
     injected token bit-equal to the generator's, K of every injected token and
     layer within the bar of the oracle's value (computed from the generator's
     pre-RoPE K, one layer at a time, token chunks spread over threads), and a
     count of non-sentinel elements over the whole cache (nothing written
     outside the injected slots).  The paths share one cache, reset between
-    them."""
+    them.  `prepare(w)` may return the workload with its requests' facts in
+    another order (same sets); `via(dw, path)` injects instead of inject_via
+    (it must inject the workload's facts in the workload's order)."""
     spec = workloads.dataclasses.replace(workloads.SPECS[name], **variant)
     # reserve: arenas + table + slack; the cache takes the rest (up to the spec)
     w0 = workloads.make(spec)
@@ -325,6 +334,8 @@ def _full_size(name, paths=("device", "host"), chunk=4096, store_location="devic
     reserve = (arenas if store_location == "device" else 0) + (1 << 30)
     nb = harness.fit_num_blocks(spec, reserve)
     w = w0 if nb == spec.num_blocks else workloads.make(spec, num_blocks=nb)
+    if prepare is not None:
+        w = prepare(w)
     _say(f"{name}: num_blocks {nb} (spec {spec.num_blocks}), tokens {w.n_tokens}, "
          f"store in {store_location} memory")
     dw = harness.DeviceWorkload(w, store_location=store_location)
@@ -353,10 +364,10 @@ def _full_size(name, paths=("device", "host"), chunk=4096, store_location="devic
                                                          spec.rope_theta, **kw)
         list(pool.map(rotate, [(l, a) for l in range(L) for a in range(0, T, chunk)]))
         reports = {}
-        for path in paths:
-            if path == "host":
+        for i, path in enumerate(paths):
+            if i > 0:
                 dw.reset_cache()
-            inject_via(dw, path)
+            (via or inject_via)(dw, path)
             assert int(dw.status.item()) == 0
             t0, v_bad = 0, torch.zeros((), dtype=torch.int64, device="cuda")
             for ids in w.retrieved:

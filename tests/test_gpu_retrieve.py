@@ -16,8 +16,8 @@ import torch
 from oracle import retrieve
 from pre_rope_kv_amd import harness, prkv, workloads
 
-from test_gpu_parity import (_release_device_memory, compare, oracle_images,  # noqa: F401
-                             written_mask, _say)
+from test_gpu_parity import (_full_size, _release_device_memory, check_device_mapping,  # noqa: F401
+                             compare, oracle_images, written_mask, _say)
 
 pytestmark = pytest.mark.gpu
 
@@ -135,7 +135,47 @@ def test_retrieve_bad_store_reports(F):
     assert list(ids[0]) == [0, 1, 2, 3, 4]   # all scores 0: id order
 
 
-@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k50", "llama3_8b_batch64_k50"])
+def _oracle_ids(w):
+    """The oracle's top-k of each request's store for the workload's queries
+    (global fact ids, best first)."""
+    sp = w.spec
+    embs, emb = _embeddings(w)
+    q = w.query_embeddings("cuda", emb=embs)
+    del embs
+    emb_h = emb.cpu().numpy().view(np.uint16).reshape(sp.n_requests, sp.facts_per_store, -1)
+    q_h = q.cpu().numpy().view(np.uint16)
+    del emb, q
+    return [[int(r * sp.facts_per_store + f)
+             for f in retrieve.topk(retrieve.scores(q_h[r], emb_h[r]), sp.k)]
+            for r in range(sp.n_requests)]
+
+
+def _retrieve_then_inject(dw, w_drawn):
+    """retrieve_topk over the embeddings of w_drawn (the workload as drawn:
+    its embeddings and queries depend on the rank order of its facts) writes
+    the fact ids into the device batch, inject_topk_device injects them: the
+    ids must be dw's (the oracle's top-k order, set by the caller), the
+    device mapping the oracle's."""
+    w, sp = dw.w, dw.w.spec
+    embs, emb = _embeddings(w_drawn)
+    q = w_drawn.query_embeddings("cuda", emb=embs)
+    del embs
+    dw.setup_device_batch()
+    dw.d_ids.fill_(-1)
+    ws_bytes = prkv.retrieve_workspace_bytes(sp.n_requests, sp.facts_per_store)
+    ws = torch.empty(ws_bytes, dtype=torch.uint8, device="cuda")
+    d_rs = torch.as_tensor(w.req_store(), device="cuda")
+    prkv.retrieve_topk(emb, sp.n_requests, sp.facts_per_store, sp.emb_dim, q, d_rs,
+                       sp.n_requests, sp.k, dw.d_ids, ws, ws_bytes, d_status=dw.status)
+    dw.inject_device()
+    torch.cuda.synchronize()
+    assert int(dw.status.item()) == 0
+    got = dw.d_ids.cpu().numpy().reshape(sp.n_requests, sp.k)
+    assert [list(map(int, row)) for row in got] == [list(map(int, r)) for r in w.retrieved]
+    check_device_mapping(dw)
+
+
+@pytest.mark.parametrize("name", ["tiny_L1_H2_D64", "llama3_8b_k50"])
 def test_retrieve_then_inject(name):
     """retrieve_topk writes the fact ids straight into the device batch;
     inject_topk_device then injects them.  Expected: the oracle's own top-k
@@ -164,17 +204,26 @@ def test_retrieve_then_inject(name):
     w_oracle = dataclasses.replace(w, retrieved=oracle_ids)
     assert w_oracle.n_tokens == w.n_tokens
     blocks = w.listed_blocks()
-    if name.startswith("llama3_8b_batch64"):
-        # full size: compare 16 requests' blocks against the oracle
-        sub = dataclasses.replace(w_oracle, retrieved=oracle_ids[:16],
-                                  prefix=w.prefix[:16], block_tables=w.block_tables[:16],
-                                  spec=dataclasses.replace(sp, n_requests=16))
-        blocks = sub.listed_blocks()
-        img_k, img_v, _ = oracle_images(sub, gen)
-        gk, gv = dw.listed_blocks_host(blocks)
-        compare(img_k, img_v, gk, gv, written_mask(sub, blocks))
-    else:
-        img_k, img_v, _ = oracle_images(w_oracle, gen)
-        gk, gv = dw.listed_blocks_host(blocks)
-        compare(img_k, img_v, gk, gv, written_mask(w_oracle, blocks))
+    img_k, img_v, _ = oracle_images(w_oracle, gen)
+    gk, gv = dw.listed_blocks_host(blocks)
+    compare(img_k, img_v, gk, gv, written_mask(w_oracle, blocks))
     assert dw.count_non_sentinel() == 2 * sp.num_layers * w.n_tokens * sp.num_kv_heads * sp.head_dim
+
+
+@pytest.mark.timeout(900)
+def test_retrieve_then_inject_batch64_full_size():
+    """The 64-request batch end to end at full size: retrieve_topk's ids (the
+    oracle's top-k and the drawn facts) injected by inject_topk_device, every
+    K and V element of every request checked against the oracle."""
+    drawn = {}
+
+    def in_retrieval_order(w):
+        # the queries are built around the drawn facts: the oracle retrieves
+        # exactly those sets (checked), in the order of their scores
+        ids = _oracle_ids(w)
+        assert [sorted(r) for r in ids] == [sorted(map(int, r)) for r in w.retrieved]
+        drawn["w"] = w
+        return dataclasses.replace(w, retrieved=ids)
+
+    _full_size("llama3_8b_batch64_k50", paths=("retrieve",), prepare=in_retrieval_order,
+               via=lambda dw, path: _retrieve_then_inject(dw, drawn["w"]))
