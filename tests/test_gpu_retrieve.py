@@ -227,3 +227,39 @@ def test_retrieve_then_inject_batch64_full_size():
 
     _full_size("llama3_8b_batch64_k50", paths=("retrieve",), prepare=in_retrieval_order,
                via=lambda dw, path: _retrieve_then_inject(dw, drawn["w"]))
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_retrieve_random_shapes(seed):
+    """Seeded random shapes: requests, stores, facts per store (1 to 12,000),
+    k (1 to min(64, F)), width (a multiple of 8 up to 2,048), duplicated
+    embeddings (exact ties across the store) and the store each request
+    reads; ids and scores against the oracle's, request by request."""
+    rng = np.random.default_rng(1000 + seed)
+    n_stores = int(rng.integers(1, 4))
+    F = int(np.exp(rng.uniform(0, np.log(12000))))
+    F = max(1, min(F, 12000))
+    k = int(rng.integers(1, min(64, F) + 1))
+    dim = 8 * int(rng.integers(1, 257))
+    n_req = int(rng.integers(1, 25))
+    g = torch.Generator(device="cuda")
+    g.manual_seed(seed)
+    emb = (torch.randn((n_stores * F, dim), generator=g, device="cuda") / dim ** 0.5)
+    emb = emb.to(torch.bfloat16)
+    if F >= 4:   # a quarter of each store's rows duplicated elsewhere in it: exact ties
+        for s in range(n_stores):
+            src = torch.as_tensor(rng.integers(0, F, F // 4), device="cuda") + s * F
+            dst = torch.as_tensor(rng.integers(0, F, F // 4), device="cuda") + s * F
+            emb[dst] = emb[src]
+    emb = emb.view(torch.int16).contiguous()
+    req_store = rng.integers(0, n_stores, n_req).astype(np.int32)
+    # queries: a stored row plus noise, so each request has clear leaders
+    rows = torch.as_tensor(req_store.astype(np.int64) * F + rng.integers(0, F, n_req),
+                           device="cuda")
+    q = emb.view(torch.bfloat16)[rows].float() + \
+        0.3 * torch.randn((n_req, dim), generator=g, device="cuda") / dim ** 0.5
+    q = q.to(torch.bfloat16).view(torch.int16).contiguous()
+    ids, sc, st = run_retrieve(emb, q, req_store, F, k, dim, n_stores)
+    assert st == 0
+    check_against_oracle(emb.cpu().numpy().view(np.uint16).reshape(n_stores, F, dim),
+                         q.cpu().numpy().view(np.uint16), req_store, F, k, ids, sc)
