@@ -369,7 +369,8 @@ int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
  * k <= facts_per_store.  Scores are inner products of the bf16 values
  * accumulated in float64 (products are exact).  Output d_fact_ids: device
  * int32 [n_req][k], global ids store * facts_per_store + fact, best first
- * (higher score, then smaller id); d_scores: optional device double
+ * (higher score, then smaller id; a NaN score ranks below every number);
+ * d_scores: optional device double
  * [n_req][k].  A request with an out-of-range store gets ids -1 and sets
  * bit 64 in d_status.  d_workspace: device, retrieve_workspace_bytes
  * (scores, plus partial top-64 lists when few requests have many facts),

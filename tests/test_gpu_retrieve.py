@@ -263,3 +263,26 @@ def test_retrieve_random_shapes(seed):
     assert st == 0
     check_against_oracle(emb.cpu().numpy().view(np.uint16).reshape(n_stores, F, dim),
                          q.cpu().numpy().view(np.uint16), req_store, F, k, ids, sc)
+
+
+def test_retrieve_nan_scores_rank_last():
+    """Facts whose embedding holds a NaN score NaN: they rank below every
+    number, among themselves by id (the oracle's sort puts NaN last the same
+    way), and their scores come back NaN."""
+    F, dim, k = 100, 64, 20
+    g = torch.Generator(device="cuda")
+    g.manual_seed(3)
+    emb = (torch.randn((F, dim), generator=g, device="cuda") / dim ** 0.5).to(torch.bfloat16)
+    emb = emb.view(torch.int16).contiguous()
+    emb[:90, 7] = 0x7FC0                 # bf16 quiet NaN in rows 0..89
+    q = (torch.randn((1, dim), generator=g, device="cuda") / dim ** 0.5).to(torch.bfloat16)
+    q = q.view(torch.int16).contiguous()
+    ids, sc, st = run_retrieve(emb, q, np.array([0], np.int32), F, k, dim, 1)
+    assert st == 0
+    score = retrieve.scores(q.cpu().numpy().view(np.uint16)[0], emb.cpu().numpy().view(np.uint16))
+    want = retrieve.topk(score, k)
+    assert np.isnan(score[:90]).all() and np.isfinite(score[90:]).all()
+    assert list(want) == list(np.argsort(-score[90:], kind="stable") + 90) + list(range(10))
+    assert list(ids[0]) == list(want)
+    assert np.allclose(sc[0][:10], score[want[:10]], rtol=0, atol=1e-13)
+    assert np.isnan(sc[0][10:]).all()
