@@ -714,8 +714,19 @@ def check_retrieve_topk_brute_force():
             assert s[got].min() >= s[rest].max()
 
 
+def check_retrieve_topk_nan_last():
+    # hand-derived: a NaN score ranks below every number; NaNs by index
+    nan = float("nan")
+    assert list(retrieve.topk([nan, 0.5, nan, 0.7, -1.0], 5)) == [3, 1, 4, 0, 2]
+    assert list(retrieve.topk([nan, nan, -3.0], 2)) == [2, 0]
+
+
 def test_retrieve_scores_exact():
     check_retrieve_scores_exact()
+
+
+def test_retrieve_topk_nan_last():
+    check_retrieve_topk_nan_last()
 
 
 def test_retrieve_topk_golden():
@@ -732,6 +743,7 @@ ALL_CHECKS = [
     check_llama3_continuous_and_monotone, check_chunk_local_relocation,
     check_rotation_positions,
     check_retrieve_scores_exact, check_retrieve_topk_golden, check_retrieve_topk_brute_force,
+    check_retrieve_topk_nan_last,
     check_bf16_golden, check_bf16_exhaustive_roundtrip, check_bf16_midpoints,
     check_bf16_matches_torch, check_rope_golden, check_rope_matrix_form,
     check_rope_scalar_d2, check_rope_position_zero_identity, check_rope_norm_per_pair,
