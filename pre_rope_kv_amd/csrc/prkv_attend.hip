@@ -97,6 +97,12 @@ __device__ __forceinline__ bf16x8 load8(const unsigned char* p) {
   return __builtin_bit_cast(bf16x8, *reinterpret_cast<const u32x4*>(p));
 }
 
+// A float from lane (lane ^ M) of the wave (every lane active).
+template <int M>
+__device__ __forceinline__ float xor_f(float x) {
+  return __uint_as_float(prkv_dev::xor_lane<M>(__float_as_uint(x), int(threadIdx.x % kWave)));
+}
+
 // Transposing LDS read (ds_read_b64_tr_b16): in each group of 16 lanes, lane
 // i receives element i % 4 of the 8-byte words addressed by lanes i / 4,
 // i / 4 + 4, i / 4 + 8, i / 4 + 12 of its group.
@@ -437,8 +443,10 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) mt_max = fmaxf(mt_max, s[kt][i]);
     }
-    mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 16, kWave));
-    mt_max = fmaxf(mt_max, __shfl_xor(mt_max, 32, kWave));
+    // across the lanes holding the same rows, by permlane swaps (no LDS
+    // round trip in the tile's dependency chain)
+    mt_max = fmaxf(mt_max, xor_f<16>(mt_max));
+    mt_max = fmaxf(mt_max, xor_f<32>(mt_max));
     // Lazy rescale: the reference m_run only moves (and O, l are rescaled)
     // when some row of the wave sees a score more than 2^kLazy above it;
     // otherwise the probabilities are taken against the old reference and
@@ -562,8 +570,8 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   }
 
   // normalise and write O[layer][r][qi][hq][d], d = 16mt + 4a + i
-  float l_tot = l_run + __shfl_xor(l_run, 16, kWave);
-  l_tot += __shfl_xor(l_tot, 32, kWave);
+  float l_tot = l_run + xor_f<16>(l_run);
+  l_tot += xor_f<32>(l_tot);
   if constexpr (KG > 1) {
     // Groups 1.. hand (max, sum, O) to group 0 through LDS (the rings are
     // free: every group has waited for and consumed its last tile), and

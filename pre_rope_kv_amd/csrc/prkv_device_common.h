@@ -3,6 +3,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include <cstdint>
+
 namespace prkv_dev {
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
@@ -10,6 +12,35 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef float f32x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+
+// The value lane (lane ^ M) holds, for M a power of two below 64, without a
+// trip through LDS: xor 1 and 2 are DPP quad permutations, xor 4 is the
+// quad reversal (xor 3) followed by the half-row mirror (xor 7), xor 8 is
+// the row rotation by 8; xor 16 and xor 32 use the permlane swaps, which
+// exchange the odd 16-lane rows (upper 32 lanes) of their first operand with
+// the even rows (lower 32 lanes) of their second, so with both operands x a
+// lane finds its partner's value in the first result if its own bit is set,
+// else in the second.  Every lane of the wave must be active.
+template <int M>
+__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
+  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
+  if constexpr (M == 1) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
+  } else if constexpr (M == 2) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
+  } else if constexpr (M == 4) {
+    const int y = __builtin_amdgcn_mov_dpp(int(x), 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
+    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, true);  // row_half_mirror
+  } else if constexpr (M == 8) {
+    return __builtin_amdgcn_mov_dpp(int(x), 0x128, 0xF, 0xF, true);  // row_ror:8
+  } else if constexpr (M == 16) {
+    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+    return (lane & 16) ? p[0] : p[1];
+  } else {
+    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+    return (lane & 32) ? p[0] : p[1];
+  }
+}
 
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }

@@ -15,8 +15,9 @@
 // embedding (lanes past the width take zeros in the last, partial chunk), so
 // every 16-byte load of a fact row is coalesced.  Products of
 // two bf16 values are exact; they are accumulated in float64 and reduced
-// across the wave with a butterfly, so a score differs from the exact inner
-// product by ~1e-16 relative.  HBM bound (the embeddings are read once);
+// across the wave with a butterfly (lane exchanges in the VALU, no LDS round
+// trips), so a score differs from the exact inner product by ~1e-16
+// relative.  HBM bound (the embeddings are read once);
 // no MFMA: one query per store is a matrix-vector product.
 //
 // topk_kernel: 1024-lane workgroups, one per request, or up to 16 per
@@ -38,9 +39,12 @@
 #include <algorithm>
 #include <cstdint>
 
+#include "prkv_device_common.h"
 #include "prkv_internal.h"
 
 namespace {
+
+using prkv_dev::xor_lane;
 
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
@@ -65,6 +69,16 @@ __device__ __forceinline__ double bf16_lo(unsigned w) {
 }
 __device__ __forceinline__ double bf16_hi(unsigned w) {
   return double(__uint_as_float(w & 0xffff0000u));
+}
+
+// A double from lane (lane ^ M) of the wave, both halves through the lane
+// exchanges of prkv_dev::xor_lane (every lane active).
+template <int M>
+__device__ __forceinline__ double xor_double(double x, int lane) {
+  const uint64_t b = uint64_t(__double_as_longlong(x));
+  const uint32_t lo = xor_lane<M>(uint32_t(b), lane);
+  const uint32_t hi = xor_lane<M>(uint32_t(b >> 32), lane);
+  return __longlong_as_double(int64_t((uint64_t(hi) << 32) | lo));
 }
 
 template <int CHUNKS>  // ceil(dim / 512); dim is a multiple of 8
@@ -116,8 +130,13 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
           acc = __builtin_fma(bf16_hi(q[j][d]), bf16_hi(e[i][j][d]), acc);
         }
       }
-#pragma unroll
-      for (int off = kWave / 2; off > 0; off >>= 1) acc += __shfl_xor(acc, off, kWave);
+      // butterfly across the wave (lane exchanges, no LDS round trips)
+      acc += xor_double<32>(acc, lane);
+      acc += xor_double<16>(acc, lane);
+      acc += xor_double<8>(acc, lane);
+      acc += xor_double<4>(acc, lane);
+      acc += xor_double<2>(acc, lane);
+      acc += xor_double<1>(acc, lane);
       if (lane == 0 && g0 + i < f1) p.scores[int64_t(r) * p.facts_per_store + g0 + i] = acc;
     }
   }
@@ -142,35 +161,6 @@ struct Cand {
 
 __device__ __forceinline__ bool better(const Cand& a, const Cand& b) {
   return a.key > b.key || (a.key == b.key && a.id < b.id);
-}
-
-// The value lane (lane ^ M) holds, for M a power of two below 64, without a
-// trip through LDS: xor 1 and 2 are DPP quad permutations, xor 4 is the
-// quad reversal (xor 3) followed by the half-row mirror (xor 7), xor 8 is
-// the row rotation by 8; xor 16 and xor 32 use the permlane swaps, which
-// exchange the odd 16-lane rows (upper 32 lanes) of their first operand with
-// the even rows (lower 32 lanes) of their second, so with both operands x a
-// lane finds its partner's value in the first result if its own bit is set,
-// else in the second.  Every lane of the wave must be active.
-template <int M>
-__device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
-  static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane mask");
-  if constexpr (M == 1) {
-    return __builtin_amdgcn_mov_dpp(int(x), 0xB1, 0xF, 0xF, true);  // quad_perm [1,0,3,2]
-  } else if constexpr (M == 2) {
-    return __builtin_amdgcn_mov_dpp(int(x), 0x4E, 0xF, 0xF, true);  // quad_perm [2,3,0,1]
-  } else if constexpr (M == 4) {
-    const int y = __builtin_amdgcn_mov_dpp(int(x), 0x1B, 0xF, 0xF, true);  // quad_perm [3,2,1,0]
-    return __builtin_amdgcn_mov_dpp(y, 0x141, 0xF, 0xF, true);  // row_half_mirror
-  } else if constexpr (M == 8) {
-    return __builtin_amdgcn_mov_dpp(int(x), 0x128, 0xF, 0xF, true);  // row_ror:8
-  } else if constexpr (M == 16) {
-    const auto p = __builtin_amdgcn_permlane16_swap(x, x, false, false);
-    return (lane & 16) ? p[0] : p[1];
-  } else {
-    const auto p = __builtin_amdgcn_permlane32_swap(x, x, false, false);
-    return (lane & 32) ? p[0] : p[1];
-  }
 }
 
 template <int M>
