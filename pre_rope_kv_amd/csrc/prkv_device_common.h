@@ -42,6 +42,56 @@ __device__ __forceinline__ uint32_t xor_lane(uint32_t x, int lane) {
   }
 }
 
+// Inclusive prefix sums over the 64 lanes of a wave in the VALU (every lane
+// active): within each 16-lane row by DPP row shifts of 1, 2, 4 and 8
+// (lanes shifted in from outside the row read 0), then the last lane of row
+// 0 and of row 2 added to rows 1 and 3 (row broadcast 15) and the last lane
+// of row 1 to rows 2 and 3 (row broadcast 31); rows left out of a step by
+// its row mask add 0.
+template <int CTRL, int ROW_MASK, bool ZERO_OUTSIDE>
+__device__ __forceinline__ uint32_t dpp_move(uint32_t x) {
+  return __builtin_amdgcn_update_dpp(0u, x, CTRL, ROW_MASK, 0xF, ZERO_OUTSIDE);
+}
+
+__device__ __forceinline__ int32_t wave_scan_incl(int32_t x) {
+  uint32_t v = uint32_t(x);
+  v += dpp_move<0x111, 0xF, true>(v);    // row_shr:1
+  v += dpp_move<0x112, 0xF, true>(v);    // row_shr:2
+  v += dpp_move<0x114, 0xF, true>(v);    // row_shr:4
+  v += dpp_move<0x118, 0xF, true>(v);    // row_shr:8
+  v += dpp_move<0x142, 0xA, false>(v);   // row_bcast:15 into rows 1, 3
+  v += dpp_move<0x143, 0xC, false>(v);   // row_bcast:31 into rows 2, 3
+  return int32_t(v);
+}
+
+template <int CTRL, int ROW_MASK, bool ZERO_OUTSIDE>
+__device__ __forceinline__ int64_t dpp_move64(int64_t x) {
+  const uint64_t b = uint64_t(x);
+  const uint32_t lo = dpp_move<CTRL, ROW_MASK, ZERO_OUTSIDE>(uint32_t(b));
+  const uint32_t hi = dpp_move<CTRL, ROW_MASK, ZERO_OUTSIDE>(uint32_t(b >> 32));
+  return int64_t((uint64_t(hi) << 32) | lo);
+}
+
+__device__ __forceinline__ int64_t wave_scan_incl(int64_t x) {
+  x += dpp_move64<0x111, 0xF, true>(x);
+  x += dpp_move64<0x112, 0xF, true>(x);
+  x += dpp_move64<0x114, 0xF, true>(x);
+  x += dpp_move64<0x118, 0xF, true>(x);
+  x += dpp_move64<0x142, 0xA, false>(x);
+  x += dpp_move64<0x143, 0xC, false>(x);
+  return x;
+}
+
+// Inclusive prefix sums within the first 16 lanes (row 0) only.
+__device__ __forceinline__ int32_t row_scan_incl(int32_t x) {
+  uint32_t v = uint32_t(x);
+  v += dpp_move<0x111, 0xF, true>(v);
+  v += dpp_move<0x112, 0xF, true>(v);
+  v += dpp_move<0x114, 0xF, true>(v);
+  v += dpp_move<0x118, 0xF, true>(v);
+  return int32_t(v);
+}
+
 __device__ __forceinline__ float lo_bf16(unsigned w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float hi_bf16(unsigned w) { return __uint_as_float(w & 0xffff0000u); }
 

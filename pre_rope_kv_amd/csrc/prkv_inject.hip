@@ -302,12 +302,9 @@ __device__ int64_t fused_plan(const DeviceBatch& b, FusedLds& s) {
     }
     if (len == 0 && lead) flag(b.status, 8);
   }
-  int64_t x = len;  // inclusive scan within the wave, then across the 4 waves
-#pragma unroll
-  for (int d = 1; d < kWave; d <<= 1) {
-    const int64_t y = __shfl_up(x, d, kWave);
-    if (lane >= d) x += y;
-  }
+  // inclusive scan within the wave (DPP, no LDS round trips), then across
+  // the 4 waves
+  const int64_t x = prkv_dev::wave_scan_incl(int64_t(len));
   if (lane == kWave - 1) s.wsum[wave] = x;
   __syncthreads();
   int64_t before = 0, total = 0;
@@ -659,21 +656,13 @@ __global__ __launch_bounds__(kPlanThreads) void plan_kernel(DeviceBatch b) {
       }
       if (len == 0) flag(b.status, 8);
     }
-    int x = len;  // inclusive scan within the wave
-#pragma unroll
-    for (int d = 1; d < kWave; d <<= 1) {
-      const int y = __shfl_up(x, d, kWave);
-      if (lane >= d) x += y;
-    }
+    const int x = prkv_dev::wave_scan_incl(int32_t(len));  // inclusive, within the wave
     if (lane == kWave - 1) wave_sums[wave] = x;
     __syncthreads();
     if (wave == 0) {
+      static_assert(kPlanThreads / kWave == 16, "the wave sums fill one 16-lane row");
       int s = lane < kPlanThreads / kWave ? wave_sums[lane] : 0;
-#pragma unroll
-      for (int d = 1; d < kPlanThreads / kWave; d <<= 1) {
-        const int y = __shfl_up(s, d, kWave);
-        if (lane >= d) s += y;
-      }
+      s = prkv_dev::row_scan_incl(s);
       if (lane < kPlanThreads / kWave) wave_sums[lane] = s;
     }
     __syncthreads();
