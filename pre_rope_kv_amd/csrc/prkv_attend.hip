@@ -520,8 +520,8 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();                 // ... and every wave's; tile t-1 is consumed
       __asm__ volatile("" ::: "memory");
-      if (t + kStages < ntiles) fill_slots(t + kStages);
       if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
+      if (t + kStages < ntiles) fill_slots(t + kStages);
       const int* sl = s_slots[0][t % kSlotRing];
       const bool masked = any_missing || base + kTile - 1 > q_block0;
       if (masked) {
@@ -553,8 +553,8 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();                 // ... and every wave's; tile i-1 is consumed
       __asm__ volatile("" ::: "memory");
-      if (i + kStages < n_mine) fill_slots(i + kStages);
       if (i + kStages - 1 < n_mine) issue(i + kStages - 1);
+      if (i + kStages < n_mine) fill_slots(i + kStages);
       const int* sl = s_slots[kg][i % kSlotRing];
       // Zeroing masked rows is decided for the whole workgroup (the barrier
       // after it must be reached by every wave): by the iteration's last tile.
