@@ -82,7 +82,8 @@ __device__ __forceinline__ int64_t wave_scan_incl(int64_t x) {
   return x;
 }
 
-// Inclusive prefix sums within the first 16 lanes (row 0) only.
+// Inclusive prefix sums within each 16-lane row of the wave (no carry
+// between rows), for a caller whose values fill one row.
 __device__ __forceinline__ int32_t row_scan_incl(int32_t x) {
   uint32_t v = uint32_t(x);
   v += dpp_move<0x111, 0xF, true>(v);
