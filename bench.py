@@ -11,6 +11,16 @@ heads and requests.  The roofline figures time the dominant kernel alone
 (host build_slot_mapping + H2D of the mapping + inject) is reported separately
 under "e2e" and is never `value`.
 
+Timing: the headline step and kernel are K launches with an event after
+each (so the line has per-launch percentiles; an event costs a few
+microseconds against a 5 ms launch), `ms_per_step` the larger of that mean
+and the host's wall clock.  Launches of tens of microseconds (the small
+workloads, retrieval, the reference copies and reads) are timed as runs of
+back-to-back launches enqueued behind a clock spin with one event before
+and one after the run, since an event between launches would add its own
+3-5 us to each; cold figures are runs of (MALL-evicting fill, launch) minus
+runs of the fills alone.
+
 Prints one JSON line.  Only one GPU: --gpus above 1 exits with a message.
 """
 
