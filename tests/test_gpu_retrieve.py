@@ -135,19 +135,22 @@ def test_retrieve_bad_store_reports(F):
     assert list(ids[0]) == [0, 1, 2, 3, 4]   # all scores 0: id order
 
 
-def _oracle_ids(w):
-    """The oracle's top-k of each request's store for the workload's queries
-    (global fact ids, best first)."""
-    sp = w.spec
-    embs, emb = _embeddings(w)
-    q = w.query_embeddings("cuda", emb=embs)
-    del embs
+def _oracle_ids_of(sp, emb, q):
+    """The oracle's top-k of each request's own store (request r searches
+    store r) for device embeddings and queries: global fact ids, best first."""
     emb_h = emb.cpu().numpy().view(np.uint16).reshape(sp.n_requests, sp.facts_per_store, -1)
     q_h = q.cpu().numpy().view(np.uint16)
-    del emb, q
     return [[int(r * sp.facts_per_store + f)
              for f in retrieve.topk(retrieve.scores(q_h[r], emb_h[r]), sp.k)]
             for r in range(sp.n_requests)]
+
+
+def _oracle_ids(w):
+    """The oracle's top-k for the workload's own embeddings and queries."""
+    embs, emb = _embeddings(w)
+    q = w.query_embeddings("cuda", emb=embs)
+    del embs
+    return _oracle_ids_of(w.spec, emb, q)
 
 
 def _retrieve_then_inject(dw, w_drawn):
@@ -185,11 +188,8 @@ def test_retrieve_then_inject(name):
     gen = "cpu" if name.startswith("tiny") else "cuda"
     embs, emb = _embeddings(w)
     q = w.query_embeddings("cuda", emb=embs)
-    emb_h = emb.cpu().numpy().view(np.uint16).reshape(sp.n_requests, sp.facts_per_store, -1)
-    q_h = q.cpu().numpy().view(np.uint16)
-    oracle_ids = [[int(r * sp.facts_per_store + f)
-                   for f in retrieve.topk(retrieve.scores(q_h[r], emb_h[r]), sp.k)]
-                  for r in range(sp.n_requests)]
+    assert list(w.req_store()) == list(range(sp.n_requests))   # request r searches store r
+    oracle_ids = _oracle_ids_of(sp, emb, q)
     dw = harness.DeviceWorkload(w, gen_device=gen, host_mapping=False)
     dw.setup_device_batch()
     dw.d_ids.fill_(-1)
