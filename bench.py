@@ -318,7 +318,8 @@ _CEILING = None
 
 def ceiling_lib():
     """libprkv_ceiling.so (built by pre_rope_kv_amd.build): the plain copy the
-    inject kernel is measured against, and the plain read the retrieval is."""
+    inject kernel is measured against, the plain read the retrieval is, and
+    the plain gather of the cache rows the attention kernel is."""
     global _CEILING
     if _CEILING is None:
         path = os.path.join(ROOT, "pre_rope_kv_amd", "libprkv_ceiling.so")
@@ -334,6 +335,9 @@ def ceiling_lib():
         lib.ceiling_empty.restype = ctypes.c_int
         lib.ceiling_read.argtypes = [vp, i64, vp, i32, i32, vp]
         lib.ceiling_read.restype = ctypes.c_int
+        lib.ceiling_gather_kv.argtypes = [vp, vp, i64, i32, i32, i32, vp, i32, vp, vp, i32, i32,
+                                          i64, i32, vp, i32, i32, vp]
+        lib.ceiling_gather_kv.restype = ctypes.c_int
         _CEILING = lib
     return _CEILING
 
@@ -1445,6 +1449,41 @@ def run(args, workers):
         assert kv_bytes == sum(ctxs) * spec.num_layers * spec.num_kv_heads * spec.head_dim * 4
         flops = sum(ctxs) * spec.num_layers * hq * q_len * spec.head_dim * 4
         a_traffic = read_profile_traffic(spec.name, "attend_kernel") if profiled_config else None
+        gather_ceiling = gather_by_heads = None
+        if not args.no_ceiling and not dw.hnd:
+            # the same cache rows (every context position's K and V rows, through the
+            # same block tables, in the same XCD-aware workgroup order) read by a plain
+            # gather with no arithmetic, fastest of 1-8 passes in flight x plain /
+            # nontemporal loads; one workgroup per (layer, request, KV head) as the
+            # attention kernel splits the work, and for comparison per 2, 4, 8 adjacent
+            # heads (longer contiguous pieces of each cache row)
+            clib = ceiling_lib()
+            sink = torch.zeros(256, dtype=torch.int32, device="cuda")
+            d_ctx = torch.as_tensor(ctxs, dtype=torch.int32, device="cuda")
+            layer_bytes = dw.k_cache.stride(0) * dw.k_cache.element_size()
+            gather_by_heads = {}
+            for hg in (1, 2, 4, 8):
+                if spec.num_kv_heads % hg or 256 % (hg * spec.head_dim // 8):
+                    continue
+                best = None
+                for nt in (0, 1):
+                    for passes in (1, 2, 4, 8):
+                        def step_gather(ps=passes, n=nt, h=hg):
+                            rc = clib.ceiling_gather_kv(
+                                dw.k_cache.data_ptr(), dw.v_cache.data_ptr(), layer_bytes,
+                                spec.num_layers, spec.num_kv_heads, spec.head_dim,
+                                dw.d_bt.data_ptr(), dw.d_bt.shape[1], dw.d_bt_len.data_ptr(),
+                                d_ctx.data_ptr(), spec.n_requests, spec.block_size,
+                                w.num_blocks, h, sink.data_ptr(), ps, n, stream.cuda_stream)
+                            if rc != 0:
+                                raise RuntimeError(f"ceiling_gather_kv failed ({rc})")
+                        c_ms = time_span(torch, step_gather, stream, args.steps, args.warmup)
+                        if best is None or c_ms < best["ms"]:
+                            best = {"ms": c_ms, "gbps": kv_bytes / (c_ms * 1e-3) / 1e9,
+                                    "passes": passes, "nontemporal": bool(nt)}
+                gather_by_heads[str(hg)] = best
+            gather_ceiling = gather_by_heads["1"]
+            del sink, d_ctx
         attn = {
             "what": f"attend_paged: {q_len} query tokens x {hq} query heads per request over "
                     "its whole context in the paged cache, all layers, one launch",
@@ -1460,6 +1499,10 @@ def run(args, workers):
                          "traffic": a_traffic, "kernel": f"attend_kernel<{spec.head_dim}>",
                          "bytes_per_launch": a_alg},
             "bound": "hbm (about 64 flop per byte of cache read, below the MFMA ridge)",
+            "gather_ceiling": gather_ceiling,
+            "pct_of_gather_ceiling": (100.0 * gather_ceiling["ms"] / a_ms
+                                      if gather_ceiling else None),
+            "gather_ceiling_by_heads_per_workgroup": gather_by_heads,
         }
         del out, qt
 

@@ -4,8 +4,9 @@
 
 The host half (prkv_host.cpp) is plain C++17 built with g++; the device half
 (prkv_inject.hip, prkv_retrieve.hip, prkv_attend.hip) is built with hipcc for
-gfx950 only.  libprkv_ceiling.so (prkv_ceiling.hip, a plain streaming copy)
-is built beside it for the bench's attainable-bandwidth reference.  Packed fp32 VALU
+gfx950 only.  libprkv_ceiling.so (prkv_ceiling.hip: a plain copy, a streaming read and a
+gather of the attention launch's cache rows) is built beside it for the
+bench's attainable-bandwidth references.  Packed fp32 VALU
 instructions are disabled and FP contraction is off: the compensated
 rotation relies on every product and sum being rounded exactly as written.
 """

@@ -1,5 +1,6 @@
-// libprkv_ceiling.so: a measuring stick for the inject kernel, not part of
-// the path.  A plain copy over the inject launch's own buffers and
+// libprkv_ceiling.so: measuring sticks for the kernels of the path (inject,
+// retrieval scoring, attention), not part of it.  For the inject kernel,
+// a plain copy over the inject launch's own buffers and
 // addresses, with no rotation, metadata staging or index arithmetic beyond
 // the row lookup: for every token t and layer l,
 //
@@ -39,6 +40,27 @@
 //     kept and nothing is written).  sink holds 256 uint32.  The read-only
 //     counterpart of the gather-scatter copy, for the retrieval score
 //     kernel (which reads the fact embeddings once).
+//   ceiling_gather_kv(k_cache, v_cache, layer_bytes, num_layers,
+//                     num_kv_heads, head_dim, block_tables, bt_stride, bt_len,
+//                     ctx, n_req, block_size, num_blocks, heads_per_group, sink,
+//                     passes, nontemporal, stream)
+//     the cache reads of an attention launch over the paged cache (NHD
+//     layout, [layer][slot][head][dim]), with no arithmetic: one 256-lane
+//     workgroup per (layer, request, group of heads_per_group adjacent KV
+//     heads), in the attention kernel's XCD-aware order, reads the group's
+//     K and V rows (heads_per_group x head_dim contiguous bf16 values) of
+//     every position pos < ctx[r] of request r, at slot
+//     block_tables[r][pos / block_size] * block_size + pos % block_size.
+//     heads_per_group 1 is the attention kernel's own split (a workgroup
+//     per KV head); it must divide num_kv_heads, and its rows must split
+//     evenly over 256 lanes of 16 bytes.  A lane loads one 16-byte piece of
+//     a row per pass, `passes` (1, 2, 4 or 8) passes of K and V in flight,
+//     plain or nontemporal loads; the block ids of the next passes are
+//     loaded while the current ones fly.  Loads are folded with xor and nothing is
+//     written (sink as for ceiling_read).  A position whose block index is
+//     past bt_len[r] or whose block id is outside [0, num_blocks) reads
+//     nothing.  layer_bytes must cover num_blocks * block_size slots of
+//     num_kv_heads * head_dim bf16 values.
 
 #include <hip/hip_runtime.h>
 
@@ -142,6 +164,91 @@ __global__ __launch_bounds__(256) void read_kernel(const u32x4* __restrict__ src
   if (f == 0x9e3779b9u && acc.x == 0x7f4a7c15u && acc.y == 0xf39cc060u) sink[threadIdx.x] = f;
 }
 
+template <int D, int PASSES, bool NT>
+__global__ __launch_bounds__(256) void gather_kv_kernel(
+    const u32x4* __restrict__ kc, const u32x4* __restrict__ vc, int64_t layer_vecs,
+    const int32_t* __restrict__ bt, int32_t bt_stride, const int32_t* __restrict__ bt_len,
+    const int32_t* __restrict__ ctx, int32_t n_req, int32_t num_kv_heads, int32_t block_size,
+    int64_t num_blocks, int32_t heads_per_group, uint32_t* __restrict__ sink) {
+  constexpr int DC = D / 8;                 // 16-byte pieces per head row
+  const int CP = heads_per_group * DC;      // pieces per row of the head group
+  const int KP = 256 / CP;                  // keys per pass of the workgroup
+  const int groups = num_kv_heads / heads_per_group;
+  const int nwg = gridDim.x;
+  const int bid = (nwg % 8 == 0) ? (blockIdx.x % 8) * (nwg / 8) + blockIdx.x / 8 : blockIdx.x;
+  const int g = bid % groups * heads_per_group;   // first head of the group
+  const int r = (bid / groups) % n_req;
+  const int layer = bid / (groups * n_req);
+  const int kp = threadIdx.x / CP, c = threadIdx.x % CP;
+  const int n_ctx = ctx[r];
+  const int nb = min(bt_len[r], bt_stride);
+  const int32_t* btr = bt + int64_t(r) * bt_stride;
+  const u32x4* kl = kc + layer * layer_vecs;
+  const u32x4* vl = vc + layer * layer_vecs;
+  const int64_t slot_vecs = int64_t(num_kv_heads) * DC;
+  // block id of position pos, or -1 where nothing is read
+  auto block_of = [&](int pos) -> int {
+    const int bi = pos / block_size;
+    return pos < n_ctx && bi < nb ? btr[bi] : -1;
+  };
+  int blk[PASSES];
+#pragma unroll
+  for (int j = 0; j < PASSES; ++j) blk[j] = block_of(j * KP + kp);
+  u32x4 acc = {0u, 0u, 0u, 0u};
+  for (int base = 0; base < n_ctx; base += PASSES * KP) {
+    u32x4 xk[PASSES], xv[PASSES];
+#pragma unroll
+    for (int j = 0; j < PASSES; ++j) {
+      const int pos = base + j * KP + kp;
+      const bool ok = blk[j] >= 0 && blk[j] < num_blocks;
+      const int64_t slot = ok ? int64_t(blk[j]) * block_size + pos % block_size : 0;
+      const u32x4* kp16 = kl + slot * slot_vecs + g * DC + c;
+      const u32x4* vp16 = vl + slot * slot_vecs + g * DC + c;
+      const u32x4 zero = {0u, 0u, 0u, 0u};
+      if (NT) {
+        xk[j] = ok ? __builtin_nontemporal_load(kp16) : zero;
+        xv[j] = ok ? __builtin_nontemporal_load(vp16) : zero;
+      } else {
+        xk[j] = ok ? *kp16 : zero;
+        xv[j] = ok ? *vp16 : zero;
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < PASSES; ++j) blk[j] = block_of(base + (PASSES + j) * KP + kp);
+#pragma unroll
+    for (int j = 0; j < PASSES; ++j) acc ^= xk[j] ^ xv[j];
+  }
+  const uint32_t f = acc.x ^ acc.y ^ acc.z ^ acc.w;
+  if (f == 0x9e3779b9u && acc.x == 0x7f4a7c15u && acc.y == 0xf39cc060u) sink[threadIdx.x] = f;
+}
+
+template <int D, int PASSES, bool NT>
+void launch_gather_kv(int64_t grid, hipStream_t s, const u32x4* kc, const u32x4* vc,
+                      int64_t layer_vecs, const int32_t* bt, int32_t bt_stride,
+                      const int32_t* bt_len, const int32_t* ctx, int32_t n_req,
+                      int32_t num_kv_heads, int32_t block_size, int64_t num_blocks, int32_t hg,
+                      uint32_t* sink) {
+  hipLaunchKernelGGL((gather_kv_kernel<D, PASSES, NT>), dim3(unsigned(grid)), dim3(256), 0, s, kc,
+                     vc, layer_vecs, bt, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size,
+                     num_blocks, hg, sink);
+}
+
+template <int D, bool NT>
+int launch_gather_kv_passes(int passes, int64_t grid, hipStream_t s, const u32x4* kc,
+                            const u32x4* vc, int64_t layer_vecs, const int32_t* bt,
+                            int32_t bt_stride, const int32_t* bt_len, const int32_t* ctx,
+                            int32_t n_req, int32_t num_kv_heads, int32_t block_size,
+                            int64_t num_blocks, int32_t hg, uint32_t* sink) {
+  switch (passes) {
+    case 1: launch_gather_kv<D, 1, NT>(grid, s, kc, vc, layer_vecs, bt, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, hg, sink); break;
+    case 2: launch_gather_kv<D, 2, NT>(grid, s, kc, vc, layer_vecs, bt, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, hg, sink); break;
+    case 4: launch_gather_kv<D, 4, NT>(grid, s, kc, vc, layer_vecs, bt, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, hg, sink); break;
+    case 8: launch_gather_kv<D, 8, NT>(grid, s, kc, vc, layer_vecs, bt, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, hg, sink); break;
+    default: return -1;
+  }
+  return 0;
+}
+
 template <int THREADS, int ORDER>
 int launch(const void* ks, const void* vs, int64_t src_layer_vecs, void* kd, void* vd,
            int64_t dst_layer_vecs, const int32_t* sr, const int32_t* dr, int64_t n, int L,
@@ -241,6 +348,40 @@ int ceiling_read(const void* src, int64_t bytes, uint32_t* sink, int32_t per_lan
     case 8: hipLaunchKernelGGL(read_kernel<8>, dim3(unsigned(grid)), dim3(256), 0, s, p, n, sink); break;
     default: return -1;
   }
+  return hipGetLastError() == hipSuccess ? 0 : -10;
+}
+
+int ceiling_gather_kv(const void* k_cache, const void* v_cache, int64_t layer_bytes,
+                      int32_t num_layers, int32_t num_kv_heads, int32_t head_dim,
+                      const int32_t* block_tables, int32_t bt_stride, const int32_t* bt_len,
+                      const int32_t* ctx, int32_t n_req, int32_t block_size, int64_t num_blocks,
+                      int32_t heads_per_group, uint32_t* sink, int32_t passes, int32_t nontemporal,
+                      void* stream) {
+  if (!k_cache || !v_cache || !block_tables || !bt_len || !ctx || !sink) return -1;
+  if ((reinterpret_cast<uintptr_t>(k_cache) | reinterpret_cast<uintptr_t>(v_cache)) & 15u)
+    return -1;
+  if (num_layers < 1 || num_kv_heads < 1 || n_req < 1 || bt_stride < 1 || block_size < 1 ||
+      num_blocks < 1 || (head_dim != 64 && head_dim != 128) || layer_bytes % 16)
+    return -1;
+  if (num_blocks * int64_t(block_size) > INT32_MAX) return -1;
+  if (layer_bytes < num_blocks * block_size * int64_t(num_kv_heads) * head_dim * 2) return -1;
+  if (heads_per_group < 1 || num_kv_heads % heads_per_group) return -1;
+  const int pieces = heads_per_group * (head_dim / 8);
+  if (pieces > 256 || 256 % pieces) return -1;
+  const int64_t grid = int64_t(num_layers) * n_req * (num_kv_heads / heads_per_group);
+  if (grid > INT32_MAX) return -1;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const u32x4* kc = static_cast<const u32x4*>(k_cache);
+  const u32x4* vc = static_cast<const u32x4*>(v_cache);
+  const int64_t lv = layer_bytes / 16;
+  int rc;
+  if (head_dim == 128)
+    rc = nontemporal ? launch_gather_kv_passes<128, true>(passes, grid, s, kc, vc, lv, block_tables, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, heads_per_group, sink)
+                     : launch_gather_kv_passes<128, false>(passes, grid, s, kc, vc, lv, block_tables, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, heads_per_group, sink);
+  else
+    rc = nontemporal ? launch_gather_kv_passes<64, true>(passes, grid, s, kc, vc, lv, block_tables, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, heads_per_group, sink)
+                     : launch_gather_kv_passes<64, false>(passes, grid, s, kc, vc, lv, block_tables, bt_stride, bt_len, ctx, n_req, num_kv_heads, block_size, num_blocks, heads_per_group, sink);
+  if (rc != 0) return rc;
   return hipGetLastError() == hipSuccess ? 0 : -10;
 }
 
