@@ -37,10 +37,13 @@
 // products), below the MFMA ridge: it is bound by reading the cache.
 // A three-tile LDS ring (49.5 KB with the slot buffers, plus the block
 // table): three workgroups per CU, each with two tiles in flight while it
-// computes the third.  Bytes in flight decide the rate: measured on MI355X,
-// the kernel with its compute removed reads 5.6 TB/s with a two-tile ring
-// at four workgroups per CU, and the full kernel with three tiles at three
-// per CU is 2 % faster than with two tiles at four per CU.
+// computes the third.  Measured on MI355X, this reads the cache at 82-88 %
+// of a plain gather of the same rows in the same workgroup split; it is 2 %
+// faster than two tiles at four workgroups per CU, and 16-key tiles in a
+// six-tile ring (more bytes in flight, twice the barriers) are 13-19 %
+// slower.  What a tile costs between its arrival and the reuse of its ring
+// slot (the matrix products, softmax, operand reads and the barrier) sets
+// the rate, more than the bytes in flight.
 //
 // The query is rotated in-kernel with the store's RoPE table and pairing
 // (compensated fp32, as in injection).  Keys outside [0, q_start + q_len),
