@@ -19,10 +19,11 @@
 // ring of three tiles: while tile t is computed, tiles t+1 and t+2's K and V
 // rows travel from the paged cache straight into LDS (global_load_lds_dwordx4,
 // no register staging), gathered through the block table (kept in LDS; the
-// slot of every key is computed once, two tiles ahead).  Per tile each wave
-// computes
-//   S^T = K Q^T   (v_mfma_f32_16x16x32_bf16; the accumulator then holds, per
-//                  lane, scores of the lane's own query row)
+// slot and cache-row offset of every key are computed once, three tiles
+// ahead, by one wave in turn).  Per tile each wave computes
+//   S^T = K Q^T - m (v_mfma_f32_16x16x32_bf16 from accumulators that start
+//                  at minus the row's running reference m; the accumulator
+//                  then holds, per lane, scores of the lane's own query row)
 //   online softmax in fp32 (exp2, lazily rescaled running max, running sum)
 //   O^T += V^T P^T (same MFMA; S^T's accumulator layout is exactly the B
 //                  operand layout P^T needs; the V^T A operand comes from
@@ -35,9 +36,12 @@
 // fp32 rounding; K and V are the cache's bf16 values.  At 16 query tokens
 // the kernel does about 64 flop per byte of cache (128 with the doubled
 // products), below the MFMA ridge: it is bound by reading the cache.
-// A three-tile LDS ring (49.5 KB with the slot buffers, plus the block
-// table): three workgroups per CU, each with two tiles in flight while it
-// computes the third.  Measured on MI355X, this reads the cache at 82-88 %
+// A three-tile LDS ring (50 KB with the slot and offset buffers, plus the
+// block table): three workgroups per CU, each with two tiles in flight while
+// it computes the third.  The tile loop is unrolled over the three ring
+// slots, so every LDS address of a tile is an immediate offset and the
+// per-tile vector-ALU work (which three waves per SIMD share with the matrix
+// products) stays small.  Measured on MI355X, this reads the cache at 82-88 %
 // of a plain gather of the same rows in the same workgroup split; it is 2 %
 // faster than two tiles at four workgroups per CU, and 16-key tiles in a
 // six-tile ring (more bytes in flight, twice the barriers) are 13-19 %
@@ -55,6 +59,7 @@
 #include <atomic>
 #include <cmath>
 #include <cstdint>
+#include <type_traits>
 
 #include "prkv_device_common.h"
 #include "prkv_internal.h"
@@ -69,6 +74,10 @@ constexpr int kSlotRing = 4;    // slot buffers (>= kStages + 1, a power of two)
 constexpr int kMaxRows = 64;    // query rows per workgroup
 constexpr int kThreads = kMaxRows / 16 * kWave;
 constexpr int kBtLds = 2048;    // block-table entries kept in LDS
+
+// a ring slot known at compile time
+template <int X>
+using Slot = std::integral_constant<int, X>;
 
 typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) i16x4 lds_i16x4;
@@ -153,7 +162,10 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   constexpr int TILEB = kTile * ROWB;   // bytes per K or V tile
   // a ring of tiles of K and V, row-major, 16-byte chunks XOR-swizzled per row
   __shared__ __align__(1024) unsigned char s_kv[KG][kStages][2][TILEB];
-  __shared__ __align__(16) int s_slots[KG][kSlotRing][kTile];  // per key: slot, -1 beyond ctx, -2 missing
+  // per key: slot, -1 beyond ctx, -2 missing; and the byte offset of its head
+  // row in a layer's cache (0 for a masked key: a valid address)
+  __shared__ __align__(16) int s_slots[KG][kSlotRing][kTile];
+  __shared__ __align__(16) int64_t s_offs[KG][kSlotRing][kTile];
   extern __shared__ int s_bt[];         // the request's block table (bt_stride <= kBtLds)
 
   // XCD-aware order: workgroups are dealt round-robin over the 8 XCDs, so
@@ -289,7 +301,12 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   f32x4 o[MT];
 #pragma unroll
   for (int mt = 0; mt < MT; ++mt) o[mt] = f32x4{0.f, 0.f, 0.f, 0.f};
-  float m_run = -INFINITY, l_run = 0.f;
+  // Per row: the reference m_run (-inf until a finite score), m_use the same
+  // but 0 while there is none, negm = -m_use in all four accumulator lanes
+  // (the score products start from it, so scores come out relative to the
+  // reference), thr the relative score that moves the reference.
+  float m_run = -INFINITY, l_run = 0.f, m_use = 0.f, thr = -INFINITY;
+  f32x4 negm = {0.f, 0.f, 0.f, 0.f};
 
   const uint16_t* kl = kc.p[layer];
   const uint16_t* vl = vc.p[layer];
@@ -360,10 +377,25 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   // Group kg's i-th tile is key tile i * KG + kg; group-local index i runs
   // its ring.  The slots of a tile, one per key, by the group's first kTile
   // lanes kStages tiles ahead, in a ring of kSlotRing buffers.
+  // Tile i's slots are looked up by wave i % 4 of the group, so the work
+  // rotates over the SIMDs.
   auto fill_slots = [&](int i) {
-    if (lt < kTile) {
-      const int pos = (i * KG + kg) * kTile + lt;
-      s_slots[kg][i % kSlotRing][lt] = pos < ctx ? slot_of(pos) : -1;
+    if (wave == (i & 3) && lane < kTile) {
+      const int pos = (i * KG + kg) * kTile + lane;
+      const int sk = pos < ctx ? slot_of(pos) : -1;
+      // element offset of (slot sk, head g): NHD sk * H * D + g * D; HND
+      // (with sk = b * bs + o) ((sk - o) * H + o) * D + g * bs * D
+      int64_t off = 0;
+      if (sk >= 0) {
+        if (p.hnd) {
+          const int o = p.bs_shift >= 0 ? (sk & (p.block_size - 1)) : sk % p.block_size;
+          off = (int64_t(sk - o) * p.num_kv_heads + o) * D + int64_t(g) * p.block_size * D;
+        } else {
+          off = int64_t(sk) * row_elems + g * D;
+        }
+      }
+      s_slots[kg][i % kSlotRing][lane] = sk;
+      s_offs[kg][i % kSlotRing][lane] = 2 * off;
     }
   };
   // Issue the direct loads of tile t into ring buffer t % kStages.
@@ -377,31 +409,27 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   static_assert(NI >= 1 && kTile * DC % 256 == 0, "a tile must split over the 4 waves");
   const uint32_t kv_lds =
       uint32_t(reinterpret_cast<uintptr_t>((lds_void*)(&s_kv[kg][0][0][0])));
-  auto issue = [&](int ti) {
-    const int* sl = s_slots[kg][ti % kSlotRing];
-    const uint32_t kd = kv_lds + uint32_t(ti % kStages) * (2 * TILEB);
+  // this wave's 1 KB piece of ring slot 0, a scalar: the destination of each
+  // load adds a constant to it
+  const uint32_t lds_w = __builtin_amdgcn_readfirstlane(kv_lds + uint32_t(wave) * 1024u);
+  auto issue = [&](int ti, auto SLOT) {
+    constexpr int slot = decltype(SLOT)::value;
+    const int64_t* so = s_offs[kg][ti % kSlotRing];
+    const uint32_t kd = lds_w + uint32_t(slot) * (2 * TILEB);
     const uint32_t vd = kd + TILEB;
 #pragma unroll
     for (int i = 0; i < NI; ++i) {
       const int n = i * 4 + wave;
       const int k = n * RPI + lane / DC;
       const int pk = lane % DC;
-      const int sk = sl[k] >= 0 ? sl[k] : 0;
-      // element offset of (slot sk, head g): NHD sk * H * D + g * D; HND
-      // (with sk = b * bs + o) ((sk - o) * H + o) * D + g * bs * D
-      int64_t off;
-      if (p.hnd) {
-        const int o = p.bs_shift >= 0 ? (sk & (p.block_size - 1)) : sk % p.block_size;
-        off = (int64_t(sk - o) * p.num_kv_heads + o) * D + int64_t(g) * p.block_size * D;
-      } else {
-        off = int64_t(sk) * row_elems + g * D;
-      }
-      load_lds16(kl + off + 8 * (pk ^ swk(k)), kd + n * 1024);
-      load_lds16(vl + off + 8 * (pk ^ swv(k)), vd + n * 1024);
+      const int64_t off = so[k];
+      load_lds16(reinterpret_cast<const char*>(kl + 8 * (pk ^ swk(k))) + off, kd + i * 4096);
+      load_lds16(reinterpret_cast<const char*>(vl + 8 * (pk ^ swv(k))) + off, vd + i * 4096);
     }
   };
   // Zero the K and V rows of masked keys of the group's tile in buffer `buf`.
-  auto zero_masked = [&](const int* sl, int buf) {
+  auto zero_masked = [&](const int* sl, auto SLOT) {
+    constexpr int buf = decltype(SLOT)::value;
     const u32x4 zero = {0u, 0u, 0u, 0u};
     for (int e = lt; e < kTile * DC; e += kThreads) {
       const int k = e / DC;
@@ -416,11 +444,11 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   auto compute = [&](const unsigned char* kt_lds, const unsigned char* vt_lds, int base,
                      const int* sl, bool masked) {
     constexpr int KT = kTile / 16;      // 16-key blocks of the tile
-    // S^T = K Q^T: lane holds keys 16kt + 4a + i of its row
+    // S^T = K Q^T - m_use: lane holds keys 16kt + 4a + i of its row
     f32x4 s[KT];
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
-      s[kt] = f32x4{0.f, 0.f, 0.f, 0.f};
+      s[kt] = negm;
       const int k = 16 * kt + c16;
 #pragma unroll
       for (int kb = 0; kb < KB; ++kb) {
@@ -455,21 +483,29 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
     // otherwise the probabilities are taken against the old reference and
     // may exceed 1 (by at most 2^kLazy), which the final division by l
     // cancels exactly.
+    // (Scores and mt_max are relative to m_use; the first finite score of a
+    // row always sets its reference.)
     constexpr float kLazy = 8.f;
-    if (__builtin_amdgcn_ballot_w64(mt_max > m_run + kLazy) != 0) {
-      const float m_new = fmaxf(m_run, mt_max);
+    if (__builtin_amdgcn_ballot_w64(mt_max > thr) != 0) {
+      const float m_new = fmaxf(m_run, m_use + mt_max);
       const float alpha = __builtin_amdgcn_exp2f(m_run - (m_new == -INFINITY ? 0.f : m_new));
       l_run *= alpha;
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) o[mt] *= alpha;
       m_run = m_new;
+      const float m_use_new = m_new == -INFINITY ? 0.f : m_new;
+      const float d = m_use_new - m_use;
+#pragma unroll
+      for (int kt = 0; kt < KT; ++kt) s[kt] -= d;
+      m_use = m_use_new;
+      negm = f32x4{-m_use, -m_use, -m_use, -m_use};
+      thr = m_new == -INFINITY ? -INFINITY : kLazy;
     }
-    const float m_use = m_run == -INFINITY ? 0.f : m_run;
 #pragma unroll
     for (int kt = 0; kt < KT; ++kt) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float e = __builtin_amdgcn_exp2f(s[kt][i] - m_use);
+        const float e = __builtin_amdgcn_exp2f(s[kt][i]);
         s[kt][i] = e;
         l_run += e;
       }
@@ -482,14 +518,19 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
     // 16mt + 4 (c16 % 4) .. + 3.
 #pragma unroll
     for (int kk = 0; kk < KT / 2; ++kk) {
-      bf16x8 ph, pl;
+      // hi parts rounded in pairs; each lo part is the value minus its hi
+      // part read back from the packed word
+      u32x4 phw, plw;
 #pragma unroll
-      for (int j = 0; j < 8; ++j) {
-        const float v = j < 4 ? s[2 * kk][j] : s[2 * kk + 1][j - 4];
-        const __bf16 h = (__bf16)v;
-        ph[j] = h;
-        pl[j] = (__bf16)(v - (float)h);
+      for (int j = 0; j < 4; ++j) {
+        const float v0 = j < 2 ? s[2 * kk][2 * j] : s[2 * kk + 1][2 * j - 4];
+        const float v1 = j < 2 ? s[2 * kk][2 * j + 1] : s[2 * kk + 1][2 * j - 3];
+        const unsigned hw = pack_bf16(v0, v1);
+        phw[j] = hw;
+        plw[j] = pack_bf16(v0 - lo_bf16(hw), v1 - hi_bf16(hw));
       }
+      const bf16x8 ph = __builtin_bit_cast(bf16x8, phw);
+      const bf16x8 pl = __builtin_bit_cast(bf16x8, plw);
       const int k = 32 * kk + 4 * a + c16 / 4;   // swv(k + 16) == swv(k)
 #pragma unroll
       for (int mt = 0; mt < MT; ++mt) {
@@ -508,30 +549,37 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   if constexpr (KG == 1) {
     // Pipeline: tiles t+1 .. t+kStages-1 stream into the ring while tile t
     // is computed; slots run kStages tiles ahead.
+    static_assert(kStages == 3, "the loops below are unrolled over the ring");
     if (ntiles > 0) {
       for (int u = 0; u < kStages && u < ntiles; ++u) fill_slots(u);
       __syncthreads();
-      for (int u = 0; u < kStages - 1 && u < ntiles; ++u) issue(u);
+      issue(0, Slot<0>{});
+      if (ntiles > 1) issue(1, Slot<1>{});
     }
-    for (int t = 0; t < ntiles; ++t) {
+    // Tile t in ring slot SLOT = t % 3 (a constant in each unrolled copy, so
+    // the slot's LDS addresses are immediate offsets).
+    auto step = [&](int t, auto SLOT) {
+      constexpr int rs = decltype(SLOT)::value;
       const int base = t * kTile;
-      // this wave's loads of tile t have landed (later tiles may still fly)
-      const int later = min(kStages - 2, ntiles - 1 - t);
-      static_assert(kStages <= 4, "extend the waits below");
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      // this wave's loads of tile t have landed (tile t+1's may still fly)
+      if (t + 1 < ntiles) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();                 // ... and every wave's; tile t-1 is consumed
       __asm__ volatile("" ::: "memory");
-      if (t + kStages - 1 < ntiles) issue(t + kStages - 1);
-      if (t + kStages < ntiles) fill_slots(t + kStages);
+      if (t + 2 < ntiles) issue(t + 2, Slot<(rs + 2) % 3>{});
+      if (t + 3 < ntiles) fill_slots(t + 3);
       const int* sl = s_slots[0][t % kSlotRing];
       const bool masked = any_missing || base + kTile - 1 > q_block0;
       if (masked) {
-        zero_masked(sl, t % kStages);
+        zero_masked(sl, SLOT);
         __syncthreads();
       }
-      compute(s_kv[0][t % kStages][0], s_kv[0][t % kStages][1], base, sl, masked);
+      compute(s_kv[0][rs][0], s_kv[0][rs][1], base, sl, masked);
+    };
+    for (int t = 0; t < ntiles; t += 3) {
+      step(t, Slot<0>{});
+      if (t + 1 < ntiles) step(t + 1, Slot<1>{});
+      if (t + 2 < ntiles) step(t + 2, Slot<2>{});
     }
   } else {
     // Pipeline (per key group, on its own tiles): tiles i+1 .. i+kStages-1
@@ -540,34 +588,39 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
     // match; a group whose tiles have run out only takes part in them.
     const int n_mine = ntiles > kg ? (ntiles - kg + KG - 1) / KG : 0;   // this group's tiles
     const int n_iter = (ntiles + KG - 1) / KG;
+    static_assert(kStages == 3, "the loops below are unrolled over the ring");
     if (n_iter > 0) {
       for (int u = 0; u < kStages && u < n_mine; ++u) fill_slots(u);
       __syncthreads();
-      for (int u = 0; u < kStages - 1 && u < n_mine; ++u) issue(u);
+      if (n_mine > 0) issue(0, Slot<0>{});
+      if (n_mine > 1) issue(1, Slot<1>{});
     }
-    for (int i = 0; i < n_iter; ++i) {
+    auto step = [&](int i, auto SLOT) {
+      constexpr int rs = decltype(SLOT)::value;
       const int base = (i * KG + kg) * kTile;
       const bool mine = i < n_mine;
-      // this wave's loads of tile i have landed (later tiles may still fly)
-      const int later = mine ? min(kStages - 2, n_mine - 1 - i) : 0;
-      static_assert(kStages <= 4, "extend the waits below");
-      if (later >= 2) __builtin_amdgcn_s_waitcnt(vmcnt_imm(2 * LPT));
-      else if (later == 1) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
+      // this wave's loads of tile i have landed (tile i+1's may still fly)
+      if (mine && i + 1 < n_mine) __builtin_amdgcn_s_waitcnt(vmcnt_imm(LPT));
       else __builtin_amdgcn_s_waitcnt(vmcnt_imm(0));
       __syncthreads();                 // ... and every wave's; tile i-1 is consumed
       __asm__ volatile("" ::: "memory");
-      if (i + kStages - 1 < n_mine) issue(i + kStages - 1);
-      if (i + kStages < n_mine) fill_slots(i + kStages);
+      if (i + 2 < n_mine) issue(i + 2, Slot<(rs + 2) % 3>{});
+      if (i + 3 < n_mine) fill_slots(i + 3);
       const int* sl = s_slots[kg][i % kSlotRing];
       // Zeroing masked rows is decided for the whole workgroup (the barrier
       // after it must be reached by every wave): by the iteration's last tile.
       const bool any_masked = any_missing || (i + 1) * KG * kTile - 1 > q_block0;
       if (any_masked) {
-        if (mine) zero_masked(sl, i % kStages);
+        if (mine) zero_masked(sl, SLOT);
         __syncthreads();
       }
       const bool masked = any_missing || base + kTile - 1 > q_block0;
-      if (mine) compute(s_kv[kg][i % kStages][0], s_kv[kg][i % kStages][1], base, sl, masked);
+      if (mine) compute(s_kv[kg][rs][0], s_kv[kg][rs][1], base, sl, masked);
+    };
+    for (int i = 0; i < n_iter; i += 3) {
+      step(i, Slot<0>{});
+      if (i + 1 < n_iter) step(i + 1, Slot<1>{});
+      if (i + 2 < n_iter) step(i + 2, Slot<2>{});
     }
 
   }
