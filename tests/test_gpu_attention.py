@@ -328,6 +328,47 @@ def test_attention_one_key_group_grids(D, H, hq, q_len):
     check(dw, qb, got, q_len, hq, layers, "cpu")
 
 
+def random_attention_case(seed):
+    """A seeded random attention shape: head dim, KV heads, group size, block
+    size (powers of two and not), layers, requests, prefix and fact lengths,
+    query length, RoPE base and cache layout.  Odd seeds have grids of more
+    than one workgroup per CU (the one-key-group kernel), even seeds small
+    ones (three key groups); tile counts take every value modulo the ring
+    depth."""
+    rng = np.random.default_rng(1000 + seed)
+    D = int(rng.choice([64, 128]))
+    group = int(rng.choice([1, 2, 3, 4, 7]))
+    bs = int(rng.choice([1, 2, 3, 5, 8, 16, 24, 32]))
+    if seed % 2:     # at least 3 x 11 x 8 = 264 workgroups: the one-key-group kernel
+        H, L, n_req = 8, int(rng.integers(3, 5)), int(rng.integers(11, 15))
+    else:
+        H, L, n_req = int(rng.choice([1, 2, 4, 8])), int(rng.integers(1, 5)), int(rng.integers(1, 7))
+    q_len = int(rng.integers(1, 25))
+    prefix = int(rng.integers(1, 200))
+    lens = [rng.integers(1, 81, size=int(rng.integers(0, 7))) for _ in range(n_req)]
+    theta = float(rng.choice([1e4, 5e5]))
+    layout = int(rng.integers(0, 2))
+    w = context_workload(f"attn_rand_{seed}", L, H, D, bs, prefix, lens, q_len, n_req=n_req,
+                         seed=seed, theta=theta)
+    if layout:
+        w = workloads.dataclasses.replace(
+            w, spec=workloads.dataclasses.replace(w.spec, cache_layout=prkv.CACHE_HND))
+    return w, q_len, H * group
+
+
+@pytest.mark.parametrize("seed", range(12))
+def test_attention_random_shapes(seed):
+    w, q_len, hq = random_attention_case(seed)
+    sp = w.spec
+    grid = sp.num_layers * sp.n_requests * sp.num_kv_heads * -(-q_len * (hq // sp.num_kv_heads) // 64)
+    _say(f"seed {seed}: D {sp.head_dim}, H {sp.num_kv_heads}, {hq} query heads, bs "
+         f"{sp.block_size}, L {sp.num_layers}, {sp.n_requests} requests, q_len {q_len}, "
+         f"layout {'HND' if sp.cache_layout else 'NHD'}, grid {grid}")
+    dw, qb, got, layers = run_attention(w, q_len, hq, gen="cpu", seed=seed)
+    assert int(dw.status.item()) == 0
+    check(dw, qb, got, q_len, hq, layers, "cpu")
+
+
 def test_attention_query_positions_out_of_range_are_reported():
     # request 0 starts past max_position - q_len, request 1 before 0: both are
     # reported (bit 2) and produce 0; request 2 is unaffected
