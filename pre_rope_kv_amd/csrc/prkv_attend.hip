@@ -375,10 +375,10 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
   auto swv = [](int k) { return D == 128 ? 2 * (k % 8) : 2 * ((k / 2) % 4); };
 
   // Group kg's i-th tile is key tile i * KG + kg; group-local index i runs
-  // its ring.  The slots of a tile, one per key, by the group's first kTile
-  // lanes kStages tiles ahead, in a ring of kSlotRing buffers.
-  // Tile i's slots are looked up by wave i % 4 of the group, so the work
-  // rotates over the SIMDs.
+  // its ring.  Each key's slot and the byte offset of its head row in a
+  // layer's cache (0 for a masked key) are looked up kStages tiles ahead,
+  // into a ring of kSlotRing buffers, by the first kTile lanes of the
+  // group's wave i % 4, so the work rotates over the SIMDs.
   auto fill_slots = [&](int i) {
     if (wave == (i & 3) && lane < kTile) {
       const int pos = (i * KG + kg) * kTile + lane;
@@ -398,11 +398,12 @@ attend_kernel(AttnParams p, LayerCPtrs kc, LayerCPtrs vc) {
       s_offs[kg][i % kSlotRing][lane] = 2 * off;
     }
   };
-  // Issue the direct loads of tile t into ring buffer t % kStages.
-  // Instruction n of the tile fills 1 KB = rows n * RPI .. n * RPI + RPI - 1;
-  // lane l takes row n * RPI + l / DC, chunk position l % DC, i.e. logical
-  // chunk (l % DC) ^ swizzle.  Masked keys load slot 0 (a valid address) and
-  // are zeroed before use.
+  // Issue the direct loads of tile t into ring slot SLOT (t % kStages, a
+  // compile-time constant).  Instruction n of the tile fills 1 KB = rows
+  // n * RPI .. n * RPI + RPI - 1; lane l takes row n * RPI + l / DC, chunk
+  // position l % DC, i.e. logical chunk (l % DC) ^ swizzle.  Masked keys load
+  // from offset 0 (the layer's first cache row, a valid address) and are
+  // zeroed before use.
   constexpr int RPI = 64 / DC;                  // rows per load instruction
   constexpr int NI = kTile * DC / 64 / 4;       // instructions per wave per tile, for K and for V
   constexpr unsigned LPT = 2 * NI;              // loads per wave per tile
