@@ -56,7 +56,6 @@
 
 #include <hip/hip_runtime.h>
 
-#include <atomic>
 #include <cmath>
 #include <cstdint>
 #include <type_traits>
@@ -692,30 +691,13 @@ void launch_attend_kg(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtr
                        dim3(kThreads * KG), sizeof(int32_t), s, p, kc, vc);
 }
 
-// Compute units of the current device (cached per device; 256 if unknown).
-int attend_compute_units() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int v = cached[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      n <= 0)
-    n = 256;
-  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 template <int D, int STYLE>
 void launch_attend_style(const AttnParams& p, const LayerCPtrs& kc, const LayerCPtrs& vc,
                          int64_t grid, hipStream_t s) {
   // A grid of at most one workgroup per CU (e.g. one request: L x H
   // workgroups) leaves each CU one workgroup's tiles in flight: there, three
   // key groups per workgroup (12 waves, three LDS rings) triple them.
-  if (grid <= attend_compute_units())
+  if (grid <= prkv::compute_units())
     launch_attend_kg<D, STYLE, 3>(p, kc, vc, grid, s);
   else
     launch_attend_kg<D, STYLE, 1>(p, kc, vc, grid, s);

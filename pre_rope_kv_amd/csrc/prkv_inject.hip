@@ -759,22 +759,6 @@ int hip_fail(hipError_t e, const char* what) {
 
 bool aligned16(const void* ptr) { return (reinterpret_cast<uintptr_t>(ptr) & 15u) == 0; }
 
-int compute_units() {
-  static std::atomic<int> cached[64];
-  int dev = 0;
-  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
-  if (dev < 64) {
-    const int v = cached[dev].load(std::memory_order_relaxed);
-    if (v > 0) return v;
-  }
-  int n = 0;
-  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-      n <= 0)
-    n = 256;
-  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
-  return n;
-}
-
 template <int D, int STYLE, bool MULTI>
 void launch_one(const InjectParams& p, const LayerPtrs& kc, const LayerPtrs& vc,
                 const DeviceBatch* fused, int64_t grid, size_t lds, hipStream_t s) {
@@ -863,7 +847,7 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   const int tpw = (nc < kWave && kWave % nc == 0) ? kWave / nc : 1;
   const int64_t chunks = int64_t(d.num_layers) * nc;
   const int iters = tpw > 1 ? d.num_layers : int((chunks + kWave - 1) / kWave);
-  const int64_t want_waves = int64_t(compute_units()) * 16;
+  const int64_t want_waves = int64_t(prkv::compute_units()) * 16;
   const int64_t tile_tokens = int64_t(kWavesPerGroup) * tpw;
   const bool device_count = n_tokens_dev || fused;
   const int64_t sized_for =
@@ -902,7 +886,7 @@ int launch_inject(const prkv_store* st, int64_t n_tokens, const int64_t* n_token
   // grid stride (same-process A/B: k = 5 -8 %, k = 10 -1.4 %, k = 20 -2.9 %;
   // at k = 50, 2k tokens, +1 %, so larger batches keep the wider grid).
   if (fused && expect_tokens >= 0 && expect_tokens <= kFuseCapTokens) {
-    const int64_t cap = int64_t(compute_units()) * 4;
+    const int64_t cap = int64_t(prkv::compute_units()) * 4;
     if (grid > cap) grid = cap;
   }
   size_t lds = size_t(tile_tokens) * (size_t(D / 2) * 16 + 12);
@@ -1343,3 +1327,23 @@ int inject_topk_device_noalloc(const prkv_store* st, const void* d_fact_table,
 }
 
 }  // extern "C"
+
+namespace prkv {
+
+int compute_units() {
+  static std::atomic<int> cached[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 256;
+  if (dev < 64) {
+    const int v = cached[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      n <= 0)
+    n = 256;
+  if (dev < 64) cached[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
+}  // namespace prkv

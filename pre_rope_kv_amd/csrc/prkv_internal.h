@@ -39,4 +39,8 @@ void commit_put(prkv_store* st, int32_t fact_id, int32_t len);
 
 constexpr int kMaxLayers = 128;
 
+// Compute units of the current device (cached per device; 256 if unknown).
+// Defined with the device code.
+int compute_units();
+
 }  // namespace prkv

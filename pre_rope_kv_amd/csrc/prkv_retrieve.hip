@@ -10,7 +10,9 @@
 // Check" -- the index backend changes latency, not which facts are found.
 // Exact search stands in for the approximate index.
 //
-// score_kernel: one wave per group of facts of one request.  The query is
+// score_kernel: one wave per group of facts of one request (8 facts, or 2
+// when 8 would leave fewer than two workgroups per CU, e.g. one request: then
+// the store's rows are read by four times as many waves).  The query is
 // read once per wave; lane l owns elements [8l + 512j, 8l + 512j + 8) of the
 // embedding (lanes past the width take zeros in the last, partial chunk), so
 // every 16-byte load of a fact row is coalesced.  Products of
@@ -50,7 +52,8 @@ typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kWave = 64;
 constexpr int kScoreWaves = 4;
-constexpr int kFactsPerWave = 8;
+constexpr int kFactsPerWave = 8;        // facts per wave when the grid fills the chip
+constexpr int kFactsPerWaveSmall = 2;   // otherwise
 constexpr int kTopkThreads = 1024;
 constexpr int kMaxK = 64;
 constexpr int kMaxList = 64;   // candidates per partial list (one per lane)
@@ -61,7 +64,7 @@ struct ScoreParams {
   const int32_t* req_store;   // [n_req]
   double* scores;             // [n_req][F]
   int32_t* status;
-  int32_t n_req, n_stores, facts_per_store, dim, groups_per_req;
+  int32_t n_req, n_stores, facts_per_store, dim, groups_per_req, facts_per_wave;
 };
 
 __device__ __forceinline__ double bf16_lo(unsigned w) {
@@ -87,7 +90,7 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
   const int lane = threadIdx.x % kWave;
   const int r = gw / p.groups_per_req;
   if (r >= p.n_req) return;
-  const int f0 = (gw - r * p.groups_per_req) * kFactsPerWave;
+  const int f0 = (gw - r * p.groups_per_req) * p.facts_per_wave;
   const int s = p.req_store[r];
   if (s < 0 || s >= p.n_stores) {
     if (lane == 0 && f0 == 0 && p.status) atomicOr(p.status, 64);
@@ -104,7 +107,7 @@ __global__ __launch_bounds__(kWave * kScoreWaves) void score_kernel(ScoreParams 
   for (int j = 0; j < CHUNKS; ++j)
     q[j] = (j < CHUNKS - 1 || tail_in) ? *reinterpret_cast<const u32x4*>(qrow + 512 * j) : zero;
   const uint16_t* base = p.fact_emb + (int64_t(s) * p.facts_per_store) * p.dim + lane * 8;
-  const int f1 = min(f0 + kFactsPerWave, p.facts_per_store);
+  const int f1 = min(f0 + p.facts_per_wave, p.facts_per_store);
   // G facts' rows are loaded together before any is reduced, so G rows per
   // wave are in flight (G * CHUNKS * 4 VGPRs)
   constexpr int G = CHUNKS <= 2 ? 8 : (CHUNKS <= 4 ? 4 : 2);
@@ -428,7 +431,13 @@ int retrieve_topk(const void* d_fact_emb, int32_t n_stores, int32_t facts_per_st
   sp.n_stores = n_stores;
   sp.facts_per_store = facts_per_store;
   sp.dim = dim;
-  sp.groups_per_req = (facts_per_store + kFactsPerWave - 1) / kFactsPerWave;
+  // fewer facts per wave when the default would leave CUs idle
+  const int64_t wgs_default =
+      (int64_t(n_req) * ((facts_per_store + kFactsPerWave - 1) / kFactsPerWave) + kScoreWaves - 1) /
+      kScoreWaves;
+  sp.facts_per_wave =
+      wgs_default < 2 * int64_t(prkv::compute_units()) ? kFactsPerWaveSmall : kFactsPerWave;
+  sp.groups_per_req = (facts_per_store + sp.facts_per_wave - 1) / sp.facts_per_wave;
   if (int64_t(n_req) * sp.groups_per_req / kScoreWaves + 1 > INT32_MAX)
     return prkv::fail(PRKV_ERR_INVALID_ARG, "grid too large");
   hipStream_t s = static_cast<hipStream_t>(stream);
